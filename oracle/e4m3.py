@@ -1,0 +1,108 @@
+"""OCP FP8 E4M3 (e4m3fn) encoding and the blockwise FP8 expert path (test infrastructure only).
+
+Sources (the pages):
+  * "DeepSeek-V3 ... 技术解析" (devpress), section 2: weights are quantised per 128x128
+    block and activations per 1x128 tile; heavy matmuls run in FP8 with FP32
+    accumulation every 128 elements.
+  * stapisi blog, section 6.2: the largest E4M3 value is 448.
+
+Format (OCP 8-bit floating point, E4M3 "fn" variant): sign bit, 4 exponent bits with
+bias 7, 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9); no infinities;
+S.1111.111 is NaN; the largest finite magnitude is 1.75 * 2^8 = 448.
+
+Readings (listed in the design notes):
+  * block scale s = amax / 448 as a float32 division, s = 1 when amax == 0
+  * code = round-to-nearest-even of the float32 quotient x / s, saturating at +-448;
+    the sign of a value that rounds to zero is kept (0x80 for negative values)
+  * a quantised GEMM equals sum over 128-wide K blocks of (s_a * s_w * sum q_a q_w);
+    the oracle computes it as the exact product of dequantised values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .moe_layer import _f64, silu
+
+E4M3_MAX = 448.0
+
+
+def e4m3_table() -> np.ndarray:
+    """float64 value of each of the 256 e4m3fn codes (NaN for 0x7F and 0xFF)."""
+    vals = np.empty(256, np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * m * 2.0 ** -9
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_POS = e4m3_table()[:0x7F]          # codes 0x00..0x7E: 0, ..., 448, ascending
+
+
+def e4m3_encode_rne(v) -> np.ndarray:
+    """Round values to e4m3 codes: nearest, ties to the even code, saturate at +-448.
+
+    Works on the exact float64 value of the input (float32 inputs are exact in float64).
+    NaN maps to 0x7F.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    lo = np.clip(np.searchsorted(_POS, a, side="right") - 1, 0, 0x7E)   # _POS[lo] <= a
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = a - _POS[lo]
+    d_hi = _POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    code = code | np.where(np.signbit(v), 0x80, 0)
+    code = np.where(np.isnan(v), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_1x128(x):
+    """Per row and per 128-column block: s = f32(amax / 448) (1 if amax == 0),
+    code = e4m3_rne(f32(x / s)).  x [rows, cols] with cols % 128 == 0 (float32-exact values).
+
+    Returns (codes uint8 [rows, cols], scales float32 [rows, cols/128]).
+    """
+    x32 = np.asarray(_f64(x), dtype=np.float32)
+    rows, cols = x32.shape
+    blocks = x32.reshape(rows, cols // 128, 128)
+    amax = np.abs(blocks).max(axis=2)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    quot = (blocks / scale[:, :, None]).astype(np.float32)
+    return e4m3_encode_rne(quot).reshape(rows, cols), scale
+
+
+def dequantize_1x128(codes, scales) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, cols = codes.shape
+    vals = e4m3_table()[codes].reshape(rows, cols // 128, 128)
+    return (vals * np.asarray(scales, np.float64)[:, :, None]).reshape(rows, cols)
+
+
+def dequantize_blocks_128(codes, scales) -> np.ndarray:
+    """Weights stored as e4m3 codes [n, k] with one scale per 128x128 block [n/128, k/128]."""
+    if hasattr(codes, "detach"):
+        codes = codes.detach().to("cpu").view(__import__("torch").uint8).numpy()
+    codes = np.asarray(codes, dtype=np.uint8)
+    sc = _f64(scales)
+    n, k = codes.shape
+    vals = e4m3_table()[codes]
+    return vals * np.repeat(np.repeat(sc, 128, axis=0), 128, axis=1)[:n, :k]
+
+
+def expert_ffn_fp8_emulated(u, w_gate, w_up, w_down) -> np.ndarray:
+    """Diagnostic FP8 expert: u and the SwiGLU output h are each quantised per 1x128
+    along their own K dimension before the GEMM that consumes them; weights are
+    already dequantised float64 arrays.  All products and sums in float64."""
+    uq = dequantize_1x128(*quantize_1x128(np.asarray(_f64(u), np.float32)))
+    h = silu(uq @ _f64(w_gate).T) * (uq @ _f64(w_up).T)
+    hq = dequantize_1x128(*quantize_1x128(h.astype(np.float32)))
+    return hq @ _f64(w_down).T

@@ -1,0 +1,166 @@
+"""Pins for the e4m3 format, the 1x128 / 128x128 FP8 block quantisation and the
+SwiGLU expert / layer combination of the oracle."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_e4m3_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    ref = codes.to(torch.float64).numpy()
+    tab = oracle.e4m3_table()
+    nan = np.isnan(ref)
+    assert nan.tolist() == np.isnan(tab).tolist()
+    assert np.nonzero(nan)[0].tolist() == [0x7F, 0xFF]
+    np.testing.assert_array_equal(tab[~nan], ref[~nan])
+    assert np.nanmax(tab) == 448.0 and tab[0x01] == 2.0 ** -9
+
+
+def test_e4m3_rne_matches_torch_cast_sweep():
+    rng = np.random.default_rng(0)
+    tab = oracle.e4m3_table()
+    mids = (tab[1:0x7F] + tab[0:0x7E]) / 2           # every midpoint: the ties
+    v = np.concatenate([
+        rng.uniform(-448, 448, 200000), rng.standard_normal(100000) * 1e-2,
+        mids, -mids, tab[:0x7F], np.nextafter(mids, 0), np.nextafter(mids, 1000),
+        [0.0, -0.0, 447.99, -447.99, 2.0 ** -10, -(2.0 ** -11)],
+    ]).astype(np.float32)
+    ours = oracle.e4m3_encode_rne(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_saturates():
+    v = np.array([448.0, 464.0, 1e6, -500.0, np.inf, -np.inf], np.float32)
+    assert oracle.e4m3_encode_rne(v).tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE]
+
+
+def _golden_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_quant_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            vals, scale, codes = (p.strip() for p in line.split("|"))
+            rows.append(([float(v) for v in vals.split()], float(scale),
+                         [int(c, 16) for c in codes.split()]))
+    return rows
+
+
+def test_quantize_1x128_golden():
+    for vals, scale, codes in _golden_rows():
+        x = np.zeros((1, 128), np.float32)
+        x[0, :len(vals)] = vals
+        q, s = oracle.quantize_1x128(x)
+        assert s.shape == (1, 1) and s[0, 0] == np.float32(scale)
+        assert q[0, :len(codes)].tolist() == codes
+        assert np.all(q[0, len(codes):] == 0)
+
+
+def test_quantize_1x128_bounds():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((16, 512)) * rng.uniform(0.01, 10, (16, 1))).astype(np.float32)
+    x[3, 128:256] = 0.0
+    q, s = oracle.quantize_1x128(x)
+    assert s.shape == (16, 4) and s.dtype == np.float32 and s[3, 1] == 1.0
+    tab = oracle.e4m3_table()
+    deq = oracle.dequantize_1x128(q, s)
+    blocks = x.reshape(16, 4, 128)
+    amax = np.abs(blocks).max(2)
+    # the block maximum maps to 448 (the largest code)
+    for r in range(16):
+        for j in range(4):
+            if amax[r, j] > 0:
+                k = np.argmax(np.abs(blocks[r, j]))
+                assert abs(tab[q[r, j * 128 + k]]) == 448.0
+    # error bound: at most half an e4m3 step (relative 2^-4) of each value, in scale units
+    err = np.abs(deq - x) / np.repeat(s, 128, axis=1)
+    step = np.abs(tab[q]) * 2.0 ** -3
+    assert np.all(err <= np.maximum(step, 2.0 ** -9) / 2 * (1 + 1e-6) + 1e-12)
+
+
+def test_dequantize_blocks_128():
+    codes = torch.tensor([[0x38] * 256] * 256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    scales = np.array([[1.0, 2.0], [3.0, 4.0]], np.float32)
+    w = oracle.dequantize_blocks_128(codes, scales)
+    assert w.shape == (256, 256)
+    assert w[0, 0] == 1.0 and w[0, 200] == 2.0 and w[200, 0] == 3.0 and w[255, 255] == 4.0
+
+
+def _loops_ffn(u, wg, wu, wd):
+    n, h = u.shape
+    inter = wg.shape[0]
+    out = np.zeros((n, h))
+    for r in range(n):
+        hid = []
+        for i in range(inter):
+            a = sum(u[r, c] * wg[i, c] for c in range(h))
+            b = sum(u[r, c] * wu[i, c] for c in range(h))
+            hid.append(a / (1 + np.exp(-a)) * b)
+        for c in range(h):
+            out[r, c] = sum(hid[i] * wd[c, i] for i in range(inter))
+    return out
+
+
+def test_expert_ffn_matches_loops():
+    rng = np.random.default_rng(2)
+    u = rng.standard_normal((3, 5))
+    wg, wu, wd = rng.standard_normal((4, 5)), rng.standard_normal((4, 5)), rng.standard_normal((5, 4))
+    np.testing.assert_allclose(oracle.expert_ffn(u, wg, wu, wd), _loops_ffn(u, wg, wu, wd),
+                               rtol=1e-12, atol=1e-12)
+    assert np.all(oracle.expert_ffn(u, wg, np.zeros_like(wu), wd) == 0)
+    # silu closed form at a few points
+    a = np.array([-3.0, 0.0, 0.5, 10.0])
+    np.testing.assert_allclose(oracle.silu(a), a * (1 / (1 + np.exp(-a))), rtol=1e-15)
+
+
+def _experts(rng, n, h, inter):
+    return [(rng.standard_normal((inter, h)) * 0.3, rng.standard_normal((inter, h)) * 0.3,
+             rng.standard_normal((h, inter)) * 0.3) for _ in range(n)]
+
+
+def test_layer_one_hot_and_dense_mixture():
+    rng = np.random.default_rng(3)
+    E, h, inter, T = 8, 6, 5, 7
+    ex = _experts(rng, E + 1, h, inter)
+    x = rng.standard_normal((T, h))
+    w = rng.standard_normal((E, h))
+    # K = 1: the single gate is exactly 1 -> shared + the chosen expert
+    r = oracle.route(x, w, np.zeros(E, np.float32), 1, 1, 1, 1)
+    assert np.all(r.gate == 1.0)
+    y = oracle.layer_output(x, r.idx, r.gate, lambda e: ex[e], E, 1)
+    for t in range(T):
+        ref = oracle.expert_ffn(x[t:t + 1], *ex[E]) + oracle.expert_ffn(x[t:t + 1], *ex[r.idx[t, 0]])
+        np.testing.assert_allclose(y[t:t + 1], ref, rtol=1e-12)
+    # M = G and K = E: a dense mixture weighted by s / sum(s) over all experts
+    r = oracle.route(x, w, np.zeros(E, np.float32), 2, 2, 2, E)
+    y = oracle.layer_output(x, r.idx, r.gate, lambda e: ex[e], E, 1)
+    s = 1 / (1 + np.exp(-(x @ w.T)))
+    ref = oracle.expert_ffn(x, *ex[E])
+    for e in range(E):
+        ref = ref + (s[:, e] / s.sum(1))[:, None] * oracle.expert_ffn(x, *ex[e])
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # residual adds u; a subset of rows equals the same rows of the full output
+    y_res = oracle.layer_output(x, r.idx, r.gate, lambda e: ex[e], E, 1, residual=x)
+    np.testing.assert_allclose(y_res - x, y, rtol=1e-12, atol=1e-12)
+    ys = oracle.layer_output(x, r.idx, r.gate, lambda e: ex[e], E, 1, rows=[1, 4])
+    np.testing.assert_allclose(ys, y[[1, 4]], rtol=1e-15, atol=0)
+
+
+def test_fp8_emulated_close_to_exact():
+    rng = np.random.default_rng(4)
+    h, inter = 256, 128
+    u = rng.standard_normal((8, h)).astype(np.float32)
+    wg, wu, wd = (rng.standard_normal((inter, h)) * 0.05, rng.standard_normal((inter, h)) * 0.05,
+                  rng.standard_normal((h, inter)) * 0.05)
+    exact = oracle.expert_ffn(u, wg, wu, wd)
+    emu = oracle.expert_ffn_fp8_emulated(u, wg, wu, wd)
+    rel = np.abs(emu - exact).max() / np.abs(exact).max()
+    assert 1e-4 < rel < 0.1
