@@ -1,0 +1,176 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ *
+ * The layer (DeepSeek-V3 technical report summary "深度解读报告", section 2.2):
+ *
+ *     out_t = [u_t] + sum_{s < Ns} FFN_{E+s}(u_t) + sum_{k < K} g_tk * FFN_{idx_tk}(u_t)
+ *
+ * with sigmoid affinities s_te = sigmoid(<u_t, W_r[e]>), a per-expert bias b_e
+ * added to the affinity for top-K selection only (section 2.3), selection limited
+ * to the M best of G expert groups (section 2.4, "node-limited routing": a
+ * group's score is the sum of its group_topn best biased affinities), gates
+ * g_tk = s_{t,idx_tk} / sum_j s_{t,idx_tj}, SwiGLU experts
+ * FFN(u) = W_down (silu(W_gate u) * (W_up u)), and no token dropping.  The
+ * devpress page ("DeepSeek-V3 ... 技术解析"), section 1, fixes 256 routed experts,
+ * 1 shared expert and 8 routed experts per token; its section 2 fixes the FP8
+ * blocks (128x128 for weights, 1x128 for activations).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless stated otherwise; `moe_config*` and
+ *    `moe_expert_weights*` are HOST structs read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work on `stream`; none synchronises, allocates device
+ *    memory, or keeps a pointer after it returns.  Scratch memory comes from the
+ *    caller's workspace `ws` of `ws_bytes` bytes (see moe_workspace_bytes).
+ *  - The caller owns every buffer.  Outputs are fully overwritten.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is enqueued.  Return codes only (no global error state);
+ *    moe_status_string() names a code.  MOE_ERR_HIP reports a failed launch;
+ *    faults inside kernels surface at the caller's next synchronisation.
+ *  - Calls are thread-safe (no mutable global state).  Results are
+ *    deterministic: no floating-point atomics and no split-K anywhere.
+ *  - Row-major layouts throughout.  Experts are stacked routed-first: experts
+ *    0..E-1 are routed, E..E+Ns-1 are the shared experts.
+ *
+ * Supported dtype combinations (act_dtype, w_dtype): (F32, F32), (BF16, BF16),
+ * (BF16, E4M3).  Limits: E <= 256, K <= 8, G <= 64; hidden and inter multiples of
+ * 128 for BF16/E4M3 weights, of 4 for F32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,    /* null pointer, inconsistent sizes            */
+  MOE_ERR_UNSUPPORTED = 2,         /* valid but outside this library's limits     */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < moe_workspace_bytes(cfg)          */
+  MOE_ERR_HIP = 4                  /* a HIP launch failed                          */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+
+typedef struct {
+  int32_t num_tokens;   /* T >= 1                                                  */
+  int32_t hidden;       /* h: width of u and of the layer output                   */
+  int32_t inter;        /* SwiGLU intermediate width (routed and shared experts)   */
+  int32_t num_experts;  /* E = N_r routed experts, 1..256                          */
+  int32_t num_shared;   /* N_s shared experts, >= 0                                */
+  int32_t top_k;        /* K = K_r routed experts per token, 1..8, <= M*E/G        */
+  int32_t num_groups;   /* G expert groups ("nodes"); E % G == 0; G <= 64          */
+  int32_t top_groups;   /* M groups kept per token, 1..G                           */
+  int32_t group_topn;   /* biased affinities summed into a group score, 1..E/G     */
+  moe_dtype act_dtype;  /* F32 | BF16: u, router weight, y_rows and the output     */
+  moe_dtype w_dtype;    /* F32 | BF16 | E4M3: expert weights                       */
+} moe_config;
+
+/* Expert weights (device pointers), experts stacked routed-first.
+ *   w_gate, w_up : [E+Ns, inter, hidden]     w_down : [E+Ns, hidden, inter]
+ * in w_dtype.  For E4M3 (OCP e4m3fn codes, one byte each) every 128x128 block
+ * carries one fp32 scale, the weight being code_value * scale:
+ *   s_gate, s_up : [E+Ns, inter/128, hidden/128]   s_down : [E+Ns, hidden/128, inter/128]
+ * (devpress page, section 2: per-128x128-block weight quantisation).  The scale
+ * pointers must be NULL unless w_dtype == E4M3. */
+typedef struct {
+  const void  *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;
+} moe_expert_weights;
+
+/* Bytes of device workspace every entry point below may need for `cfg` (the
+ * maximum over them; moe_layer_forward needs the most).  Host-only; 0 when cfg
+ * is invalid.  The workspace must be 256-byte aligned; its contents on entry
+ * are irrelevant and on return undefined. */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Router ("深度解读报告" sections 2.2-2.4): for every token t
+ *   s_e = sigmoid(<x_t, w_router[e]>)            (fp32 accumulation)
+ *   sb_e = s_e + bias[e]                          (selection only)
+ *   keep the top_groups groups with the largest sum of group_topn best sb
+ *   topk_idx[t, :] = the top_k experts by sb within the kept groups,
+ *                    ordered by (sb descending, expert index ascending);
+ *                    exact ties go to the lower group / expert index
+ *   topk_gate[t, k] = s_{idx_k} / sum_j s_{idx_j}
+ * x [T, hidden] act_dtype; w_router [E, hidden] act_dtype; bias [E] fp32;
+ * topk_idx [T, K] int32 out; topk_gate [T, K] fp32 out. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_gate,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Permute: groups the T*K (token, expert) pairs by expert, tokens ascending
+ * within an expert; no pair is dropped ("深度解读报告" section 2.4).
+ * topk_idx [T, K] int32 in, every entry in [0, E) and distinct per token
+ * (out-of-range entries give undefined results but stay in bounds);
+ * expert_load [E] int32 out: pairs per expert, the batch-wide load of section 2.3;
+ * expert_offsets [E+1] int32 out: exclusive prefix sum of expert_load;
+ * row_token [T*K] int32 out: token of each expert-sorted row;
+ * pair_row [T*K] int32 out: row of pair (t, k), indexed t*K + k.
+ * Deterministic and atomic-free. */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* expert_load,
+                       int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* FP8 activation quantisation (devpress page section 2, 1x128 activation tiles;
+ * largest e4m3 value 448 from the stapisi blog section 6.2): for every row r and
+ * every 128-column block j of x [rows, cols] (act_dtype BF16, cols % 128 == 0)
+ *   scales[r, j] = amax / 448 in fp32 (1 when amax == 0)
+ *   q[r, c]      = e4m3 code of round-to-nearest-even(x[r, c] / scales[r, j]),
+ *                  saturated to +-448
+ * q [rows, cols] uint8 out; scales [rows, cols/128] fp32 out.  Used inside
+ * moe_grouped_ffn for E4M3 weights; exposed for stage testing. */
+moe_status moe_act_quant_e4m3(const moe_config* cfg, const void* x, int32_t rows, int32_t cols,
+                              uint8_t* q, float* scales, void* stream);
+
+/* Grouped expert FFN ("深度解读报告" section 2.2, SwiGLU experts): for each
+ * expert-sorted row r of expert e (rows [expert_offsets[e], expert_offsets[e+1]),
+ * token row_token[r]) and for the shared rows (row T*K + s*T + t is token t of
+ * shared expert E+s):
+ *   y_rows[r] = W_down,e (silu(W_gate,e u) * (W_up,e u)),  u = x[token(r)]
+ * x [T, hidden] act_dtype; expert_offsets [E+1], row_token [T*K] as produced by
+ * moe_permute; y_rows [T*K + T*Ns, hidden] act_dtype out.  fp32 accumulation;
+ * the intermediate h is held in act_dtype (BF16/F32) or, for E4M3 weights,
+ * re-quantised per 1x128 block to e4m3, like x. */
+moe_status moe_grouped_ffn(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
+                           const int32_t* row_token, const moe_expert_weights* weights,
+                           void* y_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine ("深度解读报告" section 2.2): for every token t
+ *   y[t] = [residual[t]] + sum_s y_rows[T*K + s*T + t] + sum_k topk_gate[t,k] * y_rows[pair_row[t*K+k]]
+ * summed in fp32 in that order, rounded once to act_dtype.
+ * y_rows [T*K + T*Ns, hidden], residual [T, hidden] (nullable), y [T, hidden]. */
+moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t* pair_row,
+                       const float* topk_gate, const void* residual, void* y, void* stream);
+
+/* Auxiliary-loss-free bias update ("深度解读报告" section 2.3): at the end of a
+ * step, from the whole batch's loads, for every expert e (fp32 arithmetic)
+ *   expert_load[e] * E > T*K  (overloaded)   ->  bias[e] -= gamma
+ *   expert_load[e] * E < T*K  (underloaded)  ->  bias[e] += gamma
+ *   otherwise unchanged.
+ * expert_load [E] int32 in; bias [E] fp32 in/out; gamma >= 0 (finite). */
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* expert_load, float gamma,
+                           float* bias, void* stream);
+
+/* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
+ * enqueued back to back on `stream` with no host synchronisation in between.
+ * residual (nullable) is u of "out = u + ..." in section 2.2; NULL gives the MoE
+ * branch alone.  topk_idx [T, K], topk_gate [T, K] and expert_load [E] are
+ * written as by the stage calls (expert_load feeds moe_bias_update). */
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* bias, const moe_expert_weights* weights,
+                             const void* residual, void* y, int32_t* topk_idx,
+                             float* topk_gate, int32_t* expert_load,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Static string naming a status code ("unknown status" for other values). */
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -70,12 +70,21 @@ class RouteResult:
         return self.near_tie_group | self.near_tie_expert
 
 
-def _top_sum_f32(v32: np.ndarray, n: int) -> np.float32:
-    """Sum of the n largest float32 values, added largest first in float32."""
-    acc = np.float32(0.0)
-    for val in sorted(v32.tolist(), reverse=True)[:n]:
-        acc = np.float32(acc + np.float32(val))
+def _top_sum_f32(v32: np.ndarray, n: int) -> np.ndarray:
+    """Sum of the n largest float32 values along the last axis, added largest first
+    in float32 arithmetic."""
+    desc = -np.sort(-v32, axis=-1)
+    acc = np.zeros(v32.shape[:-1], np.float32)
+    for i in range(n):
+        acc = (acc + desc[..., i]).astype(np.float32)
     return acc
+
+
+def _gap_at(values: np.ndarray, order: np.ndarray, pos: int) -> np.ndarray:
+    """values[order[pos-1]] - values[order[pos]] per row (float64)."""
+    a = np.take_along_axis(values, order[:, pos - 1:pos], 1)[:, 0]
+    b = np.take_along_axis(values, order[:, pos:pos + 1], 1)[:, 0]
+    return np.abs(a - b)
 
 
 def route(x, w_router, bias, num_groups: int, top_groups: int, group_topn: int,
@@ -90,7 +99,9 @@ def route(x, w_router, bias, num_groups: int, top_groups: int, group_topn: int,
       select the top_k experts by sb among the kept groups' experts
       gate_k = s_{idx_k} / sum_j s_{idx_j}         (unbiased affinities)
     Selection decisions use float32 s and sb (float32 add of the float32 bias) and a
-    float32 group-score sum; gates and near-tie gaps use float64.
+    float32 group-score sum; gates and near-tie gaps use float64.  Orderings are
+    stable sorts of the negated keys, so equal keys keep the lower index first.
+    All tokens are processed at once; rows are independent.
     """
     z, s = affinities(x, w_router)
     T, E = s.shape
@@ -98,35 +109,32 @@ def route(x, w_router, bias, num_groups: int, top_groups: int, group_topn: int,
     n = E // G
     b32 = np.asarray(bias, dtype=np.float32).reshape(E)
     sb = s + b32.astype(np.float64)
-    s32 = s.astype(np.float32)
-    sb32 = (s32 + b32).astype(np.float32)
+    sb32 = (s.astype(np.float32) + b32).astype(np.float32)
 
-    idx = np.zeros((T, K), np.int32)
-    gate = np.zeros((T, K), np.float64)
-    groups = np.zeros((T, M), np.int32)
+    # stage 1: group scores and the M kept groups
+    score32 = _top_sum_f32(sb32.reshape(T, G, n), group_topn)               # [T, G]
+    order_g = np.argsort(-score32, axis=1, kind="stable")
+    groups = order_g[:, :M].astype(np.int32)
     nt_g = np.zeros(T, bool)
+    if M < G:
+        score64 = (-np.sort(-sb.reshape(T, G, n), axis=2))[:, :, :group_topn].sum(2)
+        nt_g = _gap_at(score64, order_g, M) < NEAR_TIE
+
+    # stage 2: top-K experts among the kept groups' experts
+    kept = np.zeros((T, G), bool)
+    np.put_along_axis(kept, groups.astype(np.int64), True, axis=1)
+    cand = np.repeat(kept, n, axis=1)                                        # [T, E]
+    masked = np.where(cand, sb32, np.float32(-np.inf))
+    order_e = np.argsort(-masked, axis=1, kind="stable")
+    idx = order_e[:, :K].astype(np.int32)
     nt_e = np.zeros(T, bool)
-    nt_o = np.zeros(T, bool)
-    for t in range(T):
-        # stage 1: group scores and the M kept groups
-        score32 = [_top_sum_f32(sb32[t, j * n:(j + 1) * n], group_topn) for j in range(G)]
-        order_g = sorted(range(G), key=lambda j: (-score32[j], j))
-        kept = order_g[:M]
-        groups[t] = kept
-        if M < G:
-            score64 = [sum(sorted(sb[t, j * n:(j + 1) * n].tolist(), reverse=True)[:group_topn])
-                       for j in range(G)]
-            nt_g[t] = abs(score64[order_g[M - 1]] - score64[order_g[M]]) < NEAR_TIE
-        # stage 2: top-K experts among the kept groups' experts
-        cand = [e for j in kept for e in range(j * n, (j + 1) * n)]
-        order_e = sorted(cand, key=lambda e: (-sb32[t, e], e))
-        sel = order_e[:K]
-        idx[t] = sel
-        if K < len(cand):
-            nt_e[t] = abs(sb[t, order_e[K - 1]] - sb[t, order_e[K]]) < NEAR_TIE
-        nt_o[t] = any(abs(sb[t, sel[i]] - sb[t, sel[i + 1]]) < NEAR_TIE for i in range(K - 1))
-        ss = s[t, sel]
-        gate[t] = ss / ss.sum()
+    if K < M * n:
+        nt_e = _gap_at(np.where(cand, sb, -np.inf), order_e, K) < NEAR_TIE
+    sel_sb = np.take_along_axis(sb, order_e[:, :K], 1)
+    nt_o = np.any(np.abs(np.diff(sel_sb, axis=1)) < NEAR_TIE, axis=1) if K > 1 else np.zeros(T, bool)
+
+    ss = np.take_along_axis(s, order_e[:, :K], 1)
+    gate = ss / ss.sum(1, keepdims=True)
     return RouteResult(idx, gate, s, sb, groups, nt_g, nt_e, nt_o)
 
 

@@ -1,0 +1,85 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// fp32 -> OCP e4m3fn code: round to nearest even, saturate to +-448, keep the sign
+// of values that round to zero, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7Fu;
+  if (a >= 0x43e00000u) return sign | 0x7Eu;              // |v| >= 448
+  if (a < 0x3c800000u) {                                  // |v| < 2^-6: subnormal grid of 2^-9
+    float q = rintf(__uint_as_float(a) * 512.0f);         // exact scaling, RNE to 0..8
+    return sign | uint32_t(q);                            // 8 is the smallest normal, code 0x08
+  }
+  int e = int(a >> 23) - 127;                             // -6 .. 8
+  uint32_t mant = a & 0x7fffffu;
+  uint32_t m = mant >> 20;
+  uint32_t rem = mant & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
+    if (++m == 8u) { m = 0u; ++e; }
+  }
+  uint32_t code = (uint32_t(e + 7) << 3) | m;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Value of an e4m3fn code (codes 0x7F / 0xFF never reach the kernels: the
+// quantiser saturates and weight codes are finite by contract).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float mag = e == 0 ? float(m) * (1.0f / 512.0f)
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Row range of expert-group g in the grouped row space: routed expert e < E owns
+// rows [offsets[e], offsets[e+1]); shared expert E+s owns the T rows starting at
+// T*K + s*T, in token order.
+__device__ __forceinline__ void group_rows(const int32_t* offsets, int g, int E, int T, int TK,
+                                           int& r0, int& r1) {
+  if (g < E) {
+    r0 = offsets[g];
+    r1 = offsets[g + 1];
+  } else {
+    r0 = TK + (g - E) * T;
+    r1 = r0 + T;
+  }
+}
+
+// Token whose activation feeds grouped row r.
+__device__ __forceinline__ int row_token_of(const int32_t* row_token, int r, int T, int TK) {
+  return r < TK ? row_token[r] : (r - TK) % T;
+}
+
+}  // namespace moe

@@ -1,0 +1,47 @@
+// Internal launchers of the MoE layer kernels (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Workspace carved out of the caller's buffer (all pieces 256-byte aligned).
+struct Workspace {
+  float* z;            // [T, E] router logits, fp32
+  uint64_t* masks;     // [chunks, E] per-64-token-chunk bitmask of the tokens choosing e
+  int32_t* base;       // [chunks, E] rows of expert e in earlier chunks
+  int32_t* offsets;    // [E+1] expert offsets (layer forward)
+  int32_t* row_token;  // [T*K]
+  int32_t* pair_row;   // [T*K]
+  int32_t* tiles1;     // [E+Ns+1] m-tile prefix for the first expert GEMM
+  int32_t* tiles2;     // [E+Ns+1] m-tile prefix for the second expert GEMM
+  void* h;             // [rows, inter] act dtype, or e4m3 codes
+  float* h_scales;     // [rows, inter/128] (e4m3)
+  uint8_t* xq;         // [T, hidden] e4m3 codes
+  float* x_scales;     // [T, hidden/128]
+  void* y_rows;        // [rows, hidden] act dtype (layer forward)
+  size_t bytes;        // total bytes of the layout
+};
+
+constexpr int kTokChunk = 64;   // tokens per permute chunk (one 64-bit mask)
+
+Workspace workspace_layout(const moe_config& c, void* base);
+
+hipError_t launch_router_logits(const moe_config& c, const void* x, const void* w, float* z,
+                                hipStream_t s);
+hipError_t launch_router_select(const moe_config& c, const float* z, const float* bias,
+                                int32_t* idx, float* gate, hipStream_t s);
+hipError_t launch_permute(const moe_config& c, const int32_t* idx, int32_t* load,
+                          int32_t* offsets, int32_t* row_token, int32_t* pair_row,
+                          const Workspace& ws, hipStream_t s);
+hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
+                            hipStream_t s);
+hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
+                              const int32_t* row_token, const moe_expert_weights& w,
+                              void* y_rows, const Workspace& ws, hipStream_t s);
+hipError_t launch_combine(const moe_config& c, const void* y_rows, const int32_t* pair_row,
+                          const float* gate, const void* residual, void* y, hipStream_t s);
+hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float gamma,
+                              float* bias, hipStream_t s);
+
+}  // namespace moe

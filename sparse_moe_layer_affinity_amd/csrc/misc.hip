@@ -1,0 +1,147 @@
+// Combine, auxiliary-loss-free bias update and 1x128 FP8 activation quantisation.
+#include "kernels.h"
+
+namespace moe {
+
+// ---- combine ("深度解读报告" section 2.2) -------------------------------------
+// y[t] = [u_t] + sum_s y_rows[shared row of t] + sum_k g_tk * y_rows[pair_row[t,k]],
+// fp32 in that order, one rounding at the end.  One workgroup per token; each
+// thread owns 16-byte column vectors, so every row read is fully coalesced.
+__global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__ y_rows,
+                                                    const int32_t* __restrict__ pair_row,
+                                                    const float* __restrict__ gate,
+                                                    const uint16_t* __restrict__ residual,
+                                                    uint16_t* __restrict__ y, int T, int K,
+                                                    int Ns, int H) {
+  const int t = blockIdx.x;
+  const size_t TK = size_t(T) * K;
+  for (int v = threadIdx.x; v < H / 8; v += 256) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    auto add = [&](const uint16_t* src, float g, bool scaled) {
+      uint4 p = *reinterpret_cast<const uint4*>(src + size_t(v) * 8);
+      uint32_t wds[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float lo = bf16_bits_to_f32(wds[i] & 0xffffu), hi = bf16_bits_to_f32(wds[i] >> 16);
+        acc[2 * i] = scaled ? fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
+        acc[2 * i + 1] = scaled ? fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+      }
+    };
+    if (residual) add(residual + size_t(t) * H, 1.f, false);
+    for (int s = 0; s < Ns; ++s) add(y_rows + (TK + size_t(s) * T + t) * H, 1.f, false);
+    for (int k = 0; k < K; ++k) {
+      const int r = pair_row[size_t(t) * K + k];
+      if (r >= 0) add(y_rows + size_t(r) * H, gate[size_t(t) * K + k], true);
+    }
+    uint4 o;
+    o.x = f32_to_bf16_bits(acc[0]) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
+    o.y = f32_to_bf16_bits(acc[2]) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
+    o.z = f32_to_bf16_bits(acc[4]) | (uint32_t(f32_to_bf16_bits(acc[5])) << 16);
+    o.w = f32_to_bf16_bits(acc[6]) | (uint32_t(f32_to_bf16_bits(acc[7])) << 16);
+    *reinterpret_cast<uint4*>(y + size_t(t) * H + size_t(v) * 8) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32(const float* __restrict__ y_rows,
+                                                   const int32_t* __restrict__ pair_row,
+                                                   const float* __restrict__ gate,
+                                                   const float* __restrict__ residual,
+                                                   float* __restrict__ y, int T, int K, int Ns,
+                                                   int H) {
+  const int t = blockIdx.x;
+  const size_t TK = size_t(T) * K;
+  for (int v = threadIdx.x; v < H / 4; v += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (residual) {
+      float4 p = reinterpret_cast<const float4*>(residual + size_t(t) * H)[v];
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    for (int s = 0; s < Ns; ++s) {
+      float4 p = reinterpret_cast<const float4*>(y_rows + (TK + size_t(s) * T + t) * H)[v];
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = pair_row[size_t(t) * K + k];
+      if (r < 0) continue;
+      const float g = gate[size_t(t) * K + k];
+      float4 p = reinterpret_cast<const float4*>(y_rows + size_t(r) * H)[v];
+      acc.x = fmaf(g, p.x, acc.x); acc.y = fmaf(g, p.y, acc.y);
+      acc.z = fmaf(g, p.z, acc.z); acc.w = fmaf(g, p.w, acc.w);
+    }
+    reinterpret_cast<float4*>(y + size_t(t) * H)[v] = acc;
+  }
+}
+
+hipError_t launch_combine(const moe_config& c, const void* y_rows, const int32_t* pair_row,
+                          const float* gate, const void* residual, void* y, hipStream_t s) {
+  if (c.act_dtype == MOE_F32) {
+    hipLaunchKernelGGL(combine_f32, dim3(c.num_tokens), dim3(256), 0, s,
+                       static_cast<const float*>(y_rows), pair_row, gate,
+                       static_cast<const float*>(residual), static_cast<float*>(y),
+                       c.num_tokens, c.top_k, c.num_shared, c.hidden);
+  } else {
+    hipLaunchKernelGGL(combine_bf16, dim3(c.num_tokens), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(y_rows), pair_row, gate,
+                       static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y),
+                       c.num_tokens, c.top_k, c.num_shared, c.hidden);
+  }
+  return hipGetLastError();
+}
+
+// ---- bias update ("深度解读报告" section 2.3) ---------------------------------
+// Mean load is T*K/E; compared in integers.  Plain fp32 add / subtract.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ load,
+                                                          float gamma, int E, long long total,
+                                                          float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const long long scaled = 1LL * load[e] * E;
+  float b = bias[e];
+  if (scaled > total) b = __fsub_rn(b, gamma);
+  else if (scaled < total) b = __fadd_rn(b, gamma);
+  bias[e] = b;
+}
+
+hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float gamma,
+                              float* bias, hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(ceil_div(c.num_experts, 256)), dim3(256), 0, s,
+                     load, gamma, c.num_experts, 1LL * c.num_tokens * c.top_k, bias);
+  return hipGetLastError();
+}
+
+// ---- 1x128 e4m3 activation quantisation (devpress page, section 2) ----------
+// One wave per (row, 128-column block): each lane holds 2 columns; amax by
+// butterfly max; scale = amax / 448 (1 if amax == 0); code = RNE-saturate(x / scale).
+__global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x, int rows,
+                                                      int cols, uint8_t* __restrict__ q,
+                                                      float* __restrict__ scales) {
+  const int blocks_per_row = cols / 128;
+  const long long item = 1LL * blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= 1LL * rows * blocks_per_row) return;
+  const int l = threadIdx.x & 63;
+  const long long r = item / blocks_per_row;
+  const int j = int(item % blocks_per_row);
+  const size_t off = size_t(r) * cols + size_t(j) * 128 + 2 * l;
+  const uint32_t pr = *reinterpret_cast<const uint32_t*>(x + off);
+  const float v0 = bf16_bits_to_f32(pr & 0xffffu), v1 = bf16_bits_to_f32(pr >> 16);
+  float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  const uint32_t c0 = f32_to_e4m3_rne_sat(__fdiv_rn(v0, s));
+  const uint32_t c1 = f32_to_e4m3_rne_sat(__fdiv_rn(v1, s));
+  *reinterpret_cast<uint16_t*>(q + off) = uint16_t(c0 | (c1 << 8));
+  if (l == 0) scales[size_t(r) * blocks_per_row + j] = s;
+}
+
+hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
+                            hipStream_t s) {
+  const long long items = 1LL * rows * (cols / 128);
+  hipLaunchKernelGGL(act_quant_e4m3, dim3(unsigned((items + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), rows, cols, q, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

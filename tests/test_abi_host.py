@@ -1,0 +1,139 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared entry
+point, and rejects invalid arguments with the documented status before any launch.
+No call here reaches a kernel launch, so no GPU is needed."""
+import ctypes
+import subprocess
+
+import pytest
+
+import sparse_moe_layer_affinity_amd as moe
+from sparse_moe_layer_affinity_amd import binding as B
+
+ALIGNED = 1 << 20          # a fake, 256-byte aligned address: never dereferenced here
+
+
+def cfg(**kw):
+    base = dict(T=8192, hidden=7168, inter=2048, E=256, K=8, G=8, M=4, topn=2, Ns=1,
+                act="bf16", w="bf16")
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def code_of(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except B.MoeError as e:
+        return e.code
+    return B.MOE_OK
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = B.header_symbols()
+    assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_act_quant_e4m3",
+                          "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
+                          "moe_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    assert moe.moe_status_string(0) == "ok"
+    assert moe.moe_status_string(3) == "workspace too small"
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(E=250), B.MOE_ERR_INVALID_ARGUMENT),           # E % G != 0
+    (dict(M=0), B.MOE_ERR_INVALID_ARGUMENT),
+    (dict(M=9), B.MOE_ERR_INVALID_ARGUMENT),             # M > G
+    (dict(K=129, M=4), B.MOE_ERR_INVALID_ARGUMENT),      # K > M * E / G
+    (dict(topn=33), B.MOE_ERR_INVALID_ARGUMENT),         # group_topn > E / G
+    (dict(topn=0), B.MOE_ERR_INVALID_ARGUMENT),
+    (dict(T=0), B.MOE_ERR_INVALID_ARGUMENT),
+    (dict(Ns=-1), B.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=512, G=8), B.MOE_ERR_UNSUPPORTED),           # > 256 experts
+    (dict(K=9), B.MOE_ERR_UNSUPPORTED),                  # > 8 per token
+    (dict(topn=9), B.MOE_ERR_UNSUPPORTED),
+    (dict(w="e4m3", hidden=7000), B.MOE_ERR_UNSUPPORTED),  # FP8 needs 128-multiples
+    (dict(w="e4m3", inter=2000), B.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", w="bf16"), B.MOE_ERR_UNSUPPORTED),  # dtype combination
+    (dict(act="e4m3", w="e4m3"), B.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", w="f32", hidden=258), B.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_configs(kw, expected):
+    c = cfg(**kw)
+    assert moe.moe_workspace_bytes(c) == 0
+    got = code_of(B.moe_route, c, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1 << 40,
+                  stream=0)
+    assert got == expected
+
+
+def test_valid_configs_have_workspace():
+    for kw in [dict(), dict(T=128), dict(w="e4m3"), dict(T=16384),
+               dict(T=64, hidden=256, inter=128, E=16, K=4, G=4, M=2, act="f32", w="f32")]:
+        c = cfg(**kw)
+        n = moe.moe_workspace_bytes(c)
+        assert n > 0 and n % 256 == 0
+    # y_rows (T*(K+Ns) rows of h) dominates; FP8 holds h as one-byte codes
+    assert moe.moe_workspace_bytes(cfg(w="e4m3")) < moe.moe_workspace_bytes(cfg()) < 2 * 10 ** 9
+
+
+def test_null_pointers_and_workspace_checks():
+    c = cfg()
+    need = moe.moe_workspace_bytes(c)
+    A = ALIGNED
+    assert code_of(B.moe_route, c, 0, A, A, A, A, A, need, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_route, c, A, A, A, A, A, A, need - 1, stream=0) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert code_of(B.moe_route, c, A, A, A, A, A, A + 16, need, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT                             # misaligned workspace
+    assert code_of(B.moe_route, c, A, A, A, A, A, 0, need, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_permute, c, A, 0, A, A, A, A, need, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_permute, c, A, A, A, A, A, A, 0, stream=0) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert code_of(B.moe_combine, c, A, A, 0, None, A, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_bias_update, c, A, -1.0, A, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_bias_update, c, A, float("nan"), A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_bias_update, c, A, float("inf"), A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_bias_update, c, 0, 1e-3, A, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_act_quant_e4m3, c, A, 4, 100, A, A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT                             # cols not a multiple of 128
+    assert code_of(B.moe_act_quant_e4m3, cfg(act="f32", w="f32"), A, 4, 128, A, A, stream=0) == \
+        B.MOE_ERR_UNSUPPORTED
+
+
+def test_weight_scale_pointer_rules():
+    A = ALIGNED
+    need8 = moe.moe_workspace_bytes(cfg(w="e4m3"))
+    dense = dict(w_gate=A, w_up=A, w_down=A)
+    scaled = dict(dense, s_gate=A, s_up=A, s_down=A)
+    # bf16 weights must not carry scales; e4m3 weights must
+    assert code_of(B.moe_grouped_ffn, cfg(), A, A, A, scaled, A, A, need8, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_grouped_ffn, cfg(w="e4m3"), A, A, A, dense, A, A, need8, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_grouped_ffn, cfg(), A, A, A, dict(dense, w_up=0), A, A, need8,
+                   stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_layer_forward, cfg(), A, A, A, dense, None, A, A, A, 0, A, need8,
+                   stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.moe_bias_update(cfg(), torch.zeros(256, dtype=torch.int32), 1e-3,
+                          torch.zeros(256), stream=0)
+
+
+def test_config_struct_layout():
+    # 9 int32 fields followed by two C enums (int): 44 bytes, no padding
+    assert ctypes.sizeof(B.MoeConfig) == 44
+    assert ctypes.sizeof(B.MoeExpertWeights) == 6 * ctypes.sizeof(ctypes.c_void_p)

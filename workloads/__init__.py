@@ -205,3 +205,32 @@ def sample_rows(T: int, n: int, seed: int = 0) -> torch.Tensor:
         return torch.arange(T)
     g = _gen("cpu", tensor_seed(seed, "sample_rows", n, T))
     return torch.sort(torch.randperm(T, generator=g)[:n]).values
+
+
+def make_topk_indices(T: int, E: int, K: int, hot: int = 0, hot_weight: float = 0.0,
+                      seed: int = 0) -> torch.Tensor:
+    """Seeded [T, K] int32 expert choices, K distinct per token (a permutation-stage input).
+
+    With hot > 0 the first ``hot`` experts are favoured (their random keys are raised
+    by hot_weight), which leaves many experts empty for small T.
+    """
+    g = _gen("cpu", tensor_seed(seed, "topk", T, E * 16 + K))
+    keys = torch.rand((T, E), generator=g)
+    if hot:
+        keys[:, :hot] += hot_weight
+    return torch.topk(keys, K, dim=1).indices.to(torch.int32)
+
+
+def make_loads(E: int, T: int, K: int, seed: int = 0, at_mean: int = 4) -> torch.Tensor:
+    """Seeded per-expert loads summing to T*K, the first ``at_mean`` exactly at the mean
+    when T*K is a multiple of E (a bias-update-stage input)."""
+    g = _gen("cpu", tensor_seed(seed, "loads", E, T * K))
+    idx = torch.randint(0, E, (T * K,), generator=g)
+    load = torch.bincount(idx, minlength=E)
+    at_mean = min(at_mean, E - 1)           # one expert must absorb the surplus
+    if (T * K) % E == 0 and at_mean > 0:
+        mean = T * K // E
+        surplus = int((load[:at_mean] - mean).sum())
+        load[:at_mean] = mean
+        load[at_mean] += surplus              # keep the total
+    return load.to(torch.int32)
