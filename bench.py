@@ -102,7 +102,18 @@ def main():
                     choices=["prefill_bf16", "decode_bf16", "prefill_fp8", "skewed_bf16"])
     ap.add_argument("--cpu-tokens", type=int, default=16,
                     help="tokens in the oracle's bounded sample (0 skips it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")      # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               "multi-GPU path; the layer's sharding is described in the design notes.",

@@ -69,6 +69,12 @@ static moe_status validate(const moe_config* c) {
   const long long widest = c->hidden > c->inter ? c->hidden : c->inter;
   if (f32 && rows * widest >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (1LL * c->num_tokens * c->num_experts >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // MFMA kernels address x, h and each expert matrix through 32-bit buffer offsets
+  // below 2^31 (2^31 itself marks rows to read as zero)
+  const long long lim = (1LL << 31) - (1LL << 20);
+  if (!f32 && (2LL * c->num_tokens * c->hidden > lim || 2LL * rows * c->inter > lim ||
+               2LL * c->hidden * c->inter > lim))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

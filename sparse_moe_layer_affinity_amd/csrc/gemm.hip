@@ -10,16 +10,18 @@
 // Both operands are K-contiguous (x and h rows, weight rows), which is exactly the
 // operand layout of the MFMA: no transposes anywhere.
 //
-// bf16 kernel: v_mfma_f32_16x16x32_bf16, fp32 accumulation.  A workgroup owns a
-// BM x BN tile of one expert; the K loop stages 64-wide A and B slices through
-// padded LDS (row pitch 72 bf16 keeps the 16-lane fragment reads on distinct banks)
-// with the next slice's global loads in flight during the MFMAs.  GEMM1's B tile
-// stacks BN/2 gate rows over the matching BN/2 up rows and every wave owns the
-// same columns of both halves, so the SwiGLU epilogue runs in registers.
+// Expert GEMMs use grouped_gemm_big (below); the router logits use the simpler
+// 128 x 128 grouped_gemm_bf16 (v_mfma_f32_16x16x32_bf16, padded LDS, one slice of
+// prefetch).  In both, GEMM1's B tile stacks BN/2 gate rows over the matching BN/2
+// up rows and every wave owns the same columns of both halves, so the SwiGLU
+// epilogue runs in registers; accumulation is fp32.
 // Tile order: (expert, n-tile, m-tile) with m innermost, and the linear
 // workgroup id is remapped so that each of the 8 XCDs (workgroups are dispatched
 // round-robin over them) walks one contiguous stretch of that order: m-tiles of
 // one weight tile, and n-tiles of one expert's rows, then share the XCD's L2.
+
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -37,6 +39,7 @@ struct GemmArgs {
   int E, T, TK, G;           // routed experts, tokens, T*K, groups (E + Ns)
   int n_tiles;
   int gather;
+  int a_rows;                // rows of A (bounds of the activation buffer)
 };
 
 enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };
@@ -212,6 +215,300 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
   }
 }
 
+// ---- large-tile kernel for the expert GEMMs ---------------------------------
+// A workgroup of 4 waves owns a BM x BN tile (256 x 256: an average expert at
+// T = 8192 fits one m-tile); each wave owns a 128 x 128 sub-tile as 4 x 4 blocks
+// of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).  K advances in
+// 64-wide slices through two LDS buffers; global reads are buffer loads (one
+// descriptor per operand, per expert for the weights, K position in the scalar
+// offset; rows past the tile or past N read as zero through the range check).
+// Software pipeline per slice (four 16-wide K steps): each step's MFMAs run while
+// the next step's fragments are read from LDS; after step 0 the next slice moves
+// from registers into the other LDS buffer, one 16-byte write and one buffer load
+// per MFMA, so the loads of slice k+2 have about four steps to land; the single
+// barrier sits between steps 2 and 3 and orders LDS only (a full __syncthreads
+// would drain the in-flight loads).  Scheduling-group hints keep the compiler
+// from collapsing that order.  The number of valid 32-row blocks per wave (0, 1,
+// 2 or 4) is a compile-time variant picked once per wave, so short tail tiles of
+// an expert skip MFMA work without branches in the K loop.
+// LDS rows are 8 16-byte chunks; chunk c of row r is stored in slot
+// c ^ (r & 7) ^ ((r >> 3) & 1), which keeps the row-wise 128-byte stores and the
+// 32-row fragment reads free of bank conflicts in every 8- or 16-lane group.
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range: reads zero
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which on gfx9 means draining every outstanding global load at each
+// barrier; the K loop keeps its next slice's loads in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// silu(a) = a / (1 + e^-a) from the hardware exp2 and reciprocal (each about 1 ulp
+// in fp32); h is rounded to bf16 (relative step 2^-9) right after.
+__device__ __forceinline__ float silu_fast(float a) {
+  const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);
+  return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Instruction-order hints for the scheduler (one ordered chain per region):
+// masks 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write.
+template <int MASK, int SIZE>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (SIZE > 0) __builtin_amdgcn_sched_group_barrier(MASK, SIZE, 0);
+}
+// NR fragment reads, then NM MFMAs of which the first NX are each followed by one
+// LDS write and one buffer load (the register-to-LDS move of the next slice)
+template <int NR, int NM, int NX>
+__device__ __forceinline__ void sched_step() {
+  if constexpr (NX == 0) {
+    sched_group<0x100, NR>();
+    sched_group<0x008, NM>();
+  } else {
+    sched_group<0x100, NR>();
+    sched_group<0x008, 1>();
+    sched_group<0x200, 1>();
+    sched_group<0x020, 1>();
+    sched_step<0, NM - 1, NX - 1>();
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_big(GemmArgs a) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;   // 16-byte chunks per thread per slice
+  constexpr int ROWS = BM + BN;
+  constexpr int BN_OUT = MODE == kGatedBf16 ? BN / 2 : BN;
+  static_assert(CA * NT == BM * 8 && CB * NT == BN * 8, "tile/threads");
+  static_assert((NT / 8) % 16 == 0 && BM % 16 == 0, "store slots repeat every NT/8 rows");
+  static_assert(MODE != kGatedBf16 || ((WTN / 32) % 2 == 0 && CB % 2 == 0), "gated tiles pair gate/up");
+  __shared__ uint4 lds[2][ROWS * 8];
+
+  // ---- tile decode ------------------------------------------------------------
+  const int total_m = a.tile_off[a.G];
+  const int total = total_m * a.n_tiles;
+  const int b = blockIdx.x;
+  if (b >= total) return;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int xcd = b % kXcds, slot = b / kXcds;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+  int lo = 0, hi = a.G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_off[mid] * a.n_tiles <= logical) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int mtiles = a.tile_off[g + 1] - a.tile_off[g];
+  const int local = logical - a.tile_off[g] * a.n_tiles;
+  const int nt = local / mtiles, mt = local % mtiles;
+  int r0, r1;
+  group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
+  const int m0 = r0 + mt * BM;
+  const int mvalid = min(BM, r1 - m0);
+  const int n0 = nt * BN_OUT;
+  const int tid = threadIdx.x;
+  const int K = a.K;
+  const uint32_t row_bytes = uint32_t(K) * 2u;
+
+  // ---- buffer descriptors and per-lane offsets ----------------------------------
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(a.A, uint32_t(a.a_rows) * row_bytes);
+  const uint32_t b_bytes = uint32_t(a.N) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(a.B0 + size_t(g) * a.b_stride, b_bytes);
+  const __amdgpu_buffer_rsrc_t rb1 =
+      MODE == kGatedBf16 ? make_rsrc(a.B1 + size_t(g) * a.b_stride, b_bytes) : rb0;
+  const int trow = tid >> 3, kc0 = tid & 7;
+  uint32_t oa[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int row = trow + i * (NT / 8);
+    uint32_t o = kOob;
+    if (row < mvalid) {
+      const int r = m0 + row;
+      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
+      o = uint32_t(src) * row_bytes + kc0 * 16;
+    }
+    oa[i] = o;
+  }
+  // B chunk i covers weight row n0 + trow + i*NT/8 (gated: the second half is up rows)
+  constexpr int CBH = MODE == kGatedBf16 ? CB / 2 : CB;
+  const uint32_t ob = uint32_t(n0 + trow) * row_bytes + kc0 * 16;
+  const uint32_t ob_step = uint32_t(NT / 8) * row_bytes;
+  const int st_base = trow * 8 + lds_slot(trow, kc0);       // + i*NT for chunk i
+
+  uint4 ra[CA], rb[CB];
+  auto load_slice = [&](int k0) __attribute__((always_inline)) {
+    const int kb = k0 * 2;
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, oa[i], kb, 0));
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int ih = i < CBH ? i : i - CBH;
+      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          i < CBH ? rb0 : rb1, ob + uint32_t(ih) * ob_step, kb, 0));
+    }
+  };
+  auto store_slice = [&](uint4* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) buf[st_base + i * NT] = ra[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) buf[BM * 8 + st_base + i * NT] = rb[i];
+  };
+
+  // ---- wave geometry (wave index made scalar so tile-shape branches are uniform) --
+  // MFMA 32x32x16: lane l supplies row/column l%32 at K chunk (l/32) of each 16-wide
+  // K step, and holds output rows (r/4)*8 + (l/32)*4 + r%4, column l%32, r < 16.
+  constexpr int NI32 = WTM / 32, NJ32 = WTN / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int wm = w / WN, wn = w % WN;
+  const int ni_valid = min(NI32, max(0, (mvalid - wm * WTM + 31) >> 5));
+  const int a_base = (wm * WTM + (l & 31)) * 8;
+  int b_row0[NJ32];
+#pragma unroll
+  for (int j = 0; j < NJ32; ++j) {
+    int r;
+    if (MODE == kGatedBf16)
+      r = j < NJ32 / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - NJ32 / 2) * 32;
+    else
+      r = wn * WTN + j * 32;
+    b_row0[j] = (BM + r + (l & 31)) * 8;
+  }
+  const int nk = K / BK;   // even: K is a multiple of 128
+
+  // The wave's whole tile computation for NIV valid 32-row blocks (0, 1, 2 or 4),
+  // so the K loop itself has no branches: short tiles skip MFMA work per wave and
+  // waves without valid rows only load, store and synchronise.
+  auto body = [&](auto niv_tag) __attribute__((always_inline)) {
+    constexpr int NIV = decltype(niv_tag)::value;
+    f32x16_t acc[NIV > 0 ? NIV : 1][NJ32];
+#pragma unroll
+    for (int i = 0; i < NIV; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ32; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Fragments of one 16-wide K step (s = 0..3 within the 64-wide slice).  The
+    // fragment rows are 32-aligned + l%32, so the LDS slot depends only on l and s.
+    struct Frag {
+      bf16x8_t b[NJ32];
+      bf16x8_t a[NIV > 0 ? NIV : 1];
+    };
+    auto read_frags = [&](Frag& f, const uint4* buf, int s) __attribute__((always_inline)) {
+      if constexpr (NIV > 0) {
+        const int sl = lds_slot(l & 31, s * 2 + (l >> 5));
+#pragma unroll
+        for (int j = 0; j < NJ32; ++j) f.b[j] = __builtin_bit_cast(bf16x8_t, buf[b_row0[j] + sl]);
+#pragma unroll
+        for (int i = 0; i < NIV; ++i) f.a[i] = __builtin_bit_cast(bf16x8_t, buf[a_base + i * 256 + sl]);
+      }
+    };
+    auto mfmas = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NIV; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ32; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    // Slice kt from `cur` (its step-0 fragments already in f0).  Software pipeline:
+    // every step's MFMAs run while the next step's fragments are read; after step 0
+    // slice kt+1 moves from registers into `nxt` and the loads of slice kt+2 are
+    // issued (about four steps before they are needed); the one barrier sits between
+    // steps 2 and 3, so step 3's MFMAs cover the first reads of the next slice.
+    Frag f0, f1;
+    auto slice = [&](const uint4* cur, uint4* nxt, int kt, auto st, auto ld, auto next,
+                     auto prev) __attribute__((always_inline)) {
+      constexpr int NR = NIV > 0 ? NIV + NJ32 : 0, NM = NIV * NJ32;
+      constexpr int NX = decltype(st)::value && decltype(ld)::value ? (CA + CB < NM ? CA + CB : NM) : 0;
+      read_frags(f1, cur, 1);
+      mfmas(f0);
+      if constexpr (decltype(st)::value) store_slice(nxt);
+      if constexpr (decltype(ld)::value) load_slice((kt + 2) * BK);
+      read_frags(f0, cur, 2);
+      mfmas(f1);
+      read_frags(f1, cur, 3);
+      mfmas(f0);
+      // region order: this slice's step-0 reads with the previous slice's step-3
+      // MFMAs (none after the prologue), then steps 0..2, each preceded by the reads
+      // of the step after it
+      if constexpr (decltype(prev)::value) sched_step<NR, NM, 0>();
+      else sched_step<NR, 0, 0>();
+      sched_step<NR, NM, NX>();
+      sched_step<NR, NM, 0>();
+      sched_step<NR, NM, 0>();
+      lds_barrier();
+      if constexpr (decltype(next)::value) read_frags(f0, nxt, 0);
+      mfmas(f1);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+
+    load_slice(0);
+    store_slice(lds[0]);
+    load_slice(BK);
+    lds_barrier();
+    read_frags(f0, lds[0], 0);
+    // slice kt reads lds[kt & 1]; slices 0 .. nk-3 also store slice kt+1 and load
+    // slice kt+2, slice nk-2 only stores, slice nk-1 does neither (nk is even)
+    if (nk == 2) {
+      slice(lds[0], lds[1], 0, yes{}, no{}, yes{}, no{});
+      slice(lds[1], lds[0], 1, no{}, no{}, no{}, yes{});
+    } else {
+      slice(lds[0], lds[1], 0, yes{}, yes{}, yes{}, no{});
+      int kt = 1;
+      for (; kt + 4 <= nk; kt += 2) {       // pairs of full slices (odd, even)
+        slice(lds[1], lds[0], kt, yes{}, yes{}, yes{}, yes{});
+        slice(lds[0], lds[1], kt + 1, yes{}, yes{}, yes{}, yes{});
+      }
+      slice(lds[1], lds[0], kt, yes{}, yes{}, yes{}, yes{});           // kt == nk-3
+      slice(lds[0], lds[1], kt + 1, yes{}, no{}, yes{}, yes{});        // nk-2
+      slice(lds[1], lds[0], kt + 2, no{}, no{}, no{}, yes{});          // nk-1
+    }
+
+    // ---- epilogue ---------------------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * WTM + i * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+        if (rl >= mvalid) continue;
+        const size_t row = size_t(m0 + rl);
+        if (MODE == kGatedBf16) {
+#pragma unroll
+          for (int j = 0; j < NJ32 / 2; ++j) {
+            const int col = n0 + wn * (WTN / 2) + j * 32 + (l & 31);
+            const float hv = silu_fast(acc[i][j][r]) * acc[i][j + NJ32 / 2][r];
+            if (col < a.N) static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(hv);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ32; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + (l & 31);
+            if (col < a.N)
+              static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(acc[i][j][r]);
+          }
+        }
+      }
+    }
+  };
+  static_assert(NI32 == 4, "row-block variants assume 4 blocks of 32 rows per wave");
+  if (ni_valid > 2) body(std::integral_constant<int, 4>{});
+  else if (ni_valid > 1) body(std::integral_constant<int, 2>{});
+  else if (ni_valid > 0) body(std::integral_constant<int, 1>{});
+  else body(std::integral_constant<int, 0>{});
+}
+
 // m-tile prefix over groups for two tile heights, one workgroup (G <= 512).
 __global__ __launch_bounds__(512) void build_tiles(const int32_t* __restrict__ offsets, int E,
                                                    int Ns, int T, int TK, int bm1, int bm2,
@@ -296,7 +593,8 @@ __global__ __launch_bounds__(256) void gemm2_f32(const float* __restrict__ h,
 }
 
 // ---- launch configuration ---------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;
+constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;      // router logits
+constexpr int kEBM = 256, kEBN = 256, kEWM = 2, kEWN = 2;  // expert GEMMs
 
 static int m_tiles_upper(const moe_config& c, int bm) {
   const long long TK = 1LL * c.num_tokens * c.top_k;
@@ -344,7 +642,7 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
     return hipGetLastError();
   }
   if (c.w_dtype != MOE_BF16) return hipErrorNotSupported;
-  hipLaunchKernelGGL(build_tiles, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, TK, kBM, kBM,
+  hipLaunchKernelGGL(build_tiles, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, TK, kEBM, kEBM,
                      ws.tiles1, ws.tiles2);
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
@@ -362,14 +660,16 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   a.T = T;
   a.TK = TK;
   a.G = G;
-  a.n_tiles = ceil_div(I, kBN / 2);
+  a.n_tiles = ceil_div(I, kEBN / 2);
   a.gather = 1;
-  hipLaunchKernelGGL((grouped_gemm_bf16<kBM, kBN, kWM, kWN, kGatedBf16>),
-                     dim3(m_tiles_upper(c, kBM) * a.n_tiles), dim3(kWM * kWN * 64), 0, s, a);
+  a.a_rows = T;
+  hipLaunchKernelGGL((grouped_gemm_big<kEBM, kEBN, kEWM, kEWN, kGatedBf16>),
+                     dim3(m_tiles_upper(c, kEBM) * a.n_tiles), dim3(kEWM * kEWN * 64), 0, s, a);
   GemmArgs d = a;
   d.A = static_cast<const uint16_t*>(ws.h);
   d.row_token = nullptr;
   d.gather = 0;
+  d.a_rows = rows;
   d.tile_off = ws.tiles2;
   d.B0 = static_cast<const uint16_t*>(w.w_down);
   d.B1 = nullptr;
@@ -378,9 +678,9 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   d.ldc = H;
   d.N = H;
   d.K = I;
-  d.n_tiles = ceil_div(H, kBN);
-  hipLaunchKernelGGL((grouped_gemm_bf16<kBM, kBN, kWM, kWN, kPlainBf16>),
-                     dim3(m_tiles_upper(c, kBM) * d.n_tiles), dim3(kWM * kWN * 64), 0, s, d);
+  d.n_tiles = ceil_div(H, kEBN);
+  hipLaunchKernelGGL((grouped_gemm_big<kEBM, kEBN, kEWM, kEWN, kPlainBf16>),
+                     dim3(m_tiles_upper(c, kEBM) * d.n_tiles), dim3(kEWM * kEWN * 64), 0, s, d);
   return hipGetLastError();
 }
 
