@@ -98,11 +98,21 @@ def dequantize_blocks_128(codes, scales) -> np.ndarray:
     return vals * np.repeat(np.repeat(sc, 128, axis=0), 128, axis=1)[:n, :k]
 
 
+def _round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), returned as float32."""
+    import torch
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
 def expert_ffn_fp8_emulated(u, w_gate, w_up, w_down) -> np.ndarray:
     """Diagnostic FP8 expert: u and the SwiGLU output h are each quantised per 1x128
     along their own K dimension before the GEMM that consumes them; weights are
-    already dequantised float64 arrays.  All products and sums in float64."""
+    already dequantised float64 arrays.  Products and sums in float64.
+
+    The pages fix no storage precision for h between the two GEMMs; the kernels
+    hold it in bf16, so the FP8 codes of h are decided on the bf16-rounded value
+    (a code is decided in the kernel's precision where the pages are silent)."""
     uq = dequantize_1x128(*quantize_1x128(np.asarray(_f64(u), np.float32)))
     h = silu(uq @ _f64(w_gate).T) * (uq @ _f64(w_up).T)
-    hq = dequantize_1x128(*quantize_1x128(h.astype(np.float32)))
+    hq = dequantize_1x128(*quantize_1x128(_round_bf16(h)))
     return hq @ _f64(w_down).T
