@@ -32,7 +32,8 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   w.pair_row = static_cast<int32_t*>(take(TK * 4));
   w.tiles1 = static_cast<int32_t*>(take((G + 1) * 4));
   w.tiles2 = static_cast<int32_t*>(take((G + 1) * 4));
-  w.h = take(rows * I * (fp8 ? 1 : act_bytes(c)));
+  w.h = take(rows * I * act_bytes(c));
+  w.hq = fp8 ? static_cast<uint8_t*>(take(rows * I)) : nullptr;
   w.h_scales = fp8 ? static_cast<float*>(take(rows * (I / 128) * 4)) : nullptr;
   w.xq = fp8 ? static_cast<uint8_t*>(take(T * H)) : nullptr;
   w.x_scales = fp8 ? static_cast<float*>(take(T * (H / 128) * 4)) : nullptr;

@@ -22,27 +22,11 @@
 
 #include <type_traits>
 
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace moe {
 
-struct GemmArgs {
-  const uint16_t* A;         // bf16 activations: x [T, K] (gather) or [rows, K]
-  const int32_t* row_token;  // gather map of routed rows (gather only)
-  const int32_t* offsets;    // [E+1] expert offsets (nullptr: single group of T rows)
-  const int32_t* tile_off;   // [G+1] m-tile prefix per group (nullptr: single group)
-  const uint16_t* B0;        // weights [G][N][K] bf16 (GEMM1: gate)
-  const uint16_t* B1;        // GEMM1: up
-  long long b_stride;        // elements per expert
-  void* C;                   // output [rows, ldc]
-  int ldc, N, K;             // N = output columns (GEMM1: intermediate columns)
-  int E, T, TK, G;           // routed experts, tokens, T*K, groups (E + Ns)
-  int n_tiles;
-  int gather;
-  int a_rows;                // rows of A (bounds of the activation buffer)
-};
 
-enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };
 
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
@@ -234,32 +218,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
 // LDS rows are 8 16-byte chunks; chunk c of row r is stored in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1), which keeps the row-wise 128-byte stores and the
 // 32-row fragment reads free of bank conflicts in every 8- or 16-lane group.
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
-
-__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
-}
-
-constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range: reads zero
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
-// memory, which on gfx9 means draining every outstanding global load at each
-// barrier; the K loop keeps its next slice's loads in flight across barriers.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// silu(a) = a / (1 + e^-a) from the hardware exp2 and reciprocal (each about 1 ulp
-// in fp32); h is rounded to bf16 (relative step 2^-9) right after.
-__device__ __forceinline__ float silu_fast(float a) {
-  const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);
-  return a * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
 // Instruction-order hints for the scheduler (one ordered chain per region):
 // masks 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write.
 template <int MASK, int SIZE>
@@ -624,6 +582,14 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   return hipGetLastError();
 }
 
+hipError_t launch_build_tiles(const moe_config& c, const int32_t* offsets, int bm1, int bm2,
+                              int32_t* t1, int32_t* t2, hipStream_t s) {
+  const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
+  hipLaunchKernelGGL(build_tiles, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, T * c.top_k, bm1,
+                     bm2, t1, t2);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
                               const int32_t* row_token, const moe_expert_weights& w,
                               void* y_rows, const Workspace& ws, hipStream_t s) {
@@ -641,9 +607,10 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
                        static_cast<float*>(y_rows));
     return hipGetLastError();
   }
-  if (c.w_dtype != MOE_BF16) return hipErrorNotSupported;
-  hipLaunchKernelGGL(build_tiles, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, TK, kEBM, kEBM,
-                     ws.tiles1, ws.tiles2);
+  if (c.w_dtype == MOE_E4M3)
+    return launch_grouped_ffn_fp8(c, x, offsets, row_token, w, y_rows, ws, s);
+  hipError_t err = launch_build_tiles(c, offsets, kEBM, kEBM, ws.tiles1, ws.tiles2, s);
+  if (err != hipSuccess) return err;
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
   a.row_token = row_token;

@@ -1,0 +1,54 @@
+// Shared pieces of the grouped GEMM kernels (bf16 and FP8).
+#pragma once
+
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace moe {
+
+struct GemmArgs {
+  const uint16_t* A;         // bf16 activations: x [T, K] (gather) or [rows, K]
+  const int32_t* row_token;  // gather map of routed rows (gather only)
+  const int32_t* offsets;    // [E+1] expert offsets (nullptr: single group of T rows)
+  const int32_t* tile_off;   // [G+1] m-tile prefix per group (nullptr: single group)
+  const uint16_t* B0;        // weights [G][N][K] bf16 (GEMM1: gate)
+  const uint16_t* B1;        // GEMM1: up
+  long long b_stride;        // elements per expert
+  void* C;                   // output [rows, ldc]
+  int ldc, N, K;             // N = output columns (GEMM1: intermediate columns)
+  int E, T, TK, G;           // routed experts, tokens, T*K, groups (E + Ns)
+  int n_tiles;
+  int gather;
+  int a_rows;                // rows of A (bounds of the activation buffer)
+};
+
+enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range: reads zero
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which on gfx9 means draining every outstanding global load at each
+// barrier; the K loop keeps its next slice's loads in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// silu(a) = a / (1 + e^-a) from the hardware exp2 and reciprocal (each about 1 ulp
+// in fp32); h is rounded to bf16 (relative step 2^-9) right after.
+__device__ __forceinline__ float silu_fast(float a) {
+  const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);
+  return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace moe

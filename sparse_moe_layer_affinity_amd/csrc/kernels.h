@@ -15,8 +15,9 @@ struct Workspace {
   int32_t* pair_row;   // [T*K]
   int32_t* tiles1;     // [E+Ns+1] m-tile prefix for the first expert GEMM
   int32_t* tiles2;     // [E+Ns+1] m-tile prefix for the second expert GEMM
-  void* h;             // [rows, inter] act dtype, or e4m3 codes
-  float* h_scales;     // [rows, inter/128] (e4m3)
+  void* h;             // [rows, inter] act dtype (SwiGLU output of the first GEMM)
+  uint8_t* hq;         // [rows, inter] e4m3 codes of h (e4m3 weights)
+  float* h_scales;     // [rows, inter/128] (e4m3 weights)
   uint8_t* xq;         // [T, hidden] e4m3 codes
   float* x_scales;     // [T, hidden/128]
   void* y_rows;        // [rows, hidden] act dtype (layer forward)
@@ -39,6 +40,9 @@ hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
                               const int32_t* row_token, const moe_expert_weights& w,
                               void* y_rows, const Workspace& ws, hipStream_t s);
+hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int32_t* offsets,
+                                  const int32_t* row_token, const moe_expert_weights& w,
+                                  void* y_rows, const Workspace& ws, hipStream_t s);
 hipError_t launch_combine(const moe_config& c, const void* y_rows, const int32_t* pair_row,
                           const float* gate, const void* residual, void* y, hipStream_t s);
 hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float gamma,

@@ -79,8 +79,8 @@ def test_valid_configs_have_workspace():
         c = cfg(**kw)
         n = moe.moe_workspace_bytes(c)
         assert n > 0 and n % 256 == 0
-    # y_rows (T*(K+Ns) rows of h) dominates; FP8 holds h as one-byte codes
-    assert moe.moe_workspace_bytes(cfg(w="e4m3")) < moe.moe_workspace_bytes(cfg()) < 2 * 10 ** 9
+    # y_rows and h (T*(K+Ns) rows each) dominate; FP8 adds one-byte codes of x and h
+    assert moe.moe_workspace_bytes(cfg()) < moe.moe_workspace_bytes(cfg(w="e4m3")) < 2 * 10 ** 9
 
 
 def test_null_pointers_and_workspace_checks():

@@ -1,0 +1,82 @@
+"""GPU parity of the FP8 path (e4m3 weights with 128x128 fp32 block scales, activations
+quantised per 1x128 on the fly) against the float64 oracle.
+
+Two references: the fp32 oracle (dequantised weights, unquantised activations: the
+6e-2 bound of the FP8 workload) and the oracle's FP8-emulating expert (x and h
+quantised per 1x128 exactly as the kernels do), which pins the kernel more tightly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_affinity_amd as moe
+import workloads
+from gpu_harness import (TOL, compare_routing, config_of, expert_getter, inputs_on_gpu,
+                         layer_forward, log, oracle_route, rel_err, weights_of, workspace)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = dict(hidden=256, inter=256, E=16, K=4, G=4, M=2, topn=2)
+# Against the fp32 oracle the FP8 method itself (exact quantisation, float64 sums)
+# is off by ~4.4e-2 in the global norm at >= 64 rows and up to the per-row figure
+# (~6e-2, more for a single row) when only a few rows are compared; the 6e-2 bar
+# applies from 64 rows, 0.1 below.  Against the FP8-emulating oracle the remaining
+# difference is the few e4m3 codes of h that flip because the kernel's h carries
+# fp32-accumulation rounding before its bf16 rounding: one code step is 1/16 of
+# the value, a handful per row out of `inter` terms gives a few 1e-3 (measured
+# 3e-3..9e-3 on MI355X); bound 2e-2.
+EMU_TOL = 2e-2
+
+
+def fp32_tol(n_rows):
+    return TOL["e4m3"] if n_rows >= 64 else 0.1
+
+
+def _check(cfg, d, out, rows=None):
+    r = oracle_route(cfg, d)
+    ties = compare_routing(r, out["idx"], out["gate"], where=cfg.name)
+    same = np.all(out["idx"].cpu().numpy() == r.idx, axis=1)
+    rows = np.arange(cfg.T) if rows is None else np.asarray(rows)
+    rows = rows[same[rows]]
+    get = expert_getter(cfg, d)
+    got = out["y"].float().cpu().numpy()[rows]
+    ref = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows)
+    err = rel_err(got, ref)
+    emu = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows,
+                              ffn=oracle.expert_ffn_fp8_emulated)
+    err_emu = rel_err(got, emu)
+    log(f"  {cfg.name}: rows {len(rows)}, near-ties {ties}, rel err vs fp32 {err:.3e}, "
+        f"vs fp8-emulating {err_emu:.3e}")
+    assert err <= fp32_tol(len(rows)), err
+    assert err_emu <= EMU_TOL, err_emu
+
+
+@pytest.mark.parametrize("over", [dict(T=37), dict(T=1), dict(T=300, seed=1), dict(T=64, Ns=0),
+                                  dict(T=129, Ns=2, bias="uniform", bias_range=0.02),
+                                  dict(T=200, E=64, G=8, M=4, K=6, inter=384, hidden=384)])
+def test_layer_small_fp8(over):
+    cfg = workloads.get("prefill_fp8").replace(**{**SMALL, **over})
+    log(f"layer small fp8 {over}")
+    d = inputs_on_gpu(cfg)
+    _check(cfg, d, layer_forward(cfg, d))
+
+
+def test_fp8_decode_shape():
+    cfg = workloads.get("prefill_fp8").replace(T=128, bias="uniform", bias_range=0.01,
+                                               compare_rows=None)
+    log("layer fp8 decode shape (T=128, h=7168, E=256)")
+    d = inputs_on_gpu(cfg)
+    out = layer_forward(cfg, d)
+    _check(cfg, d, out)
+    again = layer_forward(cfg, d)
+    assert torch.equal(out["y"], again["y"]), "run-to-run difference"
+
+
+@pytest.mark.slow
+def test_layer_prefill_fp8():
+    cfg = workloads.get("prefill_fp8")
+    log("layer prefill_fp8 (T=8192): routing on all tokens, output on 512 sampled rows")
+    d = inputs_on_gpu(cfg)
+    out = layer_forward(cfg, d)
+    _check(cfg, d, out, rows=workloads.sample_rows(cfg.T, cfg.compare_rows).numpy())
