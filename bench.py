@@ -100,7 +100,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_bf16",
                     choices=["prefill_bf16", "decode_bf16", "prefill_fp8", "skewed_bf16"])
-    ap.add_argument("--cpu-tokens", type=int, default=16,
+    ap.add_argument("--cpu-tokens", type=int, default=48,
                     help="tokens in the oracle's bounded sample (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
