@@ -24,7 +24,7 @@ Workspace workspace_layout(const moe_config& c, void* base) {
     off += align256(bytes);
     return r;
   };
-  w.z = static_cast<float*>(take(T * E * 4));
+  w.z = static_cast<float*>(take(size_t(router_splits(c)) * T * E * 4));
   w.masks = static_cast<uint64_t*>(take(chunks * E * 8));
   w.base = static_cast<int32_t*>(take(chunks * E * 4));
   w.offsets = static_cast<int32_t*>(take((E + 1) * 4));

@@ -79,6 +79,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int K = a.K;
+  // split-K (router): this block sums K range [kbeg, kbeg + klen) into partial ks
+  const int ks = blockIdx.y;
+  const int kbeg = ks * a.k_chunk;
+  const int klen = min(a.k_chunk, K - kbeg);
 
   // ---- per-thread global source pointers ----------------------------------
   const uint16_t* pa[CA];
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
     const int row = min(c >> 3, mvalid - 1);      // padding rows re-read the last valid row
     const int r = m0 + row;
     const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-    pa[i] = a.A + size_t(src) * K + (c & 7) * 8;
+    pa[i] = a.A + size_t(src) * K + kbeg + (c & 7) * 8;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
       n = n0 + brow - BN / 2;
     }
     n = min(n, a.N - 1);
-    pb[i] = base + size_t(g) * a.b_stride + size_t(n) * K + (c & 7) * 8;
+    pb[i] = base + size_t(g) * a.b_stride + size_t(n) * K + kbeg + (c & 7) * 8;
   }
 
   uint4 ra[CA], rb[CB];
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
+  const int nk = klen / BK;
   load_slice(0);
   for (int kt = 0; kt < nk; ++kt) {
     store_slice();
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
           const int col = n0 + wn * WTN + j * 16 + (l & 15);
           if (col >= a.N) continue;
           if (MODE == kPlainF32)
-            static_cast<float*>(a.C)[row * a.ldc + col] = acc[i][j][q];
+            static_cast<float*>(a.C)[ks * a.c_split_stride + row * a.ldc + col] = acc[i][j][q];
           else
             static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(acc[i][j][q]);
         }
@@ -576,9 +580,11 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   a.TK = 0;
   a.G = 1;
   a.n_tiles = ceil_div(c.num_experts, kBN);
+  a.k_chunk = router_k_chunk(c);
+  a.c_split_stride = 1LL * c.num_tokens * c.num_experts;
   const int grid = ceil_div(c.num_tokens, kBM) * a.n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_bf16<kBM, kBN, kWM, kWN, kPlainF32>), dim3(grid),
-                     dim3(kWM * kWN * 64), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_bf16<kBM, kBN, kWM, kWN, kPlainF32>),
+                     dim3(grid, router_splits(c)), dim3(kWM * kWN * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -21,6 +21,8 @@ struct GemmArgs {
   int n_tiles;
   int gather;
   int a_rows;                // rows of A (bounds of the activation buffer)
+  int k_chunk;               // split-K: K elements per blockIdx.y (router only)
+  long long c_split_stride;  // split-K: elements between the partial outputs
 };
 
 enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };

@@ -7,7 +7,7 @@ namespace moe {
 
 // Workspace carved out of the caller's buffer (all pieces 256-byte aligned).
 struct Workspace {
-  float* z;            // [T, E] router logits, fp32
+  float* z;            // [splits, T, E] router logit partials, fp32
   uint64_t* masks;     // [chunks, E] per-64-token-chunk bitmask of the tokens choosing e
   int32_t* base;       // [chunks, E] rows of expert e in earlier chunks
   int32_t* offsets;    // [E+1] expert offsets (layer forward)
@@ -27,6 +27,23 @@ struct Workspace {
 constexpr int kTokChunk = 64;   // tokens per permute chunk (one 64-bit mask)
 
 Workspace workspace_layout(const moe_config& c, void* base);
+
+// Split-K factor of the bf16 router-logits GEMM: enough 128 x 128 tiles x splits to
+// fill the chip at small T; the fp32 partials are summed in order by the selection
+// kernel.  1 for fp32 activations.
+inline int router_splits(const moe_config& c) {
+  if (c.act_dtype == MOE_F32) return 1;
+  const int tiles = ((c.num_tokens + 127) / 128) * ((c.num_experts + 127) / 128);
+  int s = 256 / tiles;
+  const int kmax = c.hidden / 128;
+  s = s < 1 ? 1 : (s > kmax ? kmax : s);
+  const int chunk = ((c.hidden + s - 1) / s + 63) / 64 * 64;
+  return (c.hidden + chunk - 1) / chunk;
+}
+inline int router_k_chunk(const moe_config& c) {
+  const int s = router_splits(c);
+  return ((c.hidden + s - 1) / s + 63) / 64 * 64;
+}
 
 hipError_t launch_router_logits(const moe_config& c, const void* x, const void* w, float* z,
                                 hipStream_t s);

@@ -112,34 +112,48 @@ hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float ga
 }
 
 // ---- 1x128 e4m3 activation quantisation (devpress page, section 2) ----------
-// One wave per (row, 128-column block): each lane holds 2 columns; amax by
-// butterfly max; scale = amax / 448 (1 if amax == 0); code = RNE-saturate(x / scale).
+// Each lane owns 8 consecutive columns (one 16-byte load); 16 lanes cover one
+// 128-column block and a wave four blocks.  amax by butterfly max inside the 16
+// lanes; scale = amax / 448 (1 if amax == 0); code = RNE-saturate(x / scale).
 __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x, int rows,
                                                       int cols, uint8_t* __restrict__ q,
                                                       float* __restrict__ scales) {
-  const int blocks_per_row = cols / 128;
-  const long long item = 1LL * blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= 1LL * rows * blocks_per_row) return;
-  const int l = threadIdx.x & 63;
-  const long long r = item / blocks_per_row;
-  const int j = int(item % blocks_per_row);
-  const size_t off = size_t(r) * cols + size_t(j) * 128 + 2 * l;
-  const uint32_t pr = *reinterpret_cast<const uint32_t*>(x + off);
-  const float v0 = bf16_bits_to_f32(pr & 0xffffu), v1 = bf16_bits_to_f32(pr >> 16);
-  float amax = fmaxf(fabsf(v0), fabsf(v1));
+  const int bpr = cols / 128;                                   // blocks per row
+  const long long blk = (1LL * blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + ((threadIdx.x >> 4) & 3);
+  const bool valid = blk < 1LL * rows * bpr;
+  const int l16 = threadIdx.x & 15;
+  const long long r = valid ? blk / bpr : 0;
+  const int j = valid ? int(blk % bpr) : 0;
+  const size_t off = size_t(r) * cols + size_t(j) * 128 + size_t(l16) * 8;
+  uint4 p = make_uint4(0, 0, 0, 0);
+  if (valid) p = *reinterpret_cast<const uint4*>(x + off);
+  const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
+  float v[8];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(wd[i] & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (!valid) return;
   const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  const uint32_t c0 = f32_to_e4m3_rne_sat(__fdiv_rn(v0, s));
-  const uint32_t c1 = f32_to_e4m3_rne_sat(__fdiv_rn(v1, s));
-  *reinterpret_cast<uint16_t*>(q + off) = uint16_t(c0 | (c1 << 8));
-  if (l == 0) scales[size_t(r) * blocks_per_row + j] = s;
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32_to_e4m3_rne_sat(__fdiv_rn(v[i], s));
+  *reinterpret_cast<uint2*>(q + off) =
+      make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                 c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  if (l16 == 0) scales[size_t(r) * bpr + j] = s;
 }
 
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
                             hipStream_t s) {
-  const long long items = 1LL * rows * (cols / 128);
-  hipLaunchKernelGGL(act_quant_e4m3, dim3(unsigned((items + 3) / 4)), dim3(256), 0, s,
+  const long long blocks = 1LL * rows * (cols / 128);
+  hipLaunchKernelGGL(act_quant_e4m3, dim3(unsigned((blocks + 15) / 16)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), rows, cols, q, scales);
   return hipGetLastError();
 }

@@ -45,8 +45,8 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 }
 
 __global__ __launch_bounds__(kSelWaves * 64) void router_select(
-    const float* __restrict__ z, const float* __restrict__ bias, int T, int E, int G, int M,
-    int topn, int K, int32_t* __restrict__ idx_out, float* __restrict__ gate_out) {
+    const float* __restrict__ z, int splits, const float* __restrict__ bias, int T, int E, int G,
+    int M, int topn, int K, int32_t* __restrict__ idx_out, float* __restrict__ gate_out) {
   __shared__ float sb_lds[kSelWaves][256];
   __shared__ float s_lds[kSelWaves][256];
   const int w = threadIdx.x / 64, l = threadIdx.x % 64;
@@ -61,7 +61,10 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
     int e = l + 64 * j;
     v[j] = -INFINITY;
     if (active && e < E) {
-      float s = 1.0f / (1.0f + expf(-z[size_t(t) * E + e]));
+      // logit = the split-K partials summed in split order (one partial unless split)
+      float zz = z[size_t(t) * E + e];
+      for (int p = 1; p < splits; ++p) zz += z[(size_t(p) * T + t) * E + e];
+      float s = 1.0f / (1.0f + expf(-zz));
       float sb = s + bias[e];
       s_lds[w][e] = s;
       sb_lds[w][e] = sb;
@@ -153,7 +156,7 @@ hipError_t launch_router_logits(const moe_config& c, const void* x, const void* 
 hipError_t launch_router_select(const moe_config& c, const float* z, const float* bias,
                                 int32_t* idx, float* gate, hipStream_t s) {
   hipLaunchKernelGGL(router_select, dim3(ceil_div(c.num_tokens, kSelWaves)),
-                     dim3(kSelWaves * 64), 0, s, z, bias, c.num_tokens, c.num_experts,
+                     dim3(kSelWaves * 64), 0, s, z, router_splits(c), bias, c.num_tokens, c.num_experts,
                      c.num_groups, c.top_groups, c.group_topn, c.top_k, idx, gate);
   return hipGetLastError();
 }
