@@ -10,15 +10,12 @@
 // Both operands are K-contiguous (x and h rows, weight rows), which is exactly the
 // operand layout of the MFMA: no transposes anywhere.
 //
-// Expert GEMMs use grouped_gemm_big (below); the router logits use the simpler
-// 128 x 128 grouped_gemm_bf16 (v_mfma_f32_16x16x32_bf16, padded LDS, one slice of
-// prefetch).  In both, GEMM1's B tile stacks BN/2 gate rows over the matching BN/2
-// up rows and every wave owns the same columns of both halves, so the SwiGLU
-// epilogue runs in registers; accumulation is fp32.
-// Tile order: (expert, n-tile, m-tile) with m innermost, and the linear
-// workgroup id is remapped so that each of the 8 XCDs (workgroups are dispatched
-// round-robin over them) walks one contiguous stretch of that order: m-tiles of
-// one weight tile, and n-tiles of one expert's rows, then share the XCD's L2.
+// Expert GEMMs use grouped_gemm_dma (below: row blocks of up to 320 rows, operands
+// loaded straight into LDS); the router logits use the simpler 128 x 128
+// grouped_gemm_bf16 (v_mfma_f32_16x16x32_bf16, padded LDS, one slice of prefetch).
+// In both, GEMM1's B tile stacks BN/2 gate rows over the matching BN/2 up rows and
+// every wave owns the same columns of both halves, so the SwiGLU epilogue runs in
+// registers; accumulation is fp32.
 
 #include <type_traits>
 
@@ -203,77 +200,111 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
   }
 }
 
-// ---- large-tile kernel for the expert GEMMs ---------------------------------
-// A workgroup of 4 waves owns a BM x BN tile (256 x 256: an average expert at
-// T = 8192 fits one m-tile); each wave owns a 128 x 128 sub-tile as 4 x 4 blocks
-// of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).  K advances in
-// 64-wide slices through two LDS buffers; global reads are buffer loads (one
-// descriptor per operand, per expert for the weights, K position in the scalar
-// offset; rows past the tile or past N read as zero through the range check).
-// Software pipeline per slice (four 16-wide K steps): each step's MFMAs run while
-// the next step's fragments are read from LDS; after step 0 the next slice moves
-// from registers into the other LDS buffer, one 16-byte write and one buffer load
-// per MFMA, so the loads of slice k+2 have about four steps to land; the single
-// barrier sits between steps 2 and 3 and orders LDS only (a full __syncthreads
-// would drain the in-flight loads).  Scheduling-group hints keep the compiler
-// from collapsing that order.  The number of valid 32-row blocks per wave (0, 1,
-// 2 or 4) is a compile-time variant picked once per wave, so short tail tiles of
-// an expert skip MFMA work without branches in the K loop.
-// LDS rows are 8 16-byte chunks; chunk c of row r is stored in slot
-// c ^ (r & 7) ^ ((r >> 3) & 1), which keeps the row-wise 128-byte stores and the
-// 32-row fragment reads free of bank conflicts in every 8- or 16-lane group.
-// Instruction-order hints for the scheduler (one ordered chain per region):
-// masks 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write.
-template <int MASK, int SIZE>
-__device__ __forceinline__ void sched_group() {
-  if constexpr (SIZE > 0) __builtin_amdgcn_sched_group_barrier(MASK, SIZE, 0);
-}
-// NR fragment reads, then NM MFMAs of which the first NX are each followed by one
-// LDS write and one buffer load (the register-to-LDS move of the next slice)
-template <int NR, int NM, int NX>
-__device__ __forceinline__ void sched_step() {
-  if constexpr (NX == 0) {
-    sched_group<0x100, NR>();
-    sched_group<0x008, NM>();
-  } else {
-    sched_group<0x100, NR>();
-    sched_group<0x008, 1>();
-    sched_group<0x200, 1>();
-    sched_group<0x020, 1>();
-    sched_step<0, NM - 1, NX - 1>();
+// ---- LDS-DMA pipelined kernel for the expert GEMMs ---------------------------
+// Tile: up to 320 rows (one expert's whole row block in the common case: about
+// T*K/E = 256 rows, a few dozen more for the busier experts) x 256 output columns.
+// Four waves each own a 128 x 128 block of the first 256 rows (4 x 4 MFMA 32x32x16
+// accumulators in AGPRs) and a 32 x 128 strip of rows 256..319 (4 more accumulators
+// in VGPRs, skipped when the tile has no such rows).  Covering up to 320 rows keeps
+// the weights of an n-tile to one pass over HBM; a second, nearly empty 256-row tile
+// would stream them again.
+// Operands go global -> LDS directly with buffer loads in LDS mode ("buffer_load_dwordx4
+// ... lds": lane i's 16 bytes land at M0 + 16 i): no registers stage them and no
+// LDS-write instructions are issued.  K advances 64 per stage (a full 128-byte line of
+// every row).  A (activations, mostly L2 hits: the n-tiles of a row block run side by
+// side on one XCD) has two 40 KB stage buffers; B (weights, streamed from HBM) two of
+// 32 KB.  Every B fragment of a stage is read into registers right after the stage is
+// published; a second barrier then frees its buffer for the stage after next, so B
+// stage k+2 streams while stage k is multiplied.  The loads are issued from inline
+// assembly so the compiler does not fence them; each wave's own s_waitcnt vmcnt(n)
+// before the barrier publishes a stage.
+// LDS rows are 128 bytes (8 chunks); chunk c of row r sits in slot
+// c ^ (r & 7) ^ ((r >> 3) & 1), conflict-free for the 16-lane groups of 128-bit
+// fragment reads.  Lane p of DMA instruction j writes slot p & 7 of row 8 j + (p >> 3)
+// of the wave's share, so it fetches chunk (p & 7) ^ (p >> 3) ^ (j & 1).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
 }
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                      uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_byte) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// LDS reads of this wave complete, then the workgroup barrier; no global fence
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Calls mf(m) for m in [MB, ME), with rd(q) for q < NRD and dm(q) for q < NDM spread
+// evenly between them; the order is pinned (the scheduler would otherwise bunch the
+// fragment reads and wait on each).
+template <int MB, int ME, int NRD, int NDM, class MF, class RD, class DM>
+__device__ __forceinline__ void interleave(MF&& mf, RD&& rd, DM&& dm) {
+  constexpr int NS = ME - MB > 0 ? ME - MB : 1;
+  static_for<0, NS>([&](auto q_tag) __attribute__((always_inline)) {
+    constexpr int q = decltype(q_tag)::value;
+    if constexpr (ME - MB > 0) mf(std::integral_constant<int, MB + q>{});
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<q * NRD / NS, (q + 1) * NRD / NS>(rd);
+    static_for<q * NDM / NS, (q + 1) * NDM / NS>(dm);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
 
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_big(GemmArgs a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = 64;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;   // 16-byte chunks per thread per slice
-  constexpr int ROWS = BM + BN;
+// MFMA with its accumulator in VGPRs.  The compiler gives every MFMA builtin an
+// AGPR accumulator; a 320-row tile needs 320 accumulator registers per lane, the 64
+// beyond the AGPR file in VGPRs, so the extra strip's MFMAs are written out.  Each
+// such accumulator is reused only 16 or more MFMAs later; mfma_vgpr_drain covers the
+// result latency before the first VALU read.
+// The first MFMA of a chain takes an inline zero as SrcC: a VALU write of the
+// accumulator just before an MFMA that reads it would need wait states the compiler
+// does not insert around inline assembly.
+__device__ __forceinline__ void mfma_vgpr(f32x16_t& c, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_first(f32x16_t& c, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16_t* c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
+  constexpr int BM = kExpertBM, BMAIN = 256, BN = 256, BK = 64, ROWB = 128;
+  constexpr int ASTAGE = BM * ROWB;           // 40 KB
+  constexpr int BSTAGE = BN * ROWB;           // 32 KB
+  constexpr int WTM = 128, WTN = 128, NJ = 4;
   constexpr int BN_OUT = MODE == kGatedBf16 ? BN / 2 : BN;
-  static_assert(CA * NT == BM * 8 && CB * NT == BN * 8, "tile/threads");
-  static_assert((NT / 8) % 16 == 0 && BM % 16 == 0, "store slots repeat every NT/8 rows");
-  static_assert(MODE != kGatedBf16 || ((WTN / 32) % 2 == 0 && CB % 2 == 0), "gated tiles pair gate/up");
-  __shared__ uint4 lds[2][ROWS * 8];
+  constexpr int NDA = BM / 32, NDB = BN / 32; // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint4 lds[(2 * ASTAGE + 2 * BSTAGE) / 16];
 
-  // ---- tile decode ------------------------------------------------------------
-  const int total_m = a.tile_off[a.G];
-  const int total = total_m * a.n_tiles;
+  // ---- tile decode ---------------------------------------------------------------
+  // Workgroups reach the XCDs round-robin (b % 8).  The row blocks, sorted largest
+  // first, are dealt to the XCDs in snake order (round r: XCDs 0..7, then 7..0), so
+  // every XCD gets an even share and runs its largest blocks first; the n-tiles of a
+  // row block are consecutive workgroups of one XCD and share its A rows through L2.
   const int b = blockIdx.x;
-  if (b >= total) return;
-  const int per = total / kXcds, rem = total % kXcds;
   const int xcd = b % kXcds, slot = b / kXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+  const int round = slot / a.n_tiles, nt = slot % a.n_tiles;
+  const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+  if (pos >= a.tile_off[a.G]) return;
+  const int rb = a.order[pos];
   int lo = 0, hi = a.G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] * a.n_tiles <= logical) lo = mid; else hi = mid;
+    if (a.tile_off[mid] <= rb) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int mtiles = a.tile_off[g + 1] - a.tile_off[g];
-  const int local = logical - a.tile_off[g] * a.n_tiles;
-  const int nt = local / mtiles, mt = local % mtiles;
+  const int mt = rb - a.tile_off[g];
   int r0, r1;
   group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
   const int m0 = r0 + mt * BM;
@@ -282,193 +313,241 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_big(GemmArgs a) {
   const int tid = threadIdx.x;
   const int K = a.K;
   const uint32_t row_bytes = uint32_t(K) * 2u;
-
-  // ---- buffer descriptors and per-lane offsets ----------------------------------
-  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(a.A, uint32_t(a.a_rows) * row_bytes);
-  const uint32_t b_bytes = uint32_t(a.N) * row_bytes;
-  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(a.B0 + size_t(g) * a.b_stride, b_bytes);
-  const __amdgpu_buffer_rsrc_t rb1 =
-      MODE == kGatedBf16 ? make_rsrc(a.B1 + size_t(g) * a.b_stride, b_bytes) : rb0;
-  const int trow = tid >> 3, kc0 = tid & 7;
-  uint32_t oa[CA];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int row = trow + i * (NT / 8);
-    uint32_t o = kOob;
-    if (row < mvalid) {
-      const int r = m0 + row;
-      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      o = uint32_t(src) * row_bytes + kc0 * 16;
-    }
-    oa[i] = o;
-  }
-  // B chunk i covers weight row n0 + trow + i*NT/8 (gated: the second half is up rows)
-  constexpr int CBH = MODE == kGatedBf16 ? CB / 2 : CB;
-  const uint32_t ob = uint32_t(n0 + trow) * row_bytes + kc0 * 16;
-  const uint32_t ob_step = uint32_t(NT / 8) * row_bytes;
-  const int st_base = trow * 8 + lds_slot(trow, kc0);       // + i*NT for chunk i
-
-  uint4 ra[CA], rb[CB];
-  auto load_slice = [&](int k0) __attribute__((always_inline)) {
-    const int kb = k0 * 2;
-#pragma unroll
-    for (int i = 0; i < CA; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, oa[i], kb, 0));
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int ih = i < CBH ? i : i - CBH;
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-          i < CBH ? rb0 : rb1, ob + uint32_t(ih) * ob_step, kb, 0));
-    }
-  };
-  auto store_slice = [&](uint4* buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) buf[st_base + i * NT] = ra[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) buf[BM * 8 + st_base + i * NT] = rb[i];
-  };
-
-  // ---- wave geometry (wave index made scalar so tile-shape branches are uniform) --
-  // MFMA 32x32x16: lane l supplies row/column l%32 at K chunk (l/32) of each 16-wide
-  // K step, and holds output rows (r/4)*8 + (l/32)*4 + r%4, column l%32, r < 16.
-  constexpr int NI32 = WTM / 32, NJ32 = WTN / 32;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  const int wm = w / WN, wn = w % WN;
-  const int ni_valid = min(NI32, max(0, (mvalid - wm * WTM + 31) >> 5));
-  const int a_base = (wm * WTM + (l & 31)) * 8;
-  int b_row0[NJ32];
+
+  // ---- this wave's share of every stage: A rows 80 w.., B rows 64 w.. ---------------
+  const uint32_t b_bytes = uint32_t(a.N) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A, uint32_t(a.a_rows) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      make_rsrc((MODE == kGatedBf16 && w >= 2 ? a.B1 : a.B0) + size_t(g) * a.b_stride, b_bytes);
+  uint32_t voff_a[NDA], voff_b[NDB];
 #pragma unroll
-  for (int j = 0; j < NJ32; ++j) {
-    int r;
-    if (MODE == kGatedBf16)
-      r = j < NJ32 / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - NJ32 / 2) * 32;
-    else
-      r = wn * WTN + j * 32;
-    b_row0[j] = (BM + r + (l & 31)) * 8;
+  for (int j = 0; j < NDA; ++j) {
+    const int arow = (BM / 4) * w + 8 * j + (l >> 3);
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
+    uint32_t o = kOob;
+    if (arow < mvalid) {
+      const int r = m0 + arow;
+      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
+      o = uint32_t(src) * row_bytes + chunk;
+    }
+    voff_a[j] = o;
   }
-  const int nk = K / BK;   // even: K is a multiple of 128
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    const int rw = 8 * j + (l >> 3);
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
+    // gated: B rows 0..127 are gate rows n0.., 128..255 up rows n0..; plain: n0 + row
+    const int n = MODE == kGatedBf16 ? n0 + 64 * (w & 1) + rw : n0 + 64 * w + rw;
+    voff_b[j] = uint32_t(n) * row_bytes + chunk;      // rows >= N read zero
+  }
+  // LDS: B buffers at [0, 64K), A buffers at [64K, 144K); stage k uses buffer k & 1
+  constexpr uint32_t kAOff = 2 * BSTAGE;
+  const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
+  const uint32_t wave_a = lds_base + kAOff + uint32_t(w) * (ASTAGE / 4);
+  const uint32_t wave_b = lds_base + uint32_t(w) * (BSTAGE / 4);
+  auto dma_a = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
+    dma16(rsrc_a, voff_a[j], uint32_t(ks) * ROWB, wave_a + uint32_t(par * ASTAGE + j * 1024));
+  };
+  auto dma_b = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
+    dma16(rsrc_b, voff_b[j], uint32_t(ks) * ROWB, wave_b + uint32_t(par * BSTAGE + j * 1024));
+  };
 
-  // The wave's whole tile computation for NIV valid 32-row blocks (0, 1, 2 or 4),
-  // so the K loop itself has no branches: short tiles skip MFMA work per wave and
-  // waves without valid rows only load, store and synchronise.
-  auto body = [&](auto niv_tag) __attribute__((always_inline)) {
+  // ---- fragment geometry: per-step lane bases; buffer and block offsets are immediates
+  const int wm = w >> 1, wn = w & 1;
+  const int ni_valid = min(4, max(0, (min(mvalid, BMAIN) - wm * WTM + 31) >> 5));
+  const bool has_x = mvalid > BMAIN + 32 * wm;        // rows in this wave's extra strip
+  uint32_t abase[4], bbase[4], xbase[4];
+  {
+    const int lane_row = l & 31;
+    const int b_row0 = (MODE == kGatedBf16 ? wn * (WTN / 2) : wn * WTN) + lane_row;
+    const int a_row = wm * WTM + lane_row;
+    const int x_row = BMAIN + 32 * wm + lane_row;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const uint32_t sl = uint32_t((2 * s4 + (l >> 5)) ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
+      bbase[s4] = uint32_t(b_row0) * ROWB + sl;
+      abase[s4] = kAOff + uint32_t(a_row) * ROWB + sl;
+      xbase[s4] = kAOff + uint32_t(x_row) * ROWB + sl;
+    }
+  }
+  // B block j of the wave: rows b_row0 + offset (gated: gate blocks, then up blocks)
+  auto b_blk = [](int j) constexpr {
+    return MODE == kGatedBf16 ? (j < NJ / 2 ? j * 32 : BN / 2 + (j - NJ / 2) * 32) : j * 32;
+  };
+  const int nk = K / BK;
+
+  auto body = [&](auto niv_tag, auto x_tag) __attribute__((always_inline)) {
     constexpr int NIV = decltype(niv_tag)::value;
-    f32x16_t acc[NIV > 0 ? NIV : 1][NJ32];
+    constexpr int NX = decltype(x_tag)::value;     // 1: the extra strip is computed
+    constexpr int NA = NIV + NX;                   // A fragments per K-step
+    constexpr int NMS = (NIV + NX) * NJ;           // MFMAs per K-step
+    constexpr int NRB = NA > 0 ? NJ : 0;           // B fragments per K-step (skipped if idle)
+    f32x16_t acc[NIV > 0 ? NIV : 1][NJ];
+    f32x16_t accx[NJ];
 #pragma unroll
-    for (int i = 0; i < NIV; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ32; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // Fragments of one 16-wide K step (s = 0..3 within the 64-wide slice).  The
-    // fragment rows are 32-aligned + l%32, so the LDS slot depends only on l and s.
-    struct Frag {
-      bf16x8_t b[NJ32];
-      bf16x8_t a[NIV > 0 ? NIV : 1];
-    };
-    auto read_frags = [&](Frag& f, const uint4* buf, int s) __attribute__((always_inline)) {
-      if constexpr (NIV > 0) {
-        const int sl = lds_slot(l & 31, s * 2 + (l >> 5));
-#pragma unroll
-        for (int j = 0; j < NJ32; ++j) f.b[j] = __builtin_bit_cast(bf16x8_t, buf[b_row0[j] + sl]);
-#pragma unroll
-        for (int i = 0; i < NIV; ++i) f.a[i] = __builtin_bit_cast(bf16x8_t, buf[a_base + i * 256 + sl]);
-      }
-    };
-    auto mfmas = [&](const Frag& f) __attribute__((always_inline)) {
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int i = 0; i < NIV; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ32; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-    };
-    // Slice kt from `cur` (its step-0 fragments already in f0).  Software pipeline:
-    // every step's MFMAs run while the next step's fragments are read; after step 0
-    // slice kt+1 moves from registers into `nxt` and the loads of slice kt+2 are
-    // issued (about four steps before they are needed); the one barrier sits between
-    // steps 2 and 3, so step 3's MFMAs cover the first reads of the next slice.
-    Frag f0, f1;
-    auto slice = [&](const uint4* cur, uint4* nxt, int kt, auto st, auto ld, auto next,
-                     auto prev) __attribute__((always_inline)) {
-      constexpr int NR = NIV > 0 ? NIV + NJ32 : 0, NM = NIV * NJ32;
-      constexpr int NX = decltype(st)::value && decltype(ld)::value ? (CA + CB < NM ? CA + CB : NM) : 0;
-      read_frags(f1, cur, 1);
-      mfmas(f0);
-      if constexpr (decltype(st)::value) store_slice(nxt);
-      if constexpr (decltype(ld)::value) load_slice((kt + 2) * BK);
-      read_frags(f0, cur, 2);
-      mfmas(f1);
-      read_frags(f1, cur, 3);
-      mfmas(f0);
-      // region order: this slice's step-0 reads with the previous slice's step-3
-      // MFMAs (none after the prologue), then steps 0..2, each preceded by the reads
-      // of the step after it
-      if constexpr (decltype(prev)::value) sched_step<NR, NM, 0>();
-      else sched_step<NR, 0, 0>();
-      sched_step<NR, NM, NX>();
-      sched_step<NR, NM, 0>();
-      sched_step<NR, NM, 0>();
-      lds_barrier();
-      if constexpr (decltype(next)::value) read_frags(f0, nxt, 0);
-      mfmas(f1);
-    };
-    using yes = std::true_type;
-    using no = std::false_type;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }                                              // accx: defined by its first MFMA
+    bf16x8_t fb[4][NJ];                            // B fragments of the four K-steps
+    bf16x8_t fa[2][NA > 0 ? NA : 1];               // A fragments, double-buffered by step
 
-    load_slice(0);
-    store_slice(lds[0]);
-    load_slice(BK);
-    lds_barrier();
-    read_frags(f0, lds[0], 0);
-    // slice kt reads lds[kt & 1]; slices 0 .. nk-3 also store slice kt+1 and load
-    // slice kt+2, slice nk-2 only stores, slice nk-1 does neither (nk is even)
-    if (nk == 2) {
-      slice(lds[0], lds[1], 0, yes{}, no{}, yes{}, no{});
-      slice(lds[1], lds[0], 1, no{}, no{}, no{}, yes{});
-    } else {
-      slice(lds[0], lds[1], 0, yes{}, yes{}, yes{}, no{});
-      int kt = 1;
-      for (; kt + 4 <= nk; kt += 2) {       // pairs of full slices (odd, even)
-        slice(lds[1], lds[0], kt, yes{}, yes{}, yes{}, yes{});
-        slice(lds[0], lds[1], kt + 1, yes{}, yes{}, yes{}, yes{});
+    auto lds_read = [&](uint32_t byte) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                              reinterpret_cast<const char*>(lds) + byte));
+    };
+    // B fragment (step S4, block J) and A fragment (step S4, block I; I == NIV is the
+    // extra strip) of the stage in buffer PAR
+    auto read_b = [&](auto par_tag, auto s_tag, auto j_tag) __attribute__((always_inline)) {
+      constexpr int par = decltype(par_tag)::value, s4 = decltype(s_tag)::value;
+      constexpr int j = decltype(j_tag)::value;
+      fb[s4][j] = lds_read(bbase[s4] + uint32_t(par * BSTAGE + b_blk(j) * ROWB));
+    };
+    auto read_a = [&](auto par_tag, auto s_tag, auto i_tag) __attribute__((always_inline)) {
+      constexpr int par = decltype(par_tag)::value, s4 = decltype(s_tag)::value;
+      constexpr int i = decltype(i_tag)::value;
+      if constexpr (i < NIV)
+        fa[s4 & 1][i] = lds_read(abase[s4] + uint32_t(par * ASTAGE + i * 32 * ROWB));
+      else
+        fa[s4 & 1][i] = lds_read(xbase[s4] + uint32_t(par * ASTAGE));
+    };
+    // FIRST: step 0 of stage 0, where the extra strip's accumulators start
+    auto mfma_of = [&](auto s_tag, auto m_tag, auto first_tag) __attribute__((always_inline)) {
+      constexpr int s4 = decltype(s_tag)::value, m = decltype(m_tag)::value;
+      constexpr int i = m / NJ, j = m % NJ;
+      if constexpr (i < NIV)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s4 & 1][i], fb[s4][j], acc[i][j], 0, 0, 0);
+      else if constexpr (decltype(first_tag)::value)
+        mfma_vgpr_first(accx[j], fa[s4 & 1][NIV], fb[s4][j]);
+      else
+        mfma_vgpr(accx[j], fa[s4 & 1][NIV], fb[s4][j]);
+    };
+    auto none = [&](auto) __attribute__((always_inline)) {};
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
+    // One stage k in buffer PAR, entered right after the barrier that published it:
+    //  R0  second half of stage k-1's step 3 (if PREV); reads of step 0; DMA A k+1 (if DA)
+    //  R1  step 0; reads of B steps 1..3 and A step 1; then the barrier that frees B k
+    //  R2  step 1; reads of A step 2; DMA B k+2 into B k's buffer (if DB)
+    //  R3  step 2; reads of A step 3
+    //  R4  first half of step 3; then publish stage k+1 (if PUB; VM loads may stay in flight)
+    auto stage = [&](int k, auto par_tag, auto prev_tag, auto da_tag, auto db_tag, auto pub_tag,
+                     auto vm_tag) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par_tag)::value;
+      constexpr bool PREV = decltype(prev_tag)::value, DA = decltype(da_tag)::value;
+      constexpr bool DB = decltype(db_tag)::value, PUB = decltype(pub_tag)::value;
+      constexpr int VM = decltype(vm_tag)::value;
+      using P = std::integral_constant<int, PAR>;
+      using Q = std::integral_constant<int, 1 - PAR>;
+      auto rd0 = [&](auto q_tag) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_tag)::value;
+        if constexpr (q < NRB) read_b(P{}, S0{}, q_tag);
+        else read_a(P{}, S0{}, std::integral_constant<int, q - NRB>{});
+      };
+      auto dma_a1 = [&](auto j_tag) __attribute__((always_inline)) { dma_a(k + 1, Q{}, j_tag); };
+      interleave<NMS / 2, PREV ? NMS : NMS / 2, NRB + NA, DA ? NDA : 0>(
+          [&](auto m) __attribute__((always_inline)) { mfma_of(S3{}, m, F_{}); }, rd0, dma_a1);
+      auto rd1 = [&](auto q_tag) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_tag)::value;
+        if constexpr (q < 3 * NRB)
+          read_b(P{}, std::integral_constant<int, 1 + q / NJ>{}, std::integral_constant<int, q % NJ>{});
+        else
+          read_a(P{}, S1{}, std::integral_constant<int, q - 3 * NRB>{});
+      };
+      interleave<0, NMS, 3 * NRB + NA, 0>(
+          [&](auto m) __attribute__((always_inline)) { mfma_of(S0{}, m, std::bool_constant<!PREV>{}); }, rd1, none);
+      stage_barrier();                          // every wave holds its B k fragments
+      auto rd2 = [&](auto q_tag) __attribute__((always_inline)) { read_a(P{}, S2{}, q_tag); };
+      auto dma_b2 = [&](auto j_tag) __attribute__((always_inline)) { dma_b(k + 2, P{}, j_tag); };
+      interleave<0, NMS, NA, DB ? NDB : 0>(
+          [&](auto m) __attribute__((always_inline)) { mfma_of(S1{}, m, F_{}); }, rd2, dma_b2);
+      auto rd3 = [&](auto q_tag) __attribute__((always_inline)) { read_a(P{}, S3{}, q_tag); };
+      interleave<0, NMS, NA, 0>(
+          [&](auto m) __attribute__((always_inline)) { mfma_of(S2{}, m, F_{}); }, rd3, none);
+      interleave<0, NMS / 2, 0, 0>(
+          [&](auto m) __attribute__((always_inline)) { mfma_of(S3{}, m, F_{}); }, none, none);
+      if constexpr (PUB) {
+        wait_vmcnt<VM>();
+        stage_barrier();
       }
-      slice(lds[1], lds[0], kt, yes{}, yes{}, yes{}, yes{});           // kt == nk-3
-      slice(lds[0], lds[1], kt + 1, yes{}, no{}, yes{}, yes{});        // nk-2
-      slice(lds[1], lds[0], kt + 2, no{}, no{}, no{}, yes{});          // nk-1
-    }
+    };
+    using V0 = std::integral_constant<int, 0>;
+    using VB = std::integral_constant<int, NDB>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
 
-    // ---- epilogue ---------------------------------------------------------------
-#pragma unroll
-    for (int i = 0; i < NIV; ++i) {
+    // prologue: A 0, B 0, B 1 in flight; stage 0 published once only B 1 may be pending
+    static_for<0, NDA>([&](auto j) __attribute__((always_inline)) { dma_a(0, P0{}, j); });
+    static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(0, P0{}, j); });
+    static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(1, P1{}, j); });
+    wait_vmcnt<NDB>();
+    stage_barrier();
+    // nk = K / 64 is even (K is a multiple of 128)
+    if (nk == 2) {
+      stage(0, P0{}, F_{}, T_{}, F_{}, T_{}, V0{});
+      stage(1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{});
+    } else {
+      stage(0, P0{}, F_{}, T_{}, T_{}, T_{}, VB{});
+      stage(1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{});
+      for (int k = 2; k < nk - 2; k += 2) {
+        stage(k, P0{}, T_{}, T_{}, T_{}, T_{}, VB{});
+        stage(k + 1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{});
+      }
+      stage(nk - 2, P0{}, T_{}, T_{}, F_{}, T_{}, V0{});
+      stage(nk - 1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{});
+    }
+    interleave<NMS / 2, NMS, 0, 0>(
+        [&](auto m) __attribute__((always_inline)) { mfma_of(S3{}, m, F_{}); }, none, none);
+
+    // ---- epilogue -------------------------------------------------------------------
+    auto store_block = [&](const f32x16_t* accs, int rbase) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = wm * WTM + i * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+        const int rl = rbase + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
         if (rl >= mvalid) continue;
         const size_t row = size_t(m0 + rl);
         if (MODE == kGatedBf16) {
 #pragma unroll
-          for (int j = 0; j < NJ32 / 2; ++j) {
+          for (int j = 0; j < NJ / 2; ++j) {
             const int col = n0 + wn * (WTN / 2) + j * 32 + (l & 31);
-            const float hv = silu_fast(acc[i][j][r]) * acc[i][j + NJ32 / 2][r];
+            const float hv = silu_fast(accs[j][r]) * accs[j + NJ / 2][r];
             if (col < a.N) static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(hv);
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < NJ32; ++j) {
+          for (int j = 0; j < NJ; ++j) {
             const int col = n0 + wn * WTN + j * 32 + (l & 31);
             if (col < a.N)
-              static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(acc[i][j][r]);
+              static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(accs[j][r]);
           }
         }
       }
+    };
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) store_block(acc[i], wm * WTM + i * 32);
+    if constexpr (NX) {
+      mfma_vgpr_drain(accx);
+      store_block(accx, BMAIN + 32 * wm);
     }
   };
-  static_assert(NI32 == 4, "row-block variants assume 4 blocks of 32 rows per wave");
-  if (ni_valid > 2) body(std::integral_constant<int, 4>{});
-  else if (ni_valid > 1) body(std::integral_constant<int, 2>{});
-  else if (ni_valid > 0) body(std::integral_constant<int, 1>{});
-  else body(std::integral_constant<int, 0>{});
+  using X0 = std::integral_constant<int, 0>;
+  using X1 = std::integral_constant<int, 1>;
+  if (ni_valid > 2) {
+    if (has_x) body(std::integral_constant<int, 4>{}, X1{});
+    else body(std::integral_constant<int, 4>{}, X0{});
+  } else if (ni_valid > 1) body(std::integral_constant<int, 2>{}, X0{});
+  else if (ni_valid > 0) body(std::integral_constant<int, 1>{}, X0{});
+  else body(std::integral_constant<int, 0>{}, X0{});
 }
 
 // m-tile prefix over groups for two tile heights, one workgroup (G <= 512).
@@ -503,6 +582,64 @@ __global__ __launch_bounds__(512) void build_tiles(const int32_t* __restrict__ o
     t1[G] = s1[g];
     t2[G] = s2[g];
   }
+}
+
+// Row-block schedule of the bf16 expert GEMMs, one workgroup (G <= 512): the m-tile
+// prefix over groups (tiles of bm rows) and every row block's index ordered by row
+// count, largest first (a counting sort over 32-row classes; the order inside a class
+// is arbitrary and does not change any result, each block computes the same values
+// wherever it runs).
+__global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict__ offsets, int E,
+                                                      int Ns, int T, int TK, int bm,
+                                                      int32_t* __restrict__ tile_off,
+                                                      int32_t* __restrict__ order) {
+  constexpr int kClasses = 64;
+  __shared__ int pre[512];
+  __shared__ int cls_count[kClasses], cls_next[kClasses];
+  const int t = threadIdx.x, G = E + Ns;
+  int c = 0;
+  if (t < G) {
+    int r0, r1;
+    group_rows(offsets, t, E, T, TK, r0, r1);
+    c = ceil_div(r1 - r0, bm);
+  }
+  pre[t] = c;
+  if (t < kClasses) cls_count[t] = 0;
+  __syncthreads();
+  for (int d = 1; d < 512; d <<= 1) {
+    const int v = t >= d ? pre[t - d] : 0;
+    __syncthreads();
+    pre[t] += v;
+    __syncthreads();
+  }
+  if (t < G) tile_off[t] = pre[t] - c;
+  if (t == G - 1) tile_off[G] = pre[t];
+  const int total = pre[G - 1];
+  // class of a row block: (bm - rows) / 32; its group is the first g with pre[g] > rb
+  auto cls_of = [&](int rb) {
+    int lo = -1, hi = G - 1;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] > rb) hi = mid; else lo = mid;
+    }
+    const int g = hi;
+    const int first = g > 0 ? pre[g - 1] : 0;
+    int r0, r1;
+    group_rows(offsets, g, E, T, TK, r0, r1);
+    const int rows = min(bm, r1 - r0 - (rb - first) * bm);
+    return min(kClasses - 1, (bm - rows) >> 5);
+  };
+  for (int rb = t; rb < total; rb += 512) atomicAdd(&cls_count[cls_of(rb)], 1);
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int k = 0; k < kClasses; ++k) {
+      cls_next[k] = acc;
+      acc += cls_count[k];
+    }
+  }
+  __syncthreads();
+  for (int rb = t; rb < total; rb += 512) order[atomicAdd(&cls_next[cls_of(rb)], 1)] = rb;
 }
 
 // ---- fp32 path (small fp32 workloads): one thread per output element ---------
@@ -556,14 +693,7 @@ __global__ __launch_bounds__(256) void gemm2_f32(const float* __restrict__ h,
 
 // ---- launch configuration ---------------------------------------------------
 constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;      // router logits
-constexpr int kEBM = 256, kEBN = 256, kEWM = 2, kEWN = 2;  // expert GEMMs
 
-static int m_tiles_upper(const moe_config& c, int bm) {
-  const long long TK = 1LL * c.num_tokens * c.top_k;
-  long long routed = (TK + 1LL * c.num_experts * (bm - 1)) / bm;
-  routed = routed < TK ? routed : TK;
-  return int(routed + 1LL * c.num_shared * ceil_div(c.num_tokens, bm));
-}
 
 hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const uint16_t* w,
                                    float* z, hipStream_t s) {
@@ -596,6 +726,14 @@ hipError_t launch_build_tiles(const moe_config& c, const int32_t* offsets, int b
   return hipGetLastError();
 }
 
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm,
+                                 int32_t* tile_off, int32_t* order, hipStream_t s) {
+  const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
+  hipLaunchKernelGGL(build_schedule, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, T * c.top_k, bm,
+                     tile_off, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
                               const int32_t* row_token, const moe_expert_weights& w,
                               void* y_rows, const Workspace& ws, hipStream_t s) {
@@ -615,13 +753,16 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   }
   if (c.w_dtype == MOE_E4M3)
     return launch_grouped_ffn_fp8(c, x, offsets, row_token, w, y_rows, ws, s);
-  hipError_t err = launch_build_tiles(c, offsets, kEBM, kEBM, ws.tiles1, ws.tiles2, s);
+  hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.tiles1, ws.order, s);
   if (err != hipSuccess) return err;
+  // grid: every XCD gets ceil(row blocks / 8) rounds of n_tiles workgroups
+  const int rounds = ceil_div(expert_row_blocks_upper(c, kExpertBM), kXcds);
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
   a.row_token = row_token;
   a.offsets = offsets;
   a.tile_off = ws.tiles1;
+  a.order = ws.order;
   a.B0 = static_cast<const uint16_t*>(w.w_gate);
   a.B1 = static_cast<const uint16_t*>(w.w_up);
   a.b_stride = 1LL * I * H;
@@ -633,17 +774,16 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   a.T = T;
   a.TK = TK;
   a.G = G;
-  a.n_tiles = ceil_div(I, kEBN / 2);
+  a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL((grouped_gemm_big<kEBM, kEBN, kEWM, kEWN, kGatedBf16>),
-                     dim3(m_tiles_upper(c, kEBM) * a.n_tiles), dim3(kEWM * kEWN * 64), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_dma<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(256), 0,
+                     s, a);
   GemmArgs d = a;
   d.A = static_cast<const uint16_t*>(ws.h);
   d.row_token = nullptr;
   d.gather = 0;
   d.a_rows = rows;
-  d.tile_off = ws.tiles2;
   d.B0 = static_cast<const uint16_t*>(w.w_down);
   d.B1 = nullptr;
   d.b_stride = 1LL * H * I;
@@ -651,9 +791,9 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   d.ldc = H;
   d.N = H;
   d.K = I;
-  d.n_tiles = ceil_div(H, kEBN);
-  hipLaunchKernelGGL((grouped_gemm_big<kEBM, kEBN, kEWM, kEWN, kPlainBf16>),
-                     dim3(m_tiles_upper(c, kEBM) * d.n_tiles), dim3(kEWM * kEWN * 64), 0, s, d);
+  d.n_tiles = ceil_div(H, 256);
+  hipLaunchKernelGGL(grouped_gemm_dma<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(256), 0,
+                     s, d);
   return hipGetLastError();
 }
 

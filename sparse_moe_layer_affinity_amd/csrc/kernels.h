@@ -15,6 +15,7 @@ struct Workspace {
   int32_t* pair_row;   // [T*K]
   int32_t* tiles1;     // [E+Ns+1] m-tile prefix for the first expert GEMM
   int32_t* tiles2;     // [E+Ns+1] m-tile prefix for the second expert GEMM
+  int32_t* order;      // [row-block bound] bf16 expert GEMM row blocks, largest first
   void* h;             // [rows, inter] act dtype (SwiGLU output of the first GEMM)
   uint8_t* hq;         // [rows, inter] e4m3 codes of h (e4m3 weights)
   float* h_scales;     // [rows, inter/128] (e4m3 weights)
@@ -25,6 +26,16 @@ struct Workspace {
 };
 
 constexpr int kTokChunk = 64;   // tokens per permute chunk (one 64-bit mask)
+constexpr int kExpertBM = 320;  // rows per row block of the bf16 expert GEMMs
+
+// Upper bound on the row blocks (m-tiles of bm rows) over all groups: every routed
+// expert may end in a partial block, the shared experts have T rows each.
+inline int expert_row_blocks_upper(const moe_config& c, int bm) {
+  const long long TK = 1LL * c.num_tokens * c.top_k;
+  long long routed = (TK + 1LL * c.num_experts * (bm - 1)) / bm;
+  routed = routed < TK ? routed : TK;
+  return int(routed + 1LL * c.num_shared * ((c.num_tokens + bm - 1) / bm));
+}
 
 Workspace workspace_layout(const moe_config& c, void* base);
 
