@@ -358,13 +358,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   // ---- fragment geometry: per-step lane bases; buffer and block offsets are immediates
   const int wm = w >> 1, wn = w & 1;
   const int ni_valid = min(4, max(0, (min(mvalid, BMAIN) - wm * WTM + 31) >> 5));
-  const bool has_x = mvalid > BMAIN + 32 * wm;        // rows in this wave's extra strip
+  // rows 256..319 form two 32-row extra strips; every wave takes two 32-column blocks
+  // of each strip that has rows (nx strips), so the four waves stay balanced
+  const int nx = mvalid > BMAIN + 32 ? 2 : (mvalid > BMAIN ? 1 : 0);
   uint32_t abase[4], bbase[4], xbase[4];
   {
     const int lane_row = l & 31;
     const int b_row0 = (MODE == kGatedBf16 ? wn * (WTN / 2) : wn * WTN) + lane_row;
     const int a_row = wm * WTM + lane_row;
-    const int x_row = BMAIN + 32 * wm + lane_row;
+    const int x_row = BMAIN + lane_row;                 // strip 1: + 32 rows
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const uint32_t sl = uint32_t((2 * s4 + (l >> 5)) ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
@@ -379,11 +381,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   };
   const int nk = K / BK;
 
-  auto body = [&](auto niv_tag, auto x_tag) __attribute__((always_inline)) {
+  auto body = [&](auto niv_tag, auto x_tag, auto xw_tag) __attribute__((always_inline)) {
     constexpr int NIV = decltype(niv_tag)::value;
-    constexpr int NX = decltype(x_tag)::value;     // 1: the extra strip is computed
+    constexpr int NX = decltype(x_tag)::value;     // extra strips with rows (0..2)
+    constexpr int XW = decltype(xw_tag)::value;    // the wave's wm, for the extra blocks
     constexpr int NA = NIV + NX;                   // A fragments per K-step
-    constexpr int NMS = (NIV + NX) * NJ;           // MFMAs per K-step
+    constexpr int NMS = NIV * NJ + 2 * NX;         // MFMAs per K-step
+    // extra MFMA e: strip e / 2, B block xb(e) (gated: the gate block and its up block)
+    constexpr auto xb = [](int e) constexpr { return ((e >> 1) == 0 ? XW : 1 - XW) + 2 * (e & 1); };
     constexpr int NRB = NA > 0 ? NJ : 0;           // B fragments per K-step (skipped if idle)
     f32x16_t acc[NIV > 0 ? NIV : 1][NJ];
     f32x16_t accx[NJ];
@@ -414,18 +419,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       if constexpr (i < NIV)
         fa[s4 & 1][i] = lds_read(abase[s4] + uint32_t(par * ASTAGE + i * 32 * ROWB));
       else
-        fa[s4 & 1][i] = lds_read(xbase[s4] + uint32_t(par * ASTAGE));
+        fa[s4 & 1][i] = lds_read(xbase[s4] + uint32_t(par * ASTAGE + (i - NIV) * 32 * ROWB));
     };
     // FIRST: step 0 of stage 0, where the extra strip's accumulators start
     auto mfma_of = [&](auto s_tag, auto m_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr int s4 = decltype(s_tag)::value, m = decltype(m_tag)::value;
-      constexpr int i = m / NJ, j = m % NJ;
-      if constexpr (i < NIV)
+      if constexpr (m < NIV * NJ) {
+        constexpr int i = m / NJ, j = m % NJ;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s4 & 1][i], fb[s4][j], acc[i][j], 0, 0, 0);
-      else if constexpr (decltype(first_tag)::value)
-        mfma_vgpr_first(accx[j], fa[s4 & 1][NIV], fb[s4][j]);
-      else
-        mfma_vgpr(accx[j], fa[s4 & 1][NIV], fb[s4][j]);
+      } else {
+        constexpr int e = m - NIV * NJ;
+        if constexpr (decltype(first_tag)::value)
+          mfma_vgpr_first(accx[e], fa[s4 & 1][NIV + (e >> 1)], fb[s4][xb(e)]);
+        else
+          mfma_vgpr(accx[e], fa[s4 & 1][NIV + (e >> 1)], fb[s4][xb(e)]);
+      }
     };
     auto none = [&](auto) __attribute__((always_inline)) {};
     using S0 = std::integral_constant<int, 0>;
@@ -535,19 +543,48 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     };
 #pragma unroll
     for (int i = 0; i < NIV; ++i) store_block(acc[i], wm * WTM + i * 32);
-    if constexpr (NX) {
+    if constexpr (NX > 0) {
       mfma_vgpr_drain(accx);
-      store_block(accx, BMAIN + 32 * wm);
+      static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_tag)::value;
+        constexpr int jb = st == 0 ? XW : 1 - XW;       // the strip's first block
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = BMAIN + 32 * st + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+          if (rl >= mvalid) continue;
+          const size_t row = size_t(m0 + rl);
+          if (MODE == kGatedBf16) {
+            const int col = n0 + wn * (WTN / 2) + jb * 32 + (l & 31);
+            const float hv = silu_fast(accx[2 * st][r]) * accx[2 * st + 1][r];
+            if (col < a.N) static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(hv);
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int col = n0 + wn * WTN + (jb + 2 * h) * 32 + (l & 31);
+              if (col < a.N)
+                static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(accx[2 * st + h][r]);
+            }
+          }
+        }
+      });
     }
   };
-  using X0 = std::integral_constant<int, 0>;
-  using X1 = std::integral_constant<int, 1>;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (ni_valid > 2) {
-    if (has_x) body(std::integral_constant<int, 4>{}, X1{});
-    else body(std::integral_constant<int, 4>{}, X0{});
-  } else if (ni_valid > 1) body(std::integral_constant<int, 2>{}, X0{});
-  else if (ni_valid > 0) body(std::integral_constant<int, 1>{}, X0{});
-  else body(std::integral_constant<int, 0>{}, X0{});
+    if (nx == 2) {
+      if (wm == 0) body(std::integral_constant<int, 4>{}, I2{}, I0{});
+      else body(std::integral_constant<int, 4>{}, I2{}, I1{});
+    } else if (nx == 1) {
+      if (wm == 0) body(std::integral_constant<int, 4>{}, I1{}, I0{});
+      else body(std::integral_constant<int, 4>{}, I1{}, I1{});
+    } else {
+      body(std::integral_constant<int, 4>{}, I0{}, I0{});
+    }
+  } else if (ni_valid > 1) body(std::integral_constant<int, 2>{}, I0{}, I0{});
+  else if (ni_valid > 0) body(std::integral_constant<int, 1>{}, I0{}, I0{});
+  else body(std::integral_constant<int, 0>{}, I0{}, I0{});
 }
 
 // m-tile prefix over groups for two tile heights, one workgroup (G <= 512).
