@@ -222,26 +222,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
 // c ^ (r & 7) ^ ((r >> 3) & 1), conflict-free for the 16-lane groups of 128-bit
 // fragment reads.  Lane p of DMA instruction j writes slot p & 7 of row 8 j + (p >> 3)
 // of the wave's share, so it fetches chunk (p & 7) ^ (p >> 3) ^ (j & 1).
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
-                                      uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_byte) : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-// LDS reads of this wave complete, then the workgroup barrier; no global fence
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 // Calls mf(m) for m in [MB, ME), with rd(q) for q < NRD and dm(q) for q < NDM spread
 // evenly between them; the order is pinned (the scheduler would otherwise bunch the
 // fragment reads and wait on each).

@@ -47,6 +47,37 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- direct global -> LDS loads ("buffer_load_dwordx4 ... lds") ---------------------
+// Lane i of one instruction writes its 16 bytes at LDS byte M0 + 16 i.  Issued from
+// inline assembly so the compiler does not fence them; callers wait with
+// wait_vmcnt<n>() (this wave's n most recent loads may still be in flight) and
+// publish with stage_barrier().
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                      uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_byte) : "memory", "m0");
+}
+// 4-byte variant: lane i's dword lands at M0 + 4 i
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                     uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_byte) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// LDS reads of this wave complete, then the workgroup barrier; no global fence
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 // silu(a) = a / (1 + e^-a) from the hardware exp2 and reciprocal (each about 1 ulp
 // in fp32); h is rounded to bf16 (relative step 2^-9) right after.
 __device__ __forceinline__ float silu_fast(float a) {

@@ -12,13 +12,20 @@
 // MI355X layout choice: the MFMA rows are weight rows and its columns tokens (the
 // transpose of the bf16 kernel), so the four outputs a lane holds (rows 4*(l/16)+q,
 // column l%16) share one token and one 128-row weight block, and the per-block
-// rescale is one multiplier per lane: four FMAs per MFMA, on the VALU while the
-// matrix core runs the next MFMA.  Accumulators therefore live in VGPRs.
+// rescale is one multiplier per lane: four FMAs per MFMA.  The accumulators live in
+// VGPRs (the VALU adds into them), and this file is compiled with MFMA results in
+// VGPRs as well, so no copies out of AGPRs.
 //
-// Tile: 256 weight rows (GEMM1: 128 gate rows over the matching 128 up rows) x
-// 128 tokens; 4 waves, each 128 weight rows x 64 tokens = 8 x 4 MFMA blocks.
-// K advances one 128-byte scale block per slice through two swizzled LDS buffers
-// (48 KB each), the next slice's buffer loads in flight during the MFMAs.
+// Tile: 256 weight rows (GEMM1: 128 gate rows over the matching 128 up rows) x 256
+// tokens, 8 waves (two per SIMD: one wave's rescale FMAs run while the other's
+// MFMAs hold the matrix core), each 128 weight rows x 64 tokens = 8 x 4 MFMA blocks.
+// K advances one 128-byte scale block per stage.  Operands and scales go global ->
+// LDS with buffer loads in LDS mode.  Weights (streamed from HBM) cycle through three
+// 32 KB stage buffers, so weight stage k+2 is in flight while stage k is multiplied.
+// Tokens (mostly L2 hits) use one 32 KB buffer: every wave reads all its token
+// fragments of a stage into registers first, and once a barrier confirms that, the
+// next stage's tokens and scales are loaded in its place.  Row blocks come from the
+// same largest-first XCD schedule as the bf16 kernel, 256 tokens each.
 #include "gemm_common.h"
 
 namespace moe {
@@ -28,7 +35,8 @@ struct Fp8Args {
   const float* a_scales;     // [a_rows, K/128]
   const int32_t* row_token;  // gather map of routed rows (gather only)
   const int32_t* offsets;    // [E+1]
-  const int32_t* tile_off;   // [G+1] m-tile prefix (128 tokens per m-tile)
+  const int32_t* tile_off;   // [G+1] row-block prefix (256 tokens per block)
+  const int32_t* order;      // row blocks in schedule order
   const uint8_t* B0;         // e4m3 weights [G][N][K] (GEMM1: gate)
   const uint8_t* B1;         // GEMM1: up
   const float* S0;           // weight block scales [G][N/128][K/128] (GEMM1: gate)
@@ -44,33 +52,30 @@ struct Fp8Args {
 };
 
 template <int MODE>
-__global__ __launch_bounds__(256) void grouped_gemm_fp8(Fp8Args a) {
-  constexpr int NT = 256;
-  constexpr int BT = 128;                // tokens per tile
-  constexpr int BW = 256;                // weight rows per tile
-  constexpr int ROWS = BW + BT;          // LDS rows of 128 bytes (one K block)
-  constexpr int CH = ROWS * 8 / NT;      // 16-byte chunks per thread per slice (12)
-  constexpr int CW = BW * 8 / NT;        // of which weight chunks (8)
+__global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
+  constexpr int BW = 256, BT = kFp8BT, ROWB = 128;
+  constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 32 KB each
+  constexpr int SW = 3;                                   // weight stage buffers
+  constexpr uint32_t kTOff = SW * WSTAGE;                 // token buffer
+  constexpr uint32_t kSaOff = kTOff + TSTAGE;             // token scales, 2 x 1 KB
+  constexpr uint32_t kSwOff = kSaOff + 2048;              // weight scales, 2 x 1 KB
   constexpr int BN_OUT = MODE == kGatedBf16 ? BW / 2 : BW;
-  __shared__ uint4 lds[2][ROWS * 8];
+  __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2048) / 16];
 
-  // ---- tile decode: (expert, n-tile, m-tile), m innermost, XCD-contiguous ------
-  const int total_m = a.tile_off[a.G];
-  const int total = total_m * a.n_tiles;
+  // ---- tile decode: snake-dealt row blocks (see the bf16 expert GEMM) ------------
   const int b = blockIdx.x;
-  if (b >= total) return;
-  const int per = total / kXcds, rem = total % kXcds;
   const int xcd = b % kXcds, slot = b / kXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+  const int round = slot / a.n_tiles, nt = slot % a.n_tiles;
+  const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+  if (pos >= a.tile_off[a.G]) return;
+  const int rb = a.order[pos];
   int lo = 0, hi = a.G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] * a.n_tiles <= logical) lo = mid; else hi = mid;
+    if (a.tile_off[mid] <= rb) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int mtiles = a.tile_off[g + 1] - a.tile_off[g];
-  const int local = logical - a.tile_off[g] * a.n_tiles;
-  const int nt = local / mtiles, mt = local % mtiles;
+  const int mt = rb - a.tile_off[g];
   int r0, r1;
   group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
   const int m0 = r0 + mt * BT;
@@ -78,177 +83,205 @@ __global__ __launch_bounds__(256) void grouped_gemm_fp8(Fp8Args a) {
   const int n0 = nt * BN_OUT;
   const int tid = threadIdx.x;
   const int K = a.K, KBLK = a.K / 128;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
 
-  // ---- buffer descriptors and per-lane offsets ----------------------------------
-  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(a.A, uint32_t(a.a_rows) * uint32_t(K));
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(a.a_scales, uint32_t(a.a_rows) * KBLK * 4u);
+  // ---- this wave's share of every stage: weight rows and token rows 32 w .. 32 w + 31
   const uint32_t b_bytes = uint32_t(a.N) * uint32_t(K);
-  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(a.B0 + size_t(g) * a.b_stride, b_bytes);
-  const __amdgpu_buffer_rsrc_t rb1 =
-      MODE == kGatedBf16 ? make_rsrc(a.B1 + size_t(g) * a.b_stride, b_bytes) : rb0;
-  const int trow = tid >> 3, kc0 = tid & 7;
-  // weight chunk i (< CW) is weight row trow + 32 i of the tile (gated: i >= CW/2 up)
-  constexpr int CWH = MODE == kGatedBf16 ? CW / 2 : CW;
-  const uint32_t ob = uint32_t(n0 + trow) * uint32_t(K) + kc0 * 16;
-  const uint32_t ob_step = 32u * uint32_t(K);
-  // token chunk i (CW..CH-1) is tile row trow + 32 (i - CW)
-  uint32_t oa[CH - CW];
+  const __amdgpu_buffer_rsrc_t rsrc_w =
+      make_rsrc((MODE == kGatedBf16 && w >= 4 ? a.B1 : a.B0) + size_t(g) * a.b_stride, b_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(a.A, uint32_t(a.a_rows) * uint32_t(K));
+  uint32_t voff_w[4], voff_t[4];
 #pragma unroll
-  for (int i = 0; i < CH - CW; ++i) {
-    const int row = trow + 32 * i;
+  for (int j = 0; j < 4; ++j) {
+    const int rw = 8 * j + (l >> 3);
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
+    // gated: stage rows 0..127 gate rows n0.., 128..255 up rows n0..
+    const int n = MODE == kGatedBf16 ? n0 + 32 * (w & 3) + rw : n0 + 32 * w + rw;
+    voff_w[j] = uint32_t(n) * uint32_t(K) + chunk;         // rows >= N read zero
+    const int trow = 32 * w + rw;
     uint32_t o = kOob;
+    if (trow < mvalid) {
+      const int r = m0 + trow;
+      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
+      o = uint32_t(src) * uint32_t(K) + chunk;
+    }
+    voff_t[j] = o;
+  }
+  // one scale load per wave per stage: waves 0..3 the token scales of tokens
+  // 64 w + lane, waves 4 and 5 one weight block scale each (lane 0), waves 6 and 7
+  // nothing useful (every lane out of range; they keep the load counts uniform)
+  __amdgpu_buffer_rsrc_t rsrc_s;
+  uint32_t voff_s = kOob;
+  if (w < 4) {
+    rsrc_s = make_rsrc(a.a_scales, uint32_t(a.a_rows) * KBLK * 4u);
+    const int row = 64 * w + l;
     if (row < mvalid) {
       const int r = m0 + row;
       const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      o = uint32_t(src) * uint32_t(K) + kc0 * 16;
+      voff_s = uint32_t(src) * uint32_t(KBLK) * 4u;
     }
-    oa[i] = o;
+  } else {
+    // gated: wave 4 the gate block, wave 5 the up block (same block index); plain:
+    // waves 4 and 5 the tile's two 128-row blocks (clamped in range: a block past N
+    // only feeds outputs that are never stored)
+    const bool up = MODE == kGatedBf16 && w == 5;
+    const int blk = min(MODE == kGatedBf16 ? n0 / 128 : n0 / 128 + (w - 4), ceil_div(a.N, 128) - 1);
+    rsrc_s = make_rsrc((up ? a.S1 : a.S0) + size_t(g) * a.s_stride, uint32_t(a.s_stride) * 4u);
+    if (w < 6 && l == 0) voff_s = uint32_t(blk * KBLK) * 4u;
   }
-  const int st_base = trow * 8 + lds_slot(trow, kc0);
+  const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
+  const uint32_t wave_w = lds_base + uint32_t(w) * (WSTAGE / 8);
+  const uint32_t wave_t = lds_base + kTOff + uint32_t(w) * (TSTAGE / 8);
+  const uint32_t wave_s = lds_base + (w < 4 ? kSaOff + 256u * w : kSwOff + 256u * (w - 4));
 
-  uint4 rw[CW], rt[CH - CW];
-  auto load_slice = [&](int kb) __attribute__((always_inline)) {
-    const int kofs = kb * 128;
+  auto load_w = [&](int ks) __attribute__((always_inline)) {
+    const uint32_t dst = wave_w + uint32_t(ks % SW) * WSTAGE;
 #pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int ih = i < CWH ? i : i - CWH;
-      rw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-          i < CWH ? rb0 : rb1, ob + uint32_t(ih) * ob_step, kofs, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < CH - CW; ++i)
-      rt[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, oa[i], kofs, 0));
+    for (int j = 0; j < 4; ++j) dma16(rsrc_w, voff_w[j], uint32_t(ks) * ROWB, dst + j * 1024u);
   };
-  auto store_slice = [&](uint4* buf) __attribute__((always_inline)) {
+  // token rows of stage ks, then its scales (5 loads)
+  auto load_t = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CW; ++i) buf[st_base + i * NT] = rw[i];
-#pragma unroll
-    for (int i = 0; i < CH - CW; ++i) buf[BW * 8 + st_base + i * NT] = rt[i];
+    for (int j = 0; j < 4; ++j) dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + j * 1024u);
+    dma4(rsrc_s, voff_s, uint32_t(ks) * 4u, wave_s + uint32_t(ks & 1) * 1024u);
   };
 
-  // ---- wave geometry: 2 (weight rows) x 2 (tokens) ------------------------------
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  // ---- wave geometry: 2 (weight rows) x 4 (tokens) --------------------------------
   const int wn = w & 1, wt = w >> 1;
-  int w_row[8];                            // LDS row of this lane in weight block ib
+  // LDS row of this lane in weight block ib / token block jb, and its two K chunks
+  int w_row[8];
 #pragma unroll
   for (int ib = 0; ib < 8; ++ib) {
     int r;
     if (MODE == kGatedBf16) r = ib < 4 ? wn * 64 + ib * 16 : 128 + wn * 64 + (ib - 4) * 16;
     else r = wn * 128 + ib * 16;
-    w_row[ib] = (r + (l & 15)) * 8;
+    w_row[ib] = r + (l & 15);
   }
-  const int t_row = (BW + wt * 64 + (l & 15)) * 8;       // + jb * 128
-  const int slot0 = lds_slot(l & 15, 2 * (l >> 4)), slot1 = lds_slot(l & 15, 2 * (l >> 4) + 1);
+  const int t_row = wt * 64 + (l & 15);                   // + 16 jb
+  const int c0 = 2 * (l >> 4);
+  const uint32_t sl0 = uint32_t(c0 ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
+  const uint32_t sl1 = uint32_t((c0 + 1) ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
 
-  // activation scale offsets (floats) of this lane's 4 tokens; invalid rows read zero
-  uint32_t osa[4];
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int row = wt * 64 + jb * 16 + (l & 15);
-    uint32_t o = kOob;
-    if (row < mvalid) {
-      const int r = m0 + row;
-      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      o = uint32_t(src) * uint32_t(KBLK) * 4u;
-    }
-    osa[jb] = o;
-  }
-  // weight block scales: this wave's weight rows lie in one 128-row block (per matrix)
-  // (a wave past N in a partial tile computes zeros: clamp its scale block in range)
-  const int nblk0 = min((MODE == kGatedBf16 ? n0 : n0 + wn * 128) / 128, ceil_div(a.N, 128) - 1);
-  const float* sw0 = a.S0 + size_t(g) * a.s_stride + size_t(nblk0) * KBLK;
-  const float* sw1 = MODE == kGatedBf16 ? a.S1 + size_t(g) * a.s_stride + size_t(n0 / 128) * KBLK
-                                        : sw0;
+  // token blocks of this wave that hold rows: the MFMAs of empty ones are skipped
+  const int njb = min(4, max(0, (mvalid - wt * 64 + 15) >> 4));
+  auto body = [&](auto njb_tag) __attribute__((always_inline)) {
+    constexpr int NJB = decltype(njb_tag)::value;
+    f32x4_t acc[8][NJB > 0 ? NJB : 1];
+  #pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+  #pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) acc[ib][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  f32x4_t acc[8][4];
-#pragma unroll
-  for (int ib = 0; ib < 8; ++ib)
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) acc[ib][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto lds_frag = [&](uint32_t row_byte) __attribute__((always_inline)) {
+      const char* base = reinterpret_cast<const char*>(lds) + row_byte;
+      const uint4 lo4 = *reinterpret_cast<const uint4*>(base + sl0);
+      const uint4 hi4 = *reinterpret_cast<const uint4*>(base + sl1);
+      return i32x8_t{int(lo4.x), int(lo4.y), int(lo4.z), int(lo4.w),
+                     int(hi4.x), int(hi4.y), int(hi4.z), int(hi4.w)};
+    };
+    auto lds_f32 = [&](uint32_t byte) __attribute__((always_inline)) {
+      return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lds) + byte);
+    };
 
-  auto compute = [&](const uint4* buf, int kb) __attribute__((always_inline)) {
-    float sa[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      sa[jb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, osa[jb], kb * 4, 0));
-    const float s_w0 = sw0[kb], s_w1 = sw1[kb];
-    i32x8_t tf[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const uint4 lo4 = buf[t_row + jb * 128 + slot0], hi4 = buf[t_row + jb * 128 + slot1];
-      tf[jb] = i32x8_t{int(lo4.x), int(lo4.y), int(lo4.z), int(lo4.w),
-                       int(hi4.x), int(hi4.y), int(hi4.z), int(hi4.w)};
-    }
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const uint4 lo4 = buf[w_row[ib] + slot0], hi4 = buf[w_row[ib] + slot1];
-      const i32x8_t wf = i32x8_t{int(lo4.x), int(lo4.y), int(lo4.z), int(lo4.w),
-                                 int(hi4.x), int(hi4.y), int(hi4.z), int(hi4.w)};
-      const float s_w = (MODE == kGatedBf16 && ib >= 4) ? s_w1 : s_w0;
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wf, tf[jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-        const float s = sa[jb] * s_w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s, acc[ib][jb][q]);
-      }
-    }
-  };
-
-  const int nk = KBLK;
-  load_slice(0);
-  store_slice(lds[0]);
-  if (nk > 1) load_slice(1);
-  lds_barrier();
-  for (int kb = 0; kb < nk; ++kb) {
-    uint4* cur = lds[kb & 1];
-    uint4* nxt = lds[(kb + 1) & 1];
-    compute(cur, kb);
-    if (kb + 1 < nk) store_slice(nxt);
-    if (kb + 2 < nk) load_slice(kb + 2);
-    lds_barrier();
-  }
-
-  // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int rl = wt * 64 + jb * 16 + (l & 15);
-    if (rl >= mvalid) continue;
-    uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
-    if (MODE == kGatedBf16) {
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
-        if (col >= a.N) continue;
-        uint32_t h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_bits(silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q]);
-        *reinterpret_cast<uint2*>(crow + col) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      }
+    // prologue: tokens 0 (+ scales), weights 0 and 1; stage 0 published once only
+    // weight stage 1 (4 loads) may be pending.  K is a multiple of 128: nk >= 1.
+    const int nk = KBLK;
+    load_t(0);
+    load_w(0);
+    if (nk > 1) {
+      load_w(1);
+      wait_vmcnt<4>();
     } else {
-#pragma unroll
-      for (int ib = 0; ib < 8; ++ib) {
-        const int col = n0 + wn * 128 + ib * 16 + 4 * (l >> 4);
-        if (col >= a.N) continue;
-        uint32_t h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_bits(acc[ib][jb][q]);
-        *reinterpret_cast<uint2*>(crow + col) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      wait_vmcnt<0>();
+    }
+    stage_barrier();
+    for (int k = 0; k < nk; ++k) {
+      const uint32_t wb = uint32_t(k % SW) * WSTAGE;
+      const uint32_t sp = uint32_t(k & 1) * 1024u;
+      // token fragments and scales of stage k into registers
+      i32x8_t tf[NJB > 0 ? NJB : 1];
+  #pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) tf[jb] = lds_frag(kTOff + uint32_t(t_row + 16 * jb) * ROWB);
+      float s[2][NJB > 0 ? NJB : 1];                                        // s_a * s_w per weight half
+      {
+        const float s_w0 = lds_f32(kSwOff + sp + (MODE == kGatedBf16 ? 0u : 256u * wn));
+        const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + sp + 256u) : s_w0;
+  #pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const float s_a = lds_f32(kSaOff + sp + uint32_t(t_row + 16 * jb) * 4u);
+          s[0][jb] = s_a * s_w0;
+          s[1][jb] = s_a * s_w1;
+        }
+      }
+      // each product is rescaled as soon as it is back; the other wave on the SIMD
+      // keeps the matrix core busy meanwhile
+      auto block_row = [&](int ib) __attribute__((always_inline)) {
+        if constexpr (NJB == 0) return;
+        const i32x8_t wf = lds_frag(wb + uint32_t(w_row[ib]) * ROWB);
+        const int h = (MODE == kGatedBf16 && ib >= 4) ? 1 : 0;
+  #pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf, tf[jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[h][jb], acc[ib][jb][q]);
+        }
+      };
+      block_row(0);
+      if (k + 1 < nk) {
+        // every wave holds its stage-k token fragments and scales: reload that buffer
+        // with stage k+1, then weight stage k+2 into the buffer stage k-1 left
+        stage_barrier();
+        load_t(k + 1);
+        if (k + 2 < nk) load_w(k + 2);
+      }
+  #pragma unroll
+      for (int ib = 1; ib < 8; ++ib) block_row(ib);
+      if (k + 1 < nk) {
+        if (k + 2 < nk) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+        stage_barrier();
       }
     }
-  }
+
+    // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
+  #pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      const int rl = wt * 64 + jb * 16 + (l & 15);
+      if (rl >= mvalid) continue;
+      uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
+      if (MODE == kGatedBf16) {
+  #pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
+          if (col >= a.N) continue;
+          uint32_t hh[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) hh[q] = f32_to_bf16_bits(silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q]);
+          *reinterpret_cast<uint2*>(crow + col) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        }
+      } else {
+  #pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+          const int col = n0 + wn * 128 + ib * 16 + 4 * (l >> 4);
+          if (col >= a.N) continue;
+          uint32_t hh[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) hh[q] = f32_to_bf16_bits(acc[ib][jb][q]);
+          *reinterpret_cast<uint2*>(crow + col) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        }
+      }
+    }
+
+  };
+  if (njb > 2) body(std::integral_constant<int, 4>{});
+  else if (njb == 2) body(std::integral_constant<int, 2>{});
+  else if (njb == 1) body(std::integral_constant<int, 1>{});
+  else body(std::integral_constant<int, 0>{});
 }
 
-static int m_tiles_upper_fp8(const moe_config& c, int bm) {
-  const long long TK = 1LL * c.num_tokens * c.top_k;
-  long long routed = (TK + 1LL * c.num_experts * (bm - 1)) / bm;
-  routed = routed < TK ? routed : TK;
-  return int(routed + 1LL * c.num_shared * ceil_div(c.num_tokens, bm));
-}
-
-hipError_t launch_build_tiles(const moe_config& c, const int32_t* offsets, int bm1, int bm2,
-                              int32_t* t1, int32_t* t2, hipStream_t s);
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm,
+                                 int32_t* tile_off, int32_t* order, hipStream_t s);
 
 hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int32_t* offsets,
                                   const int32_t* row_token, const moe_expert_weights& w,
@@ -258,14 +291,16 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   const int H = c.hidden, I = c.inter;
   hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s);
   if (err != hipSuccess) return err;
-  err = launch_build_tiles(c, offsets, 128, 128, ws.tiles1, ws.tiles2, s);
+  err = launch_build_schedule(c, offsets, kFp8BT, ws.tiles1, ws.order, s);
   if (err != hipSuccess) return err;
+  const int rounds = ceil_div(expert_row_blocks_upper(c, kFp8BT), kXcds);
   Fp8Args a{};
   a.A = ws.xq;
   a.a_scales = ws.x_scales;
   a.row_token = row_token;
   a.offsets = offsets;
   a.tile_off = ws.tiles1;
+  a.order = ws.order;
   a.B0 = static_cast<const uint8_t*>(w.w_gate);
   a.B1 = static_cast<const uint8_t*>(w.w_up);
   a.S0 = w.s_gate;
@@ -283,8 +318,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(m_tiles_upper_fp8(c, 128) * a.n_tiles),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512),
+                     0, s, a);
   err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s);
   if (err != hipSuccess) return err;
   Fp8Args d = a;
@@ -293,7 +328,6 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.row_token = nullptr;
   d.gather = 0;
   d.a_rows = rows;
-  d.tile_off = ws.tiles2;
   d.B0 = static_cast<const uint8_t*>(w.w_down);
   d.B1 = nullptr;
   d.S0 = w.s_down;
@@ -305,8 +339,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 256);
-  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(m_tiles_upper_fp8(c, 128) * d.n_tiles),
-                     dim3(256), 0, s, d);
+  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512),
+                     0, s, d);
   return hipGetLastError();
 }
 
