@@ -31,7 +31,6 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   w.row_token = static_cast<int32_t*>(take(TK * 4));
   w.pair_row = static_cast<int32_t*>(take(TK * 4));
   w.tiles1 = static_cast<int32_t*>(take((G + 1) * 4));
-  w.tiles2 = static_cast<int32_t*>(take((G + 1) * 4));
   w.order = static_cast<int32_t*>(take(size_t(expert_row_blocks_upper(c, kFp8BT)) * 4));
   w.h = take(rows * I * act_bytes(c));
   w.hq = fp8 ? static_cast<uint8_t*>(take(rows * I)) : nullptr;

@@ -567,41 +567,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   else body(std::integral_constant<int, 0>{}, I0{}, I0{});
 }
 
-// m-tile prefix over groups for two tile heights, one workgroup (G <= 512).
-__global__ __launch_bounds__(512) void build_tiles(const int32_t* __restrict__ offsets, int E,
-                                                   int Ns, int T, int TK, int bm1, int bm2,
-                                                   int32_t* __restrict__ t1,
-                                                   int32_t* __restrict__ t2) {
-  __shared__ int s1[512], s2[512];
-  const int g = threadIdx.x, G = E + Ns;
-  int c1 = 0, c2 = 0;
-  if (g < G) {
-    int r0, r1;
-    group_rows(offsets, g, E, T, TK, r0, r1);
-    c1 = ceil_div(r1 - r0, bm1);
-    c2 = ceil_div(r1 - r0, bm2);
-  }
-  s1[g] = c1;
-  s2[g] = c2;
-  __syncthreads();
-  for (int d = 1; d < 512; d <<= 1) {
-    int a1 = g >= d ? s1[g - d] : 0, a2 = g >= d ? s2[g - d] : 0;
-    __syncthreads();
-    s1[g] += a1;
-    s2[g] += a2;
-    __syncthreads();
-  }
-  if (g < G) {
-    t1[g] = s1[g] - c1;
-    t2[g] = s2[g] - c2;
-  }
-  if (g == G - 1) {
-    t1[G] = s1[g];
-    t2[G] = s2[g];
-  }
-}
-
-// Row-block schedule of the bf16 expert GEMMs, one workgroup (G <= 512): the m-tile
+// Row-block schedule of the expert GEMMs, one workgroup (G <= 512): the row-block
 // prefix over groups (tiles of bm rows) and every row block's index ordered by row
 // count, largest first (a counting sort over 32-row classes; the order inside a class
 // is arbitrary and does not change any result, each block computes the same values
@@ -732,14 +698,6 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   const int grid = ceil_div(c.num_tokens, kBM) * a.n_tiles;
   hipLaunchKernelGGL((grouped_gemm_bf16<kBM, kBN, kWM, kWN, kPlainF32>),
                      dim3(grid, router_splits(c)), dim3(kWM * kWN * 64), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_build_tiles(const moe_config& c, const int32_t* offsets, int bm1, int bm2,
-                              int32_t* t1, int32_t* t2, hipStream_t s) {
-  const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
-  hipLaunchKernelGGL(build_tiles, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, T * c.top_k, bm1,
-                     bm2, t1, t2);
   return hipGetLastError();
 }
 

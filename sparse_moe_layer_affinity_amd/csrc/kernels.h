@@ -13,9 +13,8 @@ struct Workspace {
   int32_t* offsets;    // [E+1] expert offsets (layer forward)
   int32_t* row_token;  // [T*K]
   int32_t* pair_row;   // [T*K]
-  int32_t* tiles1;     // [E+Ns+1] m-tile prefix for the first expert GEMM
-  int32_t* tiles2;     // [E+Ns+1] m-tile prefix for the second expert GEMM
-  int32_t* order;      // [row-block bound] bf16 expert GEMM row blocks, largest first
+  int32_t* tiles1;     // [E+Ns+1] row-block prefix per group of the expert GEMMs
+  int32_t* order;      // [row-block bound] the row blocks, largest first
   void* h;             // [rows, inter] act dtype (SwiGLU output of the first GEMM)
   uint8_t* hq;         // [rows, inter] e4m3 codes of h (e4m3 weights)
   float* h_scales;     // [rows, inter/128] (e4m3 weights)
