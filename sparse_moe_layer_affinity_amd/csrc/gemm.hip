@@ -268,25 +268,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint4 lds[(2 * ASTAGE + 2 * BSTAGE) / 16];
 
   // ---- tile decode ---------------------------------------------------------------
-  // Workgroups reach the XCDs round-robin (b % 8).  The row blocks, sorted largest
-  // first, are dealt to the XCDs in snake order (round r: XCDs 0..7, then 7..0), so
-  // every XCD gets an even share and runs its largest blocks first; the n-tiles of a
-  // row block are consecutive workgroups of one XCD and share its A rows through L2.
+  // Workgroups reach the XCDs round-robin (b % 8).  The units (see build_schedule),
+  // sorted largest first, are dealt to the XCDs in snake order (round r: XCDs 0..7,
+  // then 7..0), so every XCD gets an even share and runs its largest units first; a
+  // unit's workgroups are consecutive on one XCD, n-tile major: its blocks share each
+  // weight tile and every block's n-tiles share its A rows, through that XCD's L2.
   const int b = blockIdx.x;
   const int xcd = b % kXcds, slot = b / kXcds;
-  const int round = slot / a.n_tiles, nt = slot % a.n_tiles;
+  const int per_round = a.n_tiles * a.unit;
+  const int round = slot / per_round, rs = slot % per_round;
+  const int nt = rs / a.unit, u = rs % a.unit;
   const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
   if (pos >= a.tile_off[a.G]) return;
-  const int rb = a.order[pos];
+  const int id = a.order[pos];
   int lo = 0, hi = a.G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] <= rb) lo = mid; else hi = mid;
+    if (a.tile_off[mid] <= id) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int mt = rb - a.tile_off[g];
+  const int mt = (id - a.tile_off[g]) * a.unit + u;
   int r0, r1;
   group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
+  if (mt * BM >= r1 - r0) return;                        // unit with fewer blocks
   const int m0 = r0 + mt * BM;
   const int mvalid = min(BM, r1 - m0);
   const int n0 = nt * BN_OUT;
@@ -567,14 +571,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   else body(std::integral_constant<int, 0>{}, I0{}, I0{});
 }
 
-// Row-block schedule of the expert GEMMs, one workgroup (G <= 512): the row-block
-// prefix over groups (tiles of bm rows) and every row block's index ordered by row
-// count, largest first (a counting sort over 32-row classes; the order inside a class
-// is arbitrary and does not change any result, each block computes the same values
-// wherever it runs).
+// Schedule of the expert GEMMs, one workgroup (G <= 512).  A group's rows split into
+// blocks of bm rows; up to U consecutive blocks of one group form a unit, whose
+// workgroups run side by side (n-tile major, block minor) so the blocks share every
+// weight tile through L2.  Output: the unit prefix over groups and every unit's index
+// ordered by row count, largest first (a counting sort over 32-row classes; the order
+// inside a class is arbitrary and changes no result: each block computes the same
+// values wherever it runs).
 __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict__ offsets, int E,
-                                                      int Ns, int T, int TK, int bm,
-                                                      int32_t* __restrict__ tile_off,
+                                                      int Ns, int T, int TK, int bm, int U,
+                                                      int32_t* __restrict__ unit_off,
                                                       int32_t* __restrict__ order) {
   constexpr int kClasses = 64;
   __shared__ int pre[512];
@@ -584,7 +590,7 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
   if (t < G) {
     int r0, r1;
     group_rows(offsets, t, E, T, TK, r0, r1);
-    c = ceil_div(r1 - r0, bm);
+    c = ceil_div(ceil_div(r1 - r0, bm), U);
   }
   pre[t] = c;
   if (t < kClasses) cls_count[t] = 0;
@@ -595,24 +601,25 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     pre[t] += v;
     __syncthreads();
   }
-  if (t < G) tile_off[t] = pre[t] - c;
-  if (t == G - 1) tile_off[G] = pre[t];
+  if (t < G) unit_off[t] = pre[t] - c;
+  if (t == G - 1) unit_off[G] = pre[t];
   const int total = pre[G - 1];
-  // class of a row block: (bm - rows) / 32; its group is the first g with pre[g] > rb
-  auto cls_of = [&](int rb) {
+  const int span = U * bm;                                // rows of a full unit
+  // class of a unit: (span - rows) / 32; its group is the first g with pre[g] > id
+  auto cls_of = [&](int id) {
     int lo = -1, hi = G - 1;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pre[mid] > rb) hi = mid; else lo = mid;
+      if (pre[mid] > id) hi = mid; else lo = mid;
     }
     const int g = hi;
     const int first = g > 0 ? pre[g - 1] : 0;
     int r0, r1;
     group_rows(offsets, g, E, T, TK, r0, r1);
-    const int rows = min(bm, r1 - r0 - (rb - first) * bm);
-    return min(kClasses - 1, (bm - rows) >> 5);
+    const int rows = min(span, r1 - r0 - (id - first) * span);
+    return min(kClasses - 1, (span - rows) >> 5);
   };
-  for (int rb = t; rb < total; rb += 512) atomicAdd(&cls_count[cls_of(rb)], 1);
+  for (int id = t; id < total; id += 512) atomicAdd(&cls_count[cls_of(id)], 1);
   __syncthreads();
   if (t == 0) {
     int acc = 0;
@@ -622,7 +629,7 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  for (int rb = t; rb < total; rb += 512) order[atomicAdd(&cls_next[cls_of(rb)], 1)] = rb;
+  for (int id = t; id < total; id += 512) order[atomicAdd(&cls_next[cls_of(id)], 1)] = id;
 }
 
 // ---- fp32 path (small fp32 workloads): one thread per output element ---------
@@ -701,11 +708,11 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   return hipGetLastError();
 }
 
-hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm,
-                                 int32_t* tile_off, int32_t* order, hipStream_t s) {
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int unit,
+                                 int32_t* unit_off, int32_t* order, hipStream_t s) {
   const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
   hipLaunchKernelGGL(build_schedule, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, T * c.top_k, bm,
-                     tile_off, order);
+                     unit, unit_off, order);
   return hipGetLastError();
 }
 
@@ -728,16 +735,19 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   }
   if (c.w_dtype == MOE_E4M3)
     return launch_grouped_ffn_fp8(c, x, offsets, row_token, w, y_rows, ws, s);
-  hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.tiles1, ws.order, s);
+  // one block per unit: 320-row blocks already hold an expert's rows at the prefill shape
+  constexpr int kUnit = 1;
+  hipError_t err = launch_build_schedule(c, offsets, kExpertBM, kUnit, ws.tiles1, ws.order, s);
   if (err != hipSuccess) return err;
-  // grid: every XCD gets ceil(row blocks / 8) rounds of n_tiles workgroups
-  const int rounds = ceil_div(expert_row_blocks_upper(c, kExpertBM), kXcds);
+  // grid: every XCD gets ceil(units / 8) rounds of n_tiles x unit workgroups
+  const int rounds = ceil_div(expert_units_upper(c, kExpertBM, kUnit), kXcds);
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
   a.row_token = row_token;
   a.offsets = offsets;
   a.tile_off = ws.tiles1;
   a.order = ws.order;
+  a.unit = kUnit;
   a.B0 = static_cast<const uint16_t*>(w.w_gate);
   a.B1 = static_cast<const uint16_t*>(w.w_up);
   a.b_stride = 1LL * I * H;
@@ -752,7 +762,7 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL(grouped_gemm_dma<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(256), 0,
+  hipLaunchKernelGGL(grouped_gemm_dma<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles * kUnit), dim3(256), 0,
                      s, a);
   GemmArgs d = a;
   d.A = static_cast<const uint16_t*>(ws.h);
@@ -767,7 +777,7 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 256);
-  hipLaunchKernelGGL(grouped_gemm_dma<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(256), 0,
+  hipLaunchKernelGGL(grouped_gemm_dma<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles * kUnit), dim3(256), 0,
                      s, d);
   return hipGetLastError();
 }

@@ -11,8 +11,9 @@ struct GemmArgs {
   const uint16_t* A;         // bf16 activations: x [T, K] (gather) or [rows, K]
   const int32_t* row_token;  // gather map of routed rows (gather only)
   const int32_t* offsets;    // [E+1] expert offsets (nullptr: single group of T rows)
-  const int32_t* tile_off;   // [G+1] m-tile prefix per group (nullptr: single group)
-  const int32_t* order;      // row blocks in schedule order (bf16 expert GEMMs)
+  const int32_t* tile_off;   // [G+1] m-tile (expert GEMMs: unit) prefix per group
+  const int32_t* order;      // units in schedule order (expert GEMMs)
+  int unit;                  // row blocks per unit (expert GEMMs)
   const uint16_t* B0;        // weights [G][N][K] bf16 (GEMM1: gate)
   const uint16_t* B1;        // GEMM1: up
   long long b_stride;        // elements per expert

@@ -35,8 +35,9 @@ struct Fp8Args {
   const float* a_scales;     // [a_rows, K/128]
   const int32_t* row_token;  // gather map of routed rows (gather only)
   const int32_t* offsets;    // [E+1]
-  const int32_t* tile_off;   // [G+1] row-block prefix (256 tokens per block)
-  const int32_t* order;      // row blocks in schedule order
+  const int32_t* tile_off;   // [G+1] unit prefix per group
+  const int32_t* order;      // units in schedule order
+  int unit;                  // row blocks per unit
   const uint8_t* B0;         // e4m3 weights [G][N][K] (GEMM1: gate)
   const uint8_t* B1;         // GEMM1: up
   const float* S0;           // weight block scales [G][N/128][K/128] (GEMM1: gate)
@@ -56,28 +57,34 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   constexpr int BW = 256, BT = kFp8BT, ROWB = 128;
   constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 32 KB each
   constexpr int SW = 3;                                   // weight stage buffers
-  constexpr uint32_t kTOff = SW * WSTAGE;                 // token buffer
-  constexpr uint32_t kSaOff = kTOff + TSTAGE;             // token scales, 2 x 1 KB
+  // LDS: the token buffer first (its fragment reads then take immediate offsets, which
+  // stop at 64 KB), the weight ring, the two scale rings
+  constexpr uint32_t kTOff = 0;                           // token buffer
+  constexpr uint32_t kWOff = TSTAGE;                      // weight ring
+  constexpr uint32_t kSaOff = kWOff + SW * WSTAGE;        // token scales, 2 x 1 KB
   constexpr uint32_t kSwOff = kSaOff + 2048;              // weight scales, 2 x 1 KB
   constexpr int BN_OUT = MODE == kGatedBf16 ? BW / 2 : BW;
   __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2048) / 16];
 
-  // ---- tile decode: snake-dealt row blocks (see the bf16 expert GEMM) ------------
+  // ---- tile decode: snake-dealt units (see the bf16 expert GEMM) -----------------
   const int b = blockIdx.x;
   const int xcd = b % kXcds, slot = b / kXcds;
-  const int round = slot / a.n_tiles, nt = slot % a.n_tiles;
+  const int per_round = a.n_tiles * a.unit;
+  const int round = slot / per_round, rs = slot % per_round;
+  const int nt = rs / a.unit, u = rs % a.unit;
   const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
   if (pos >= a.tile_off[a.G]) return;
-  const int rb = a.order[pos];
+  const int id = a.order[pos];
   int lo = 0, hi = a.G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] <= rb) lo = mid; else hi = mid;
+    if (a.tile_off[mid] <= id) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int mt = rb - a.tile_off[g];
+  const int mt = (id - a.tile_off[g]) * a.unit + u;
   int r0, r1;
   group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
+  if (mt * BT >= r1 - r0) return;                        // unit with fewer blocks
   const int m0 = r0 + mt * BT;
   const int mvalid = min(BT, r1 - m0);
   const int n0 = nt * BN_OUT;
@@ -130,14 +137,23 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     if (w < 6 && l == 0) voff_s = uint32_t(blk * KBLK) * 4u;
   }
   const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
-  const uint32_t wave_w = lds_base + uint32_t(w) * (WSTAGE / 8);
+  const uint32_t wave_w = lds_base + kWOff + uint32_t(w) * (WSTAGE / 8);
   const uint32_t wave_t = lds_base + kTOff + uint32_t(w) * (TSTAGE / 8);
   const uint32_t wave_s = lds_base + (w < 4 ? kSaOff + 256u * w : kSwOff + 256u * (w - 4));
 
   auto load_w = [&](int ks) __attribute__((always_inline)) {
     const uint32_t dst = wave_w + uint32_t(ks % SW) * WSTAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(rsrc_w, voff_w[j], uint32_t(ks) * ROWB, dst + j * 1024u);
+    for (int j = 0; j < 4; ++j) {
+      // gated: every weight row of the tile is below N (n-tiles of 128 rows, N a
+      // multiple of 128), so rows 16 apart differ by a uniform offset that rides in
+      // the scalar operand and two lane offsets serve all four loads
+      if constexpr (MODE == kGatedBf16)
+        dma16(rsrc_w, voff_w[j & 1], uint32_t(ks) * ROWB + uint32_t(j >> 1) * 16u * uint32_t(K),
+              dst + j * 1024u);
+      else
+        dma16(rsrc_w, voff_w[j], uint32_t(ks) * ROWB, dst + j * 1024u);
+    }
   };
   // token rows of stage ks, then its scales (5 loads)
   auto load_t = [&](int ks) __attribute__((always_inline)) {
@@ -196,7 +212,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     }
     stage_barrier();
     for (int k = 0; k < nk; ++k) {
-      const uint32_t wb = uint32_t(k % SW) * WSTAGE;
+      const uint32_t wb = kWOff + uint32_t(k % SW) * WSTAGE;
       const uint32_t sp = uint32_t(k & 1) * 1024u;
       // token fragments and scales of stage k into registers
       i32x8_t tf[NJB > 0 ? NJB : 1];
@@ -280,8 +296,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   else body(std::integral_constant<int, 0>{});
 }
 
-hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm,
-                                 int32_t* tile_off, int32_t* order, hipStream_t s);
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int unit,
+                                 int32_t* unit_off, int32_t* order, hipStream_t s);
 
 hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int32_t* offsets,
                                   const int32_t* row_token, const moe_expert_weights& w,
@@ -291,9 +307,12 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   const int H = c.hidden, I = c.inter;
   hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s);
   if (err != hipSuccess) return err;
-  err = launch_build_schedule(c, offsets, kFp8BT, ws.tiles1, ws.order, s);
+  // one block per unit: two blocks of one expert side by side on one XCD (sharing each
+  // weight tile through L2) measured 47% slower than dealing the blocks separately
+  constexpr int kUnit = 1;
+  err = launch_build_schedule(c, offsets, kFp8BT, kUnit, ws.tiles1, ws.order, s);
   if (err != hipSuccess) return err;
-  const int rounds = ceil_div(expert_row_blocks_upper(c, kFp8BT), kXcds);
+  const int rounds = ceil_div(expert_units_upper(c, kFp8BT, kUnit), kXcds);
   Fp8Args a{};
   a.A = ws.xq;
   a.a_scales = ws.x_scales;
@@ -301,6 +320,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.offsets = offsets;
   a.tile_off = ws.tiles1;
   a.order = ws.order;
+  a.unit = kUnit;
   a.B0 = static_cast<const uint8_t*>(w.w_gate);
   a.B1 = static_cast<const uint8_t*>(w.w_up);
   a.S0 = w.s_gate;
@@ -318,7 +338,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512),
+  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles * kUnit), dim3(512),
                      0, s, a);
   err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s);
   if (err != hipSuccess) return err;
@@ -339,7 +359,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 256);
-  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512),
+  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles * kUnit), dim3(512),
                      0, s, d);
   return hipGetLastError();
 }
