@@ -1,0 +1,106 @@
+"""Row-block edges of the expert GEMMs, driven through moe_grouped_ffn with prescribed
+per-expert row counts (the grouped rows of every expert compared with the oracle).
+
+bf16 rows are blocked by 320 (the extra strips start at rows 256 and 288 of a block),
+FP8 rows by 256; the counts straddle every edge: empty experts, 1 row, 32/33, 255..257,
+288/289, 320/321, 512/513, 640, and a shared expert of several blocks.  hidden and
+inter of 128 take the one- and two-stage K loops.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_affinity_amd as moe
+import workloads
+from gpu_harness import TOL, config_of, expert_getter, inputs_on_gpu, log, rel_err, weights_of, workspace
+
+pytestmark = pytest.mark.gpu
+
+# 16 experts, K = 4, T = 1000: 4000 routed rows
+LOADS = [0, 1, 32, 33, 255, 256, 257, 288, 289, 320, 321, 512, 513, 640, 13, 270]
+
+
+def _grouped_rows_oracle(cfg, d, idx, ffn):
+    """Oracle rows in the grouped layout: routed rows expert by expert, then shared."""
+    load, off, row_token, _ = oracle.permute(idx, cfg.E)
+    get = expert_getter(cfg, d)
+    x = d["x"].to("cpu", torch.float64)
+    out = np.zeros((cfg.rows, cfg.hidden))
+    for e in range(cfg.E):
+        if off[e + 1] > off[e]:
+            out[off[e]:off[e + 1]] = ffn(x[row_token[off[e]:off[e + 1]]].numpy(), *get(e))
+    TK = cfg.T * cfg.K
+    for s in range(cfg.Ns):
+        out[TK + s * cfg.T:TK + (s + 1) * cfg.T] = ffn(x.numpy(), *get(cfg.E + s))
+    return off, row_token, out
+
+
+def _run(cfg, d, off, row_token):
+    c = config_of(cfg)
+    ws = workspace(c)
+    y_rows = torch.zeros((cfg.rows, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    moe.moe_grouped_ffn(c, d["x"], cu(off), cu(row_token), weights_of(d), y_rows, ws)
+    torch.cuda.synchronize()
+    return y_rows.float().cpu().numpy()
+
+
+def _per_expert_errors(cfg, off, got, ref):
+    errs = {}
+    TK = cfg.T * cfg.K
+    for e in range(cfg.E):
+        if off[e + 1] > off[e]:
+            errs[e] = rel_err(got[off[e]:off[e + 1]], ref[off[e]:off[e + 1]])
+    errs["shared"] = rel_err(got[TK:], ref[TK:])
+    return errs
+
+
+@pytest.mark.parametrize("dims", [(256, 256), (128, 128), (384, 128)])
+def test_row_block_edges_bf16(dims):
+    hidden, inter = dims
+    cfg = workloads.get("decode_bf16").replace(T=1000, hidden=hidden, inter=inter, E=16, K=4,
+                                               G=4, M=2, topn=2, Ns=1)
+    log(f"bf16 row-block edges, hidden {hidden}, inter {inter}")
+    d = inputs_on_gpu(cfg)
+    idx = workloads.topk_with_loads(cfg.T, cfg.K, LOADS).numpy()
+    off, row_token, ref = _grouped_rows_oracle(cfg, d, idx, oracle.expert_ffn)
+    got = _run(cfg, d, off, row_token)
+    errs = _per_expert_errors(cfg, off, got, ref)
+    log("  " + ", ".join(f"{k}:{v:.1e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def _emu_tol(inter):
+    """Bound against the FP8-emulating oracle.  What remains there is the odd e4m3 code
+    of h that flips because the kernel's h carries fp32 rounding before its bf16
+    rounding; one flip moves one of the `inter` terms of an output row by a code step,
+    so the worst row's error grows as inter shrinks (about 1/sqrt(inter)): 2e-2 from
+    inter = 256 up (the prefill shape measures 3e-3..9e-3), scaled below."""
+    return 2e-2 * max(1.0, (256 / inter) ** 0.5)
+
+
+@pytest.mark.parametrize("dims", [(256, 256), (128, 128), (128, 2048)])
+def test_row_block_edges_fp8(dims):
+    hidden, inter = dims
+    cfg = workloads.get("prefill_fp8").replace(T=1000, hidden=hidden, inter=inter, E=16, K=4,
+                                               G=4, M=2, topn=2, Ns=1)
+    log(f"fp8 row-block edges, hidden {hidden}, inter {inter}")
+    d = inputs_on_gpu(cfg)
+    idx = workloads.topk_with_loads(cfg.T, cfg.K, LOADS).numpy()
+    off, row_token, ref32 = _grouped_rows_oracle(cfg, d, idx, oracle.expert_ffn)
+    _, _, emu = _grouped_rows_oracle(cfg, d, idx, oracle.expert_ffn_fp8_emulated)
+    got = _run(cfg, d, off, row_token)
+    errs = _per_expert_errors(cfg, off, got, ref32)
+    errs_emu = _per_expert_errors(cfg, off, got, emu)
+    log("  vs fp32: " + ", ".join(f"{k}:{v:.1e}" for k, v in errs.items()))
+    log("  vs fp8-emulating: " + ", ".join(f"{k}:{v:.1e}" for k, v in errs_emu.items()))
+    # the workload's 6e-2 bound (from 64 rows, 0.1 below, as the layer tests) holds for
+    # the FP8 method itself once both GEMMs sum at least 256 products per output; with
+    # 128 the quantisation errors average less (measured up to 6.1e-2), and only the
+    # emulating oracle's bound applies
+    if min(hidden, inter) >= 256:
+        for k, v in errs.items():
+            n = cfg.T if k == "shared" else LOADS[k]
+            assert v <= (TOL["e4m3"] if n >= 64 else 0.1), (k, v)
+    assert max(errs_emu.values()) <= _emu_tol(inter), errs_emu

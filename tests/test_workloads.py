@@ -1,4 +1,5 @@
 """The seeded generators: shapes, dtypes, reproducibility and the skewed-workload recipe."""
+import numpy as np
 import torch
 
 import workloads
@@ -39,3 +40,11 @@ def test_sample_rows():
     r = workloads.sample_rows(8192, 512)
     assert r.shape == (512,) and torch.all(r[1:] > r[:-1])
     assert torch.equal(r, workloads.sample_rows(8192, 512))
+
+
+def test_topk_with_loads_histogram_and_distinct():
+    loads = [0, 3, 5, 5, 5, 5, 2]
+    idx = workloads.topk_with_loads(5, 5, loads)
+    assert idx.shape == (5, 5) and idx.dtype == torch.int32
+    assert np.bincount(idx.numpy().ravel(), minlength=7).tolist() == loads
+    assert all(len(set(row.tolist())) == 5 for row in idx)

@@ -234,3 +234,14 @@ def make_loads(E: int, T: int, K: int, seed: int = 0, at_mean: int = 4) -> torch
         load[:at_mean] = mean
         load[at_mean] += surplus              # keep the total
     return load.to(torch.int32)
+
+def topk_with_loads(T: int, K: int, loads) -> torch.Tensor:
+    """[T, K] int32 expert choices whose per-expert counts are exactly ``loads`` (each at
+    most T, summing to T*K), K distinct experts per token: the choices listed expert by
+    expert fill the slots column by column, so a token's K slots lie T apart in the list
+    and never repeat an expert.  A permutation-stage input with a prescribed histogram
+    (row-block edge cases of the grouped GEMMs)."""
+    loads = [int(v) for v in loads]
+    assert sum(loads) == T * K and max(loads) <= T
+    flat = torch.cat([torch.full((n,), e, dtype=torch.int32) for e, n in enumerate(loads) if n])
+    return flat.reshape(K, T).t().contiguous()
