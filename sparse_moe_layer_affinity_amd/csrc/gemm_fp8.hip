@@ -32,7 +32,7 @@ namespace moe {
 
 struct Fp8Args {
   const uint8_t* A;          // e4m3 activations: xq [T, K] (gather) or hq [rows, K]
-  const float* a_scales;     // [a_rows, K/128]
+  const float* a_scales;     // [K/128, a_rows] (transposed)
   const int32_t* row_token;  // gather map of routed rows (gather only)
   const int32_t* offsets;    // [E+1]
   const int32_t* tile_off;   // [G+1] unit prefix per group
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     if (row < mvalid) {
       const int r = m0 + row;
       const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      voff_s = uint32_t(src) * uint32_t(KBLK) * 4u;
+      voff_s = uint32_t(src) * 4u;
     }
   } else {
     // gated: wave 4 the gate block, wave 5 the up block (same block index); plain:
@@ -136,6 +136,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     rsrc_s = make_rsrc((up ? a.S1 : a.S0) + size_t(g) * a.s_stride, uint32_t(a.s_stride) * 4u);
     if (w < 6 && l == 0) voff_s = uint32_t(blk * KBLK) * 4u;
   }
+  // K block ks of the scales: token scales [K/128, a_rows], weight scales [.., K/128]
+  const uint32_t s_step = w < 4 ? uint32_t(a.a_rows) * 4u : 4u;
   const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
   const uint32_t wave_w = lds_base + kWOff + uint32_t(w) * (WSTAGE / 8);
   const uint32_t wave_t = lds_base + kTOff + uint32_t(w) * (TSTAGE / 8);
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   auto load_t = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + j * 1024u);
-    dma4(rsrc_s, voff_s, uint32_t(ks) * 4u, wave_s + uint32_t(ks & 1) * 1024u);
+    dma4(rsrc_s, voff_s, uint32_t(ks) * s_step, wave_s + uint32_t(ks & 1) * 1024u);
   };
 
   // ---- wave geometry: 2 (weight rows) x 4 (tokens) --------------------------------
@@ -305,7 +307,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
   const int TK = T * c.top_k, G = E + Ns, rows = TK + T * Ns;
   const int H = c.hidden, I = c.inter;
-  hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s);
+  hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s, true);
   if (err != hipSuccess) return err;
   // one block per unit: two blocks of one expert side by side on one XCD (sharing each
   // weight tile through L2) measured 47% slower than dealing the blocks separately
@@ -340,7 +342,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.a_rows = T;
   hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles * kUnit), dim3(512),
                      0, s, a);
-  err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s);
+  err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true);
   if (err != hipSuccess) return err;
   Fp8Args d = a;
   d.A = ws.hq;

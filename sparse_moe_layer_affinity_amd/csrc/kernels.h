@@ -17,9 +17,9 @@ struct Workspace {
   int32_t* order;      // [row-block bound] the units, largest first
   void* h;             // [rows, inter] act dtype (SwiGLU output of the first GEMM)
   uint8_t* hq;         // [rows, inter] e4m3 codes of h (e4m3 weights)
-  float* h_scales;     // [rows, inter/128] (e4m3 weights)
+  float* h_scales;     // [inter/128, rows] (e4m3 weights; transposed)
   uint8_t* xq;         // [T, hidden] e4m3 codes
-  float* x_scales;     // [T, hidden/128]
+  float* x_scales;     // [hidden/128, T] (transposed)
   void* y_rows;        // [rows, hidden] act dtype (layer forward)
   size_t bytes;        // total bytes of the layout
 };
@@ -71,7 +71,7 @@ hipError_t launch_permute(const moe_config& c, const int32_t* idx, int32_t* load
                           int32_t* offsets, int32_t* row_token, int32_t* pair_row,
                           const Workspace& ws, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
-                            hipStream_t s);
+                            hipStream_t s, bool transposed = false);
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
                               const int32_t* row_token, const moe_expert_weights& w,
                               void* y_rows, const Workspace& ws, hipStream_t s);

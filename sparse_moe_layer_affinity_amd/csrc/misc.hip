@@ -115,9 +115,12 @@ hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float ga
 // Each lane owns 8 consecutive columns (one 16-byte load); 16 lanes cover one
 // 128-column block and a wave four blocks.  amax by butterfly max inside the 16
 // lanes; scale = amax / 448 (1 if amax == 0); code = RNE-saturate(x / scale).
+// Scales go to [rows, cols/128] (the C ABI's layout) or, transposed, to [cols/128, rows]
+// (the expert GEMM's workspace copies: one K block's scales of consecutive rows are
+// then adjacent).
 __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x, int rows,
                                                       int cols, uint8_t* __restrict__ q,
-                                                      float* __restrict__ scales) {
+                                                      float* __restrict__ scales, int transposed) {
   const int bpr = cols / 128;                                   // blocks per row
   const long long blk = (1LL * blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + ((threadIdx.x >> 4) & 3);
   const bool valid = blk < 1LL * rows * bpr;
@@ -147,14 +150,14 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
   *reinterpret_cast<uint2*>(q + off) =
       make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                  c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-  if (l16 == 0) scales[size_t(r) * bpr + j] = s;
+  if (l16 == 0) scales[transposed ? size_t(j) * rows + r : size_t(r) * bpr + j] = s;
 }
 
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
-                            hipStream_t s) {
+                            hipStream_t s, bool transposed) {
   const long long blocks = 1LL * rows * (cols / 128);
   hipLaunchKernelGGL(act_quant_e4m3, dim3(unsigned((blocks + 15) / 16)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), rows, cols, q, scales);
+                     static_cast<const uint16_t*>(x), rows, cols, q, scales, transposed ? 1 : 0);
   return hipGetLastError();
 }
 

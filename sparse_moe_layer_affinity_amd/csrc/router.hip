@@ -61,9 +61,20 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
     int e = l + 64 * j;
     v[j] = -INFINITY;
     if (active && e < E) {
-      // logit = the split-K partials summed in split order (one partial unless split)
+      // logit = the split-K partials summed in split order (one partial unless split);
+      // eight partials are loaded ahead of their adds so the loads overlap
       float zz = z[size_t(t) * E + e];
-      for (int p = 1; p < splits; ++p) zz += z[(size_t(p) * T + t) * E + e];
+      const size_t stride = size_t(T) * E;
+      const float* zp = z + size_t(t) * E + e;
+      int p = 1;
+      for (; p + 8 <= splits; p += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = zp[size_t(p + i) * stride];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zz += v[i];
+      }
+      for (; p < splits; ++p) zz += zp[size_t(p) * stride];
       float s = 1.0f / (1.0f + expf(-zz));
       float sb = s + bias[e];
       s_lds[w][e] = s;
