@@ -10,195 +10,17 @@
 // Both operands are K-contiguous (x and h rows, weight rows), which is exactly the
 // operand layout of the MFMA: no transposes anywhere.
 //
-// Expert GEMMs use grouped_gemm_dma (below: row blocks of up to 320 rows, operands
-// loaded straight into LDS); the router logits use the simpler 128 x 128
-// grouped_gemm_bf16 (v_mfma_f32_16x16x32_bf16, padded LDS, one slice of prefetch).
-// In both, GEMM1's B tile stacks BN/2 gate rows over the matching BN/2 up rows and
-// every wave owns the same columns of both halves, so the SwiGLU epilogue runs in
-// registers; accumulation is fp32.
+// One kernel, grouped_gemm_dma (below: row blocks of up to 320 rows, operands loaded
+// straight into LDS), runs both expert GEMMs and the router logits (one group of T
+// rows, fp32 split-K partials).  GEMM1's B tile stacks 128 gate rows over the
+// matching 128 up rows and every wave owns the same columns of both halves, so the
+// SwiGLU epilogue runs in registers; accumulation is fp32.
 
 #include <type_traits>
 
 #include "gemm_common.h"
 
 namespace moe {
-
-
-
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_bf16(GemmArgs a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = 64;
-  constexpr int LD = BK + 8;                  // padded LDS row pitch (bf16 elements)
-  constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile: rows x B-rows
-  constexpr int NI = WTM / 16, NJ = WTN / 16;
-  constexpr int CA = BM * (BK / 8) / NT;      // 16-byte chunks per thread per slice
-  constexpr int CB = BN * (BK / 8) / NT;
-  constexpr int BN_OUT = MODE == kGatedBf16 ? BN / 2 : BN;
-  static_assert(CA * NT == BM * (BK / 8) && CB * NT == BN * (BK / 8), "tile/threads");
-  static_assert(MODE != kGatedBf16 || NJ % 2 == 0, "gated tiles pair gate/up blocks");
-
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LD];
-
-  // ---- tile decode --------------------------------------------------------
-  const int total_m = a.tile_off ? a.tile_off[a.G] : ceil_div(a.T, BM);
-  const int total = total_m * a.n_tiles;
-  const int b = blockIdx.x;
-  if (b >= total) return;
-  const int per = total / kXcds, rem = total % kXcds;
-  const int xcd = b % kXcds, slot = b / kXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-
-  int g, nt, mt, r0, r1;
-  if (a.tile_off) {
-    int lo = 0, hi = a.G;
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (a.tile_off[mid] * a.n_tiles <= logical) lo = mid; else hi = mid;
-    }
-    g = lo;
-    const int mtiles = a.tile_off[g + 1] - a.tile_off[g];
-    const int local = logical - a.tile_off[g] * a.n_tiles;
-    nt = local / mtiles;
-    mt = local % mtiles;
-    group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
-  } else {
-    g = 0;
-    nt = logical / total_m;
-    mt = logical % total_m;
-    r0 = 0;
-    r1 = a.T;
-  }
-  const int m0 = r0 + mt * BM;
-  const int mvalid = min(BM, r1 - m0);
-  const int n0 = nt * BN_OUT;
-
-  const int tid = threadIdx.x;
-  const int K = a.K;
-  // split-K (router): this block sums K range [kbeg, kbeg + klen) into partial ks
-  const int ks = blockIdx.y;
-  const int kbeg = ks * a.k_chunk;
-  const int klen = min(a.k_chunk, K - kbeg);
-
-  // ---- per-thread global source pointers ----------------------------------
-  const uint16_t* pa[CA];
-  const uint16_t* pb[CB];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int c = tid + i * NT;
-    const int row = min(c >> 3, mvalid - 1);      // padding rows re-read the last valid row
-    const int r = m0 + row;
-    const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-    pa[i] = a.A + size_t(src) * K + kbeg + (c & 7) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int c = tid + i * NT;
-    const int brow = c >> 3;
-    const uint16_t* base = a.B0;
-    int n = n0 + brow;
-    if (MODE == kGatedBf16 && brow >= BN / 2) {
-      base = a.B1;
-      n = n0 + brow - BN / 2;
-    }
-    n = min(n, a.N - 1);
-    pb[i] = base + size_t(g) * a.b_stride + size_t(n) * K + kbeg + (c & 7) * 8;
-  }
-
-  uint4 ra[CA], rb[CB];
-  auto load_slice = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const uint4*>(pa[i] + k0);
-#pragma unroll
-    for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const uint4*>(pb[i] + k0);
-  };
-  auto store_slice = [&]() {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<uint4*>(&As[(c >> 3) * LD + (c & 7) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<uint4*>(&Bs[(c >> 3) * LD + (c & 7) * 8]) = rb[i];
-    }
-  };
-
-  const int w = tid >> 6, l = tid & 63;
-  const int wm = w / WN, wn = w % WN;
-  int brow0[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (MODE == kGatedBf16) {
-      brow0[j] = j < NJ / 2 ? wn * (WTN / 2) + j * 16 : BN / 2 + wn * (WTN / 2) + (j - NJ / 2) * 16;
-    } else {
-      brow0[j] = wn * WTN + j * 16;
-    }
-  }
-
-  f32x4_t acc[NI][NJ];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = klen / BK;
-  load_slice(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    store_slice();
-    __syncthreads();
-    if (kt + 1 < nk) load_slice((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t af[NI], bfr[NJ];
-      const int koff = ks * 32 + (l >> 4) * 8;
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * WTM + i * 16 + (l & 15)) * LD + koff]);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[(brow0[j] + (l & 15)) * LD + koff]);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane l holds rows (l/16)*4 + q, column l%16 of each 16x16 block
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rl = wm * WTM + i * 16 + (l >> 4) * 4 + q;
-      if (rl >= mvalid) continue;
-      const size_t row = size_t(m0 + rl);
-      if (MODE == kGatedBf16) {
-#pragma unroll
-        for (int j = 0; j < NJ / 2; ++j) {
-          const int col = n0 + wn * (WTN / 2) + j * 16 + (l & 15);
-          const float gt = acc[i][j][q], up = acc[i][j + NJ / 2][q];
-          const float hv = gt / (1.0f + expf(-gt)) * up;
-          if (col < a.N) static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(hv);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int col = n0 + wn * WTN + j * 16 + (l & 15);
-          if (col >= a.N) continue;
-          if (MODE == kPlainF32)
-            static_cast<float*>(a.C)[ks * a.c_split_stride + row * a.ldc + col] = acc[i][j][q];
-          else
-            static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(acc[i][j][q]);
-        }
-      }
-    }
-  }
-}
 
 // ---- LDS-DMA pipelined kernel for the expert GEMMs ---------------------------
 // Tile: up to 320 rows (one expert's whole row block in the common case: about
@@ -279,24 +101,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   const int round = slot / per_round, rs = slot % per_round;
   const int nt = rs / a.unit, u = rs % a.unit;
   const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
-  if (pos >= a.tile_off[a.G]) return;
-  const int id = a.order[pos];
-  int lo = 0, hi = a.G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] <= id) lo = mid; else hi = mid;
-  }
-  const int g = lo;
-  const int mt = (id - a.tile_off[g]) * a.unit + u;
-  int r0, r1;
-  group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
-  if (mt * BM >= r1 - r0) return;                        // unit with fewer blocks
+  int g = 0, r0 = 0, r1 = a.T, mt = pos;
+  if (a.tile_off) {
+    if (pos >= a.tile_off[a.G]) return;
+    const int id = a.order[pos];
+    int lo = 0, hi = a.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tile_off[mid] <= id) lo = mid; else hi = mid;
+    }
+    g = lo;
+    mt = (id - a.tile_off[g]) * a.unit + u;
+    group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
+  }                                     // else: one group of T rows (router logits)
+  if (mt * BM >= r1 - r0) return;                        // past the group's blocks
   const int m0 = r0 + mt * BM;
   const int mvalid = min(BM, r1 - m0);
   const int n0 = nt * BN_OUT;
   const int tid = threadIdx.x;
-  const int K = a.K;
-  const uint32_t row_bytes = uint32_t(K) * 2u;
+  // split-K (router logits): this workgroup's K range, its own partial output slice
+  const int kst0 = blockIdx.y * (a.k_chunk / BK);      // first stage
+  const int K = a.k_chunk ? min(a.k_chunk, a.K - blockIdx.y * a.k_chunk) : a.K;
+  const uint32_t row_bytes = uint32_t(a.K) * 2u;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
 
   // ---- this wave's share of every stage: A rows 80 w.., B rows 64 w.. ---------------
@@ -332,11 +158,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   const uint32_t wave_b = lds_base + uint32_t(w) * (BSTAGE / 4);
   auto dma_a = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
     constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
-    dma16(rsrc_a, voff_a[j], uint32_t(ks) * ROWB, wave_a + uint32_t(par * ASTAGE + j * 1024));
+    dma16(rsrc_a, voff_a[j], uint32_t(ks + kst0) * ROWB, wave_a + uint32_t(par * ASTAGE + j * 1024));
   };
   auto dma_b = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
     constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
-    dma16(rsrc_b, voff_b[j], uint32_t(ks) * ROWB, wave_b + uint32_t(par * BSTAGE + j * 1024));
+    dma16(rsrc_b, voff_b[j], uint32_t(ks + kst0) * ROWB, wave_b + uint32_t(par * BSTAGE + j * 1024));
   };
 
   // ---- fragment geometry: per-step lane bases; buffer and block offsets are immediates
@@ -502,6 +328,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
         [&](auto m) __attribute__((always_inline)) { mfma_of(S3{}, m, F_{}); }, none, none);
 
     // ---- epilogue -------------------------------------------------------------------
+    // plain output element: bf16, or fp32 into this split's partial slice (router)
+    auto put = [&](size_t row, int col, float v) __attribute__((always_inline)) {
+      if constexpr (MODE == kPlainF32)
+        static_cast<float*>(a.C)[size_t(blockIdx.y) * a.c_split_stride + row * a.ldc + col] = v;
+      else
+        static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(v);
+    };
     auto store_block = [&](const f32x16_t* accs, int rbase) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -519,8 +352,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int col = n0 + wn * WTN + j * 32 + (l & 31);
-            if (col < a.N)
-              static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(accs[j][r]);
+            if (col < a.N) put(row, col, accs[j][r]);
           }
         }
       }
@@ -545,8 +377,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int col = n0 + wn * WTN + (jb + 2 * h) * 32 + (l & 31);
-              if (col < a.N)
-                static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(accx[2 * st + h][r]);
+              if (col < a.N) put(row, col, accx[2 * st + h][r]);
             }
           }
         }
@@ -682,11 +513,13 @@ __global__ __launch_bounds__(256) void gemm2_f32(const float* __restrict__ h,
 }
 
 // ---- launch configuration ---------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;      // router logits
 
 
 hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const uint16_t* w,
                                    float* z, hipStream_t s) {
+  // one group of T rows, blocks of kExpertBM rows x all E columns, split-K over
+  // router_splits(c) K ranges into fp32 partials [splits, T, E] (summed in order by the
+  // selection kernel)
   GemmArgs a{};
   a.A = x;
   a.B0 = w;
@@ -695,16 +528,16 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   a.ldc = c.num_experts;
   a.N = c.num_experts;
   a.K = c.hidden;
-  a.E = 0;
   a.T = c.num_tokens;
-  a.TK = 0;
   a.G = 1;
-  a.n_tiles = ceil_div(c.num_experts, kBN);
+  a.unit = 1;
+  a.n_tiles = ceil_div(c.num_experts, 256);
+  a.a_rows = c.num_tokens;
   a.k_chunk = router_k_chunk(c);
   a.c_split_stride = 1LL * c.num_tokens * c.num_experts;
-  const int grid = ceil_div(c.num_tokens, kBM) * a.n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_bf16<kBM, kBN, kWM, kWN, kPlainF32>),
-                     dim3(grid, router_splits(c)), dim3(kWM * kWN * 64), 0, s, a);
+  const int rounds = ceil_div(ceil_div(c.num_tokens, kExpertBM), kXcds);
+  hipLaunchKernelGGL(grouped_gemm_dma<kPlainF32>, dim3(rounds * kXcds * a.n_tiles, router_splits(c)),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

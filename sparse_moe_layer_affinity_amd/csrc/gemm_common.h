@@ -29,24 +29,12 @@ struct GemmArgs {
 
 enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };
 
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
-
-__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
 }
 
 constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range: reads zero
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
-// memory, which on gfx9 means draining every outstanding global load at each
-// barrier; the K loop keeps its next slice's loads in flight across barriers.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // ---- direct global -> LDS loads ("buffer_load_dwordx4 ... lds") ---------------------
 // Lane i of one instruction writes its 16 bytes at LDS byte M0 + 16 i.  Issued from

@@ -46,21 +46,26 @@ inline int expert_units_upper(const moe_config& c, int bm, int unit) {
 
 Workspace workspace_layout(const moe_config& c, void* base);
 
-// Split-K factor of the bf16 router-logits GEMM: enough 128 x 128 tiles x splits to
-// fill the chip at small T; the fp32 partials are summed in order by the selection
-// kernel.  1 for fp32 activations.
+// Split-K factor of the bf16 router-logits GEMM: enough row blocks (kExpertBM rows) x
+// splits to fill the chip at small T, each split an even number (at least 8, unless K
+// is shorter) of 64-wide K stages;
+// the fp32 partials are summed in order by the selection kernel.  1 for fp32
+// activations.
+inline int router_k_chunk(const moe_config& c) {
+  const int stages = c.hidden / 64;                       // even: hidden % 128 == 0
+  const int blocks = (c.num_tokens + kExpertBM - 1) / kExpertBM;
+  int s = 256 / blocks;
+  s = s < 1 ? 1 : s;
+  int chunk = (stages + s - 1) / s;
+  chunk = chunk < 8 ? 8 : chunk;                          // >= 8 stages: fixed costs amortised
+  chunk = chunk > stages ? stages : chunk;
+  chunk += chunk & 1;                                     // even stage count
+  return chunk * 64;
+}
 inline int router_splits(const moe_config& c) {
   if (c.act_dtype == MOE_F32) return 1;
-  const int tiles = ((c.num_tokens + 127) / 128) * ((c.num_experts + 127) / 128);
-  int s = 256 / tiles;
-  const int kmax = c.hidden / 128;
-  s = s < 1 ? 1 : (s > kmax ? kmax : s);
-  const int chunk = ((c.hidden + s - 1) / s + 63) / 64 * 64;
+  const int chunk = router_k_chunk(c);
   return (c.hidden + chunk - 1) / chunk;
-}
-inline int router_k_chunk(const moe_config& c) {
-  const int s = router_splits(c);
-  return ((c.hidden + s - 1) / s + 63) / 64 * 64;
 }
 
 hipError_t launch_router_logits(const moe_config& c, const void* x, const void* w, float* z,

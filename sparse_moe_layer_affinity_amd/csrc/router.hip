@@ -54,6 +54,34 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
   const bool active = t < T;
   const int n = E / G;
 
+  // logits = the split-K partials summed in split order (one partial unless split);
+  // the lane's four experts load four partials each ahead of the in-order adds, so
+  // sixteen loads are in flight per round trip
+  float zz[4];
+  const size_t stride = size_t(T) * E;
+  const size_t tofs = size_t(active ? t : 0) * E;
+  auto part = [&](int p, int j) {
+    const int e = l + 64 * j;
+    return (active && e < E) ? z[size_t(p) * stride + tofs + e] : 0.0f;
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) zz[j] = part(0, j);
+  int p = 1;
+  for (; p + 4 <= splits; p += 4) {
+    float pv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv[i][j] = part(p + i, j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) zz[j] += pv[i][j];
+  }
+  for (; p < splits; ++p)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zz[j] += part(p, j);
+
   // affinities and biased affinities (fp32)
   float v[4];
 #pragma unroll
@@ -61,21 +89,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
     int e = l + 64 * j;
     v[j] = -INFINITY;
     if (active && e < E) {
-      // logit = the split-K partials summed in split order (one partial unless split);
-      // eight partials are loaded ahead of their adds so the loads overlap
-      float zz = z[size_t(t) * E + e];
-      const size_t stride = size_t(T) * E;
-      const float* zp = z + size_t(t) * E + e;
-      int p = 1;
-      for (; p + 8 <= splits; p += 8) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = zp[size_t(p + i) * stride];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) zz += v[i];
-      }
-      for (; p < splits; ++p) zz += zp[size_t(p) * stride];
-      float s = 1.0f / (1.0f + expf(-zz));
+      float s = 1.0f / (1.0f + expf(-zz[j]));
       float sb = s + bias[e];
       s_lds[w][e] = s;
       sb_lds[w][e] = sb;
