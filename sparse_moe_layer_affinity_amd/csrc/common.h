@@ -13,12 +13,20 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
+}
+
+// Two fp32 values to packed bf16 (x0 in the low half), round to nearest even, by the
+// hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x0, x1}, bf16x2_t));
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).

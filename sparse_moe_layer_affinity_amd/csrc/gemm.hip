@@ -79,13 +79,18 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16_t* c) {
                : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]));
 }
 
-template <int MODE>
+// SHORT_K: K = 128 (two stages) only; otherwise K >= 256 (for split-K: every split).
+// The two-stage sequence is compiled apart from the K loop: in one function it makes
+// the register allocator spill around the loop.
+template <int MODE, bool SHORT_K>
 __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   constexpr int BM = kExpertBM, BMAIN = 256, BN = 256, BK = 64, ROWB = 128;
   constexpr int ASTAGE = BM * ROWB;           // 40 KB
   constexpr int BSTAGE = BN * ROWB;           // 32 KB
   constexpr int WTM = 128, WTN = 128, NJ = 4;
   constexpr int BN_OUT = MODE == kGatedBf16 ? BN / 2 : BN;
+  // bf16 outputs: the MFMAs compute the transposed tile (see the epilogue)
+  constexpr bool kTr = MODE != kPlainF32;
   constexpr int NDA = BM / 32, NDB = BN / 32; // DMA instructions per wave per stage
   __shared__ __attribute__((aligned(1024))) uint4 lds[(2 * ASTAGE + 2 * BSTAGE) / 16];
 
@@ -197,8 +202,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     constexpr int XW = decltype(xw_tag)::value;    // the wave's wm, for the extra blocks
     constexpr int NA = NIV + NX;                   // A fragments per K-step
     constexpr int NMS = NIV * NJ + 2 * NX;         // MFMAs per K-step
-    // extra MFMA e: strip e / 2, B block xb(e) (gated: the gate block and its up block)
-    constexpr auto xb = [](int e) constexpr { return ((e >> 1) == 0 ? XW : 1 - XW) + 2 * (e & 1); };
+    // extra MFMA e: strip e / 2, B block xb(e) (gated: the gate block and its up block;
+    // plain: two adjacent blocks, so the strip's outputs of a wave are 64 adjacent columns)
+    constexpr auto xb = [](int e) constexpr {
+      const int xh = (e >> 1) == 0 ? XW : 1 - XW;
+      return MODE == kGatedBf16 ? xh + 2 * (e & 1) : 2 * xh + (e & 1);
+    };
     constexpr int NRB = NA > 0 ? NJ : 0;           // B fragments per K-step (skipped if idle)
     f32x16_t acc[NIV > 0 ? NIV : 1][NJ];
     f32x16_t accx[NJ];
@@ -236,13 +245,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       constexpr int s4 = decltype(s_tag)::value, m = decltype(m_tag)::value;
       if constexpr (m < NIV * NJ) {
         constexpr int i = m / NJ, j = m % NJ;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s4 & 1][i], fb[s4][j], acc[i][j], 0, 0, 0);
+        if constexpr (kTr)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s4][j], fa[s4 & 1][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s4 & 1][i], fb[s4][j], acc[i][j], 0, 0, 0);
       } else {
         constexpr int e = m - NIV * NJ;
+        const bf16x8_t& xa = fa[s4 & 1][NIV + (e >> 1)];
+        const bf16x8_t& xbf = fb[s4][xb(e)];
         if constexpr (decltype(first_tag)::value)
-          mfma_vgpr_first(accx[e], fa[s4 & 1][NIV + (e >> 1)], fb[s4][xb(e)]);
+          mfma_vgpr_first(accx[e], kTr ? xbf : xa, kTr ? xa : xbf);
         else
-          mfma_vgpr(accx[e], fa[s4 & 1][NIV + (e >> 1)], fb[s4][xb(e)]);
+          mfma_vgpr(accx[e], kTr ? xbf : xa, kTr ? xa : xbf);
       }
     };
     auto none = [&](auto) __attribute__((always_inline)) {};
@@ -311,10 +325,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     wait_vmcnt<NDB>();
     stage_barrier();
     // nk = K / 64 is even (K is a multiple of 128)
-    if (nk == 2) {
+    auto two_stages = [&]() __attribute__((always_inline)) {
       stage(0, P0{}, F_{}, T_{}, F_{}, T_{}, V0{});
       stage(1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{});
-    } else {
+    };
+    auto k_loop = [&]() __attribute__((always_inline)) {
       stage(0, P0{}, F_{}, T_{}, T_{}, T_{}, VB{});
       stage(1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{});
       for (int k = 2; k < nk - 2; k += 2) {
@@ -323,65 +338,169 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       }
       stage(nk - 2, P0{}, T_{}, T_{}, F_{}, T_{}, V0{});
       stage(nk - 1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{});
+    };
+    if constexpr (SHORT_K) {
+      two_stages();
+    } else {
+      k_loop();
     }
     interleave<NMS / 2, NMS, 0, 0>(
         [&](auto m) __attribute__((always_inline)) { mfma_of(S3{}, m, F_{}); }, none, none);
 
     // ---- epilogue -------------------------------------------------------------------
-    // plain output element: bf16, or fp32 into this split's partial slice (router)
-    auto put = [&](size_t row, int col, float v) __attribute__((always_inline)) {
-      if constexpr (MODE == kPlainF32)
-        static_cast<float*>(a.C)[size_t(blockIdx.y) * a.c_split_stride + row * a.ldc + col] = v;
-      else
-        static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(v);
-    };
-    auto store_block = [&](const f32x16_t* accs, int rbase) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = rbase + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
-        if (rl >= mvalid) continue;
-        const size_t row = size_t(m0 + rl);
-        if (MODE == kGatedBf16) {
-#pragma unroll
-          for (int j = 0; j < NJ / 2; ++j) {
-            const int col = n0 + wn * (WTN / 2) + j * 32 + (l & 31);
-            const float hv = silu_fast(accs[j][r]) * accs[j + NJ / 2][r];
-            if (col < a.N) static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(hv);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + (l & 31);
-            if (col < a.N) put(row, col, accs[j][r]);
-          }
-        }
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < NIV; ++i) store_block(acc[i], wm * WTM + i * 32);
-    if constexpr (NX > 0) {
-      mfma_vgpr_drain(accx);
-      static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
-        constexpr int st = decltype(st_tag)::value;
-        constexpr int jb = st == 0 ? XW : 1 - XW;       // the strip's first block
+    // bf16 modes: the MFMAs compute the transposed tile (weight rows are the MFMA's
+    // rows): value r of lane l of a 32 x 32 accumulator is output row l & 31 of its
+    // block and column 8 (r >> 2) + 4 (l >> 5) + (r & 3), so each group of four values
+    // is four adjacent columns of one row.
+    if constexpr (NX > 0) mfma_vgpr_drain(accx);
+    // lane id recomputed here: lane expressions shared with the prologue would otherwise
+    // stay live (and spill) across the K loop
+    const int le = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    const int lr = le & 31, lh = le >> 5;
+    if constexpr (MODE == kPlainF32) {
+      // fp32 partials (not transposed: lane l holds column l & 31 of rows
+      // 8 (r >> 2) + 4 (l >> 5) + (r & 3)), 128 contiguous bytes per row and store
+      float* const cz = static_cast<float*>(a.C) + size_t(blockIdx.y) * a.c_split_stride;
+      auto put_blk = [&](const f32x16_t& v, int rb, int col) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rl = BMAIN + 32 * st + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
-          if (rl >= mvalid) continue;
-          const size_t row = size_t(m0 + rl);
-          if (MODE == kGatedBf16) {
-            const int col = n0 + wn * (WTN / 2) + jb * 32 + (l & 31);
-            const float hv = silu_fast(accx[2 * st][r]) * accx[2 * st + 1][r];
-            if (col < a.N) static_cast<uint16_t*>(a.C)[row * a.ldc + col] = f32_to_bf16_bits(hv);
-          } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int col = n0 + wn * WTN + (jb + 2 * h) * 32 + (l & 31);
-              if (col < a.N) put(row, col, accx[2 * st + h][r]);
-            }
-          }
+          const int rl = rb + (r >> 2) * 8 + lh * 4 + (r & 3);
+          if (rl < mvalid && col < a.N) cz[size_t(m0 + rl) * a.ldc + col] = v[r];
         }
+      };
+#pragma unroll
+      for (int i = 0; i < NIV; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) put_blk(acc[i][j], wm * WTM + i * 32, n0 + wn * WTN + j * 32 + lr);
+      static_for<0, 2 * NX>([&](auto e_tag) __attribute__((always_inline)) {
+        constexpr int e = decltype(e_tag)::value;
+        put_blk(accx[e], BMAIN + 32 * (e >> 1), n0 + wn * WTN + xb(e) * 32 + lr);
       });
+    } else {
+      // bf16 outputs go through LDS: each wave writes its rows into its own 32 KB
+      // region (8-byte writes of four adjacent columns), then reads whole rows back 16
+      // bytes per lane and stores them with full-line 16-byte global stores.  A staging
+      // row of P bytes has P / 16 chunks; chunk c of row r sits in slot
+      // c ^ ((r / (256 / P)) % (P / 16)) and its 8-byte halves are swapped when bit 4 of
+      // r is set: the 32 lanes of a half-wave write 32 distinct bank pairs, and every
+      // 16-lane quarter of a read covers the 64 banks once.
+      stage_barrier();                          // every wave is done with the last stage
+      char* const stg = reinterpret_cast<char*>(lds) + w * 32768;
+      uint16_t* const cout = static_cast<uint16_t*>(a.C);
+      auto pack = [](float x0, float x1) __attribute__((always_inline)) { return pack_bf16x2(x0, x1); };
+      // this lane's write slot base for pitch P: row lr, chunk 0, half lh
+      auto wslot = [&](auto p_tag) __attribute__((always_inline)) {
+        constexpr int P = decltype(p_tag)::value, CH = P / 16, RPB = 256 / P;
+        return uint32_t(lr * P + (((lr / RPB) % CH) << 4) + ((lh ^ ((lr >> 4) & 1)) << 3));
+      };
+      auto put8 = [&](uint32_t slot, int rb, int pitch, int c, uint32_t lo, uint32_t hi)
+          __attribute__((always_inline)) {
+        *reinterpret_cast<uint2*>(stg + rb * pitch + (slot ^ uint32_t(c << 4))) = make_uint2(lo, hi);
+      };
+      // staged rows [sb, sb + NR) of pitch P (P / 2 columns) to output rows
+      // m0 + rb + (0 .. NR), columns from cb; rows past vrows are not stored
+      auto drain = [&](auto p_tag, auto nr_tag, int sb, int rb, int vrows, int cb)
+          __attribute__((always_inline)) {
+        constexpr int P = decltype(p_tag)::value, CH = P / 16, RPB = 256 / P, RPI = 64 / CH;
+        constexpr int NR = decltype(nr_tag)::value;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int c = le % CH, col = cb + 8 * c;
+        constexpr int NQ = NR / RPI, QG = NQ < 4 ? NQ : 4;   // reads in flight per group
+#pragma unroll
+        for (int q0 = 0; q0 < NQ; q0 += QG) {
+          if (q0 * RPI >= vrows) break;
+          uint4 v[QG];
+#pragma unroll
+          for (int u = 0; u < QG; ++u) {
+            const int rs = sb + (q0 + u) * RPI + le / CH;
+            v[u] = *reinterpret_cast<const uint4*>(stg + rs * P + ((c ^ ((rs / RPB) % CH)) << 4));
+          }
+#pragma unroll
+          for (int u = 0; u < QG; ++u) {
+            const int r = (q0 + u) * RPI + le / CH, rs = sb + r;
+            if ((rs >> 4) & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
+            if (r < vrows && col < a.N)
+              *reinterpret_cast<uint4*>(cout + size_t(m0 + rb + r) * a.ldc + col) = v[u];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      };
+      const int wrows = min(mvalid - wm * WTM, WTM);      // this wave's valid main rows
+      if constexpr (MODE == kGatedBf16) {
+        // h = silu(gate) * up: 64 columns per wave (gate blocks 0, 1 with up blocks 2, 3)
+        using PW = std::integral_constant<int, 128>;
+        const uint32_t sl = wslot(PW{});
+#pragma unroll
+        for (int i = 0; i < NIV; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float hv[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                hv[t] = silu_fast(acc[i][j][4 * g + t]) * acc[i][j + NJ / 2][4 * g + t];
+              put8(sl, i * 32, 128, 4 * j + g, pack(hv[0], hv[1]), pack(hv[2], hv[3]));
+            }
+        if constexpr (NIV > 0)
+          drain(PW{}, std::integral_constant<int, NIV * 32>{}, 0, wm * WTM, wrows, n0 + wn * (WTN / 2));
+        if constexpr (NX > 0) {
+          // strips: 32 columns per wave and strip (gate accx[2 st], up accx[2 st + 1])
+          using PX = std::integral_constant<int, 64>;
+          const uint32_t sx = wslot(PX{});
+          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_tag)::value;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float hv[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                hv[t] = silu_fast(accx[2 * st][4 * g + t]) * accx[2 * st + 1][4 * g + t];
+              put8(sx, st * 32, 64, g, pack(hv[0], hv[1]), pack(hv[2], hv[3]));
+            }
+          });
+          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_tag)::value;
+            constexpr int xh = st == 0 ? XW : 1 - XW;
+            drain(PX{}, std::integral_constant<int, 32>{}, 32 * st, BMAIN + 32 * st,
+                  mvalid - BMAIN - 32 * st, n0 + wn * (WTN / 2) + xh * 32);
+          });
+        }
+      } else {
+        // 128 columns per wave
+        using PW = std::integral_constant<int, 256>;
+        const uint32_t sl = wslot(PW{});
+#pragma unroll
+        for (int i = 0; i < NIV; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              put8(sl, i * 32, 256, 4 * j + g, pack(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                   pack(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        if constexpr (NIV > 0)
+          drain(PW{}, std::integral_constant<int, NIV * 32>{}, 0, wm * WTM, wrows, n0 + wn * WTN);
+        if constexpr (NX > 0) {
+          // strips: 64 adjacent columns per wave and strip (blocks xb(2 st), xb(2 st) + 1)
+          using PX = std::integral_constant<int, 128>;
+          const uint32_t sx = wslot(PX{});
+          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_tag)::value;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                put8(sx, st * 32, 128, 4 * h + g, pack(accx[2 * st + h][4 * g], accx[2 * st + h][4 * g + 1]),
+                     pack(accx[2 * st + h][4 * g + 2], accx[2 * st + h][4 * g + 3]));
+          });
+          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_tag)::value;
+            drain(PX{}, std::integral_constant<int, 32>{}, 32 * st, BMAIN + 32 * st,
+                  mvalid - BMAIN - 32 * st, n0 + wn * WTN + xb(2 * st) * 32);
+          });
+        }
+      }
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -536,8 +655,9 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   a.k_chunk = router_k_chunk(c);
   a.c_split_stride = 1LL * c.num_tokens * c.num_experts;
   const int rounds = ceil_div(ceil_div(c.num_tokens, kExpertBM), kXcds);
-  hipLaunchKernelGGL(grouped_gemm_dma<kPlainF32>, dim3(rounds * kXcds * a.n_tiles, router_splits(c)),
-                     dim3(256), 0, s, a);
+  const dim3 grid(rounds * kXcds * a.n_tiles, router_splits(c));
+  if (c.hidden == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -595,8 +715,9 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL(grouped_gemm_dma<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles * kUnit), dim3(256), 0,
-                     s, a);
+  const dim3 grid1(rounds * kXcds * a.n_tiles * kUnit);
+  if (H == 128) hipLaunchKernelGGL((grouped_gemm_dma<kGatedBf16, true>), grid1, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_gemm_dma<kGatedBf16, false>), grid1, dim3(256), 0, s, a);
   GemmArgs d = a;
   d.A = static_cast<const uint16_t*>(ws.h);
   d.row_token = nullptr;
@@ -610,8 +731,9 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 256);
-  hipLaunchKernelGGL(grouped_gemm_dma<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles * kUnit), dim3(256), 0,
-                     s, d);
+  const dim3 grid2(rounds * kXcds * d.n_tiles * kUnit);
+  if (I == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, true>), grid2, dim3(256), 0, s, d);
+  else hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, false>), grid2, dim3(256), 0, s, d);
   return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ Workspace workspace_layout(const moe_config& c, void* base);
 
 // Split-K factor of the bf16 router-logits GEMM: enough row blocks (kExpertBM rows) x
 // splits to fill the chip at small T, each split an even number (at least 8, unless K
-// is shorter) of 64-wide K stages;
+// is shorter; never 2 unless K is 128) of 64-wide K stages;
 // the fp32 partials are summed in order by the selection kernel.  1 for fp32
 // activations.
 inline int router_k_chunk(const moe_config& c) {
@@ -60,6 +60,7 @@ inline int router_k_chunk(const moe_config& c) {
   chunk = chunk < 8 ? 8 : chunk;                          // >= 8 stages: fixed costs amortised
   chunk = chunk > stages ? stages : chunk;
   chunk += chunk & 1;                                     // even stage count
+  while (stages % chunk == 2) chunk += 2;                 // no two-stage last split
   return chunk * 64;
 }
 inline int router_splits(const moe_config& c) {
