@@ -12,7 +12,7 @@ static size_t act_bytes(const moe_config& c) { return c.act_dtype == MOE_F32 ? 4
 
 Workspace workspace_layout(const moe_config& c, void* base) {
   const size_t T = c.num_tokens, E = c.num_experts, K = c.top_k, Ns = c.num_shared;
-  const size_t H = c.hidden, I = c.inter, G = E + Ns;
+  const size_t H = c.hidden, I = c.inter;
   const size_t TK = T * K, rows = TK + T * Ns;
   const size_t chunks = (T + kTokChunk - 1) / kTokChunk;
   const bool fp8 = c.w_dtype == MOE_E4M3;
@@ -30,8 +30,8 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   w.offsets = static_cast<int32_t*>(take((E + 1) * 4));
   w.row_token = static_cast<int32_t*>(take(TK * 4));
   w.pair_row = static_cast<int32_t*>(take(TK * 4));
-  w.tiles1 = static_cast<int32_t*>(take((G + 1) * 4));
-  w.order = static_cast<int32_t*>(take(size_t(expert_row_blocks_upper(c, kFp8BT)) * 4));
+  w.sched_n = static_cast<int32_t*>(take(4));
+  w.sched = static_cast<int4*>(take(size_t(expert_row_blocks_upper(c, kFp8BT)) * 16));
   w.h = take(rows * I * act_bytes(c));
   w.hq = fp8 ? static_cast<uint8_t*>(take(rows * I)) : nullptr;
   w.h_scales = fp8 ? static_cast<float*>(take(rows * (I / 128) * 4)) : nullptr;

@@ -29,14 +29,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x0, x1}, bf16x2_t));
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
 // fp32 -> OCP e4m3fn code: round to nearest even, saturate to +-448, keep the sign
 // of values that round to zero, NaN -> 0x7F.
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {

@@ -16,6 +16,7 @@
 // matching 128 up rows and every wave owns the same columns of both halves, so the
 // SwiGLU epilogue runs in registers; accumulation is fp32.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -94,67 +95,93 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   constexpr int NDA = BM / 32, NDB = BN / 32; // DMA instructions per wave per stage
   __shared__ __attribute__((aligned(1024))) uint4 lds[(2 * ASTAGE + 2 * BSTAGE) / 16];
 
-  // ---- tile decode ---------------------------------------------------------------
-  // Workgroups reach the XCDs round-robin (b % 8).  The units (see build_schedule),
+  // ---- tiles ---------------------------------------------------------------------
+  // Workgroups reach the XCDs round-robin (b % 8).  The row blocks (see build_schedule),
   // sorted largest first, are dealt to the XCDs in snake order (round r: XCDs 0..7,
-  // then 7..0), so every XCD gets an even share and runs its largest units first; a
-  // unit's workgroups are consecutive on one XCD, n-tile major: its blocks share each
-  // weight tile and every block's n-tiles share its A rows, through that XCD's L2.
-  const int b = blockIdx.x;
-  const int xcd = b % kXcds, slot = b / kXcds;
-  const int per_round = a.n_tiles * a.unit;
-  const int round = slot / per_round, rs = slot % per_round;
-  const int nt = rs / a.unit, u = rs % a.unit;
-  const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
-  int g = 0, r0 = 0, r1 = a.T, mt = pos;
-  if (a.tile_off) {
-    if (pos >= a.tile_off[a.G]) return;
-    const int id = a.order[pos];
-    int lo = 0, hi = a.G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.tile_off[mid] <= id) lo = mid; else hi = mid;
-    }
-    g = lo;
-    mt = (id - a.tile_off[g]) * a.unit + u;
-    group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
-  }                                     // else: one group of T rows (router logits)
-  if (mt * BM >= r1 - r0) return;                        // past the group's blocks
-  const int m0 = r0 + mt * BM;
-  const int mvalid = min(BM, r1 - m0);
-  const int n0 = nt * BN_OUT;
+  // then 7..0), so every XCD gets an even share and runs its largest blocks first; a
+  // block's n-tiles are consecutive slots of one XCD, so they share its A rows through
+  // that XCD's L2.  The expert GEMMs run persistent workgroups (one per CU; gridDim.x
+  // = 8 x nwg): workgroup j of an XCD takes slots j, j + nwg, j + 2 nwg, ... and loads
+  // the first stage of its next tile while it writes out the current one.  The router
+  // logits run one workgroup per tile.
+  constexpr bool PERSIST = MODE != kPlainF32;
   const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int xcd = blockIdx.x % kXcds;
+  const int nwg = PERSIST ? int(gridDim.x) / kXcds : 0;
+  int slot = blockIdx.x / kXcds;
+  const int nblocks = a.sched ? *a.sched_n : 0;
+  // place of slot s of this XCD: schedule position pos, n-tile nt; valid if it has a block
+  auto place_of = [&](int s, int& pos_, int& nt_) __attribute__((always_inline)) {
+    const int round = s / a.n_tiles;
+    nt_ = s - round * a.n_tiles;
+    pos_ = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+    return pos_ < nblocks;
+  };
+  // tile of slot s: group g, rows m0 .. m0 + mvalid - 1, n-tile nt
+  auto tile_of = [&](int s, int& g_, int& m0_, int& mvalid_, int& nt_) __attribute__((always_inline)) {
+    int pos;
+    if (a.sched) {
+      if (!place_of(s, pos, nt_)) return false;
+      const int4 e = a.sched[pos];
+      g_ = e.x;
+      m0_ = e.y;
+      mvalid_ = e.z;
+    } else {                                              // router: one group of T rows
+      const int round = s / a.n_tiles;
+      nt_ = s - round * a.n_tiles;
+      pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+      g_ = 0;
+      m0_ = pos * BM;
+      if (m0_ >= a.T) return false;
+      mvalid_ = min(BM, a.T - m0_);
+    }
+    return true;
+  };
+  int g = 0, m0 = 0, mvalid = 0, nt = 0;
+  if (!tile_of(slot, g, m0, mvalid, nt)) return;
+  int n0 = nt * BN_OUT;
   // split-K (router logits): this workgroup's K range, its own partial output slice
   const int kst0 = blockIdx.y * (a.k_chunk / BK);      // first stage
   const int K = a.k_chunk ? min(a.k_chunk, a.K - blockIdx.y * a.k_chunk) : a.K;
   const uint32_t row_bytes = uint32_t(a.K) * 2u;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
 
   // ---- this wave's share of every stage: A rows 80 w.., B rows 64 w.. ---------------
-  const uint32_t b_bytes = uint32_t(a.N) * row_bytes;
+  // B: the tile's first weight row (gated: of the gate and of the up half) is in the
+  // buffer base, so the lane offsets hold for every tile; rows >= N read zero
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A, uint32_t(a.a_rows) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_b =
-      make_rsrc((MODE == kGatedBf16 && w >= 2 ? a.B1 : a.B0) + size_t(g) * a.b_stride, b_bytes);
+  const uint16_t* const bsel = MODE == kGatedBf16 && w >= 2 ? a.B1 : a.B0;
+  auto rsrc_b_of = [&](int g_, int nt_) __attribute__((always_inline)) {
+    const int nb = nt_ * BN_OUT;
+    return make_rsrc(bsel + size_t(g_) * a.b_stride + size_t(nb) * a.K, uint32_t(a.N - nb) * row_bytes);
+  };
+  __amdgpu_buffer_rsrc_t rsrc_b = rsrc_b_of(g, nt);
   uint32_t voff_a[NDA], voff_b[NDB];
+  // A row offsets of a tile: routed rows (below TK) gather their token through
+  // row_token; a tile of shared-expert rows maps to consecutive tokens
+  auto set_voff_a = [&](int m0_, int mvalid_) __attribute__((always_inline)) {
+    const bool lookup = a.gather && m0_ < a.TK;
+    const int base = !a.gather ? m0_ : (lookup ? 0 : (m0_ - a.TK) % a.T);
 #pragma unroll
-  for (int j = 0; j < NDA; ++j) {
-    const int arow = (BM / 4) * w + 8 * j + (l >> 3);
-    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
-    uint32_t o = kOob;
-    if (arow < mvalid) {
-      const int r = m0 + arow;
-      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      o = uint32_t(src) * row_bytes + chunk;
+    for (int j = 0; j < NDA; ++j) {
+      const int arow = (BM / 4) * w + 8 * j + (l >> 3);
+      const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
+      uint32_t o = kOob;
+      if (arow < mvalid_) {
+        const int src = lookup ? a.row_token[m0_ + arow] : base + arow;
+        o = uint32_t(src) * row_bytes + chunk;
+      }
+      voff_a[j] = o;
     }
-    voff_a[j] = o;
-  }
+  };
+  set_voff_a(m0, mvalid);
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
     const int rw = 8 * j + (l >> 3);
     const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
-    // gated: B rows 0..127 are gate rows n0.., 128..255 up rows n0..; plain: n0 + row
-    const int n = MODE == kGatedBf16 ? n0 + 64 * (w & 1) + rw : n0 + 64 * w + rw;
-    voff_b[j] = uint32_t(n) * row_bytes + chunk;      // rows >= N read zero
+    // gated: B rows 0..127 are gate rows, 128..255 the matching up rows
+    const int n = MODE == kGatedBf16 ? 64 * (w & 1) + rw : 64 * w + rw;
+    voff_b[j] = uint32_t(n) * row_bytes + chunk;
   }
   // LDS: B buffers at [0, 64K), A buffers at [64K, 144K); stage k uses buffer k & 1
   constexpr uint32_t kAOff = 2 * BSTAGE;
@@ -172,29 +199,35 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
 
   // ---- fragment geometry: per-step lane bases; buffer and block offsets are immediates
   const int wm = w >> 1, wn = w & 1;
-  const int ni_valid = min(4, max(0, (min(mvalid, BMAIN) - wm * WTM + 31) >> 5));
-  // rows 256..319 form two 32-row extra strips; every wave takes two 32-column blocks
-  // of each strip that has rows (nx strips), so the four waves stay balanced
-  const int nx = mvalid > BMAIN + 32 ? 2 : (mvalid > BMAIN ? 1 : 0);
+  // Set up again for every tile from a lane id the compiler cannot hoist: these values
+  // then die with the K loop instead of staying live (and spilling) through the
+  // epilogue of a persistent workgroup.
   uint32_t abase[4], bbase[4], xbase[4];
-  {
-    const int lane_row = l & 31;
+  auto set_frag_bases = [&]() __attribute__((always_inline)) {
+    int ll;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ll));
+    const int lane_row = ll & 31;
     const int b_row0 = (MODE == kGatedBf16 ? wn * (WTN / 2) : wn * WTN) + lane_row;
     const int a_row = wm * WTM + lane_row;
     const int x_row = BMAIN + lane_row;                 // strip 1: + 32 rows
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const uint32_t sl = uint32_t((2 * s4 + (l >> 5)) ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
+      const uint32_t sl = uint32_t((2 * s4 + (ll >> 5)) ^ (ll & 7) ^ ((ll >> 3) & 1)) * 16u;
       bbase[s4] = uint32_t(b_row0) * ROWB + sl;
       abase[s4] = kAOff + uint32_t(a_row) * ROWB + sl;
       xbase[s4] = kAOff + uint32_t(x_row) * ROWB + sl;
     }
-  }
+  };
   // B block j of the wave: rows b_row0 + offset (gated: gate blocks, then up blocks)
   auto b_blk = [](int j) constexpr {
     return MODE == kGatedBf16 ? (j < NJ / 2 ? j * 32 : BN / 2 + (j - NJ / 2) * 32) : j * 32;
   };
   const int nk = K / BK;
+  bool has_next = false;                     // next tile of this workgroup and its place
+  int pos2 = 0, g2 = 0, m02 = 0, mv2 = 0, nt2 = 0;
+  // the next tile's schedule entry, loaded at the start of a tile (a vector load: the
+  // scalar-cache wait would land in the stage barriers) and read in its epilogue
+  const __amdgpu_buffer_rsrc_t rsrc_sched = make_rsrc(a.sched, uint32_t(nblocks) * 16u);
 
   auto body = [&](auto niv_tag, auto x_tag, auto xw_tag) __attribute__((always_inline)) {
     constexpr int NIV = decltype(niv_tag)::value;
@@ -318,12 +351,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
 
-    // prologue: A 0, B 0, B 1 in flight; stage 0 published once only B 1 may be pending
-    static_for<0, NDA>([&](auto j) __attribute__((always_inline)) { dma_a(0, P0{}, j); });
-    static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(0, P0{}, j); });
-    static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(1, P1{}, j); });
-    wait_vmcnt<NDB>();
+    // A 0, B 0 and B 1 are in flight (issued before the tile loop for the first tile,
+    // during the previous tile's epilogue for the others)
+    wait_vmcnt<0>();
     stage_barrier();
+    i32x4_t next_e{};
+    if constexpr (PERSIST) {
+      if (has_next) next_e = __builtin_amdgcn_raw_buffer_load_b128(rsrc_sched, uint32_t(pos2) * 16u, 0, 0);
+    }
     // nk = K / 64 is even (K is a multiple of 128)
     auto two_stages = [&]() __attribute__((always_inline)) {
       stage(0, P0{}, F_{}, T_{}, F_{}, T_{}, V0{});
@@ -377,15 +412,27 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
         put_blk(accx[e], BMAIN + 32 * (e >> 1), n0 + wn * WTN + xb(e) * 32 + lr);
       });
     } else {
-      // bf16 outputs go through LDS: each wave writes its rows into its own 32 KB
-      // region (8-byte writes of four adjacent columns), then reads whole rows back 16
-      // bytes per lane and stores them with full-line 16-byte global stores.  A staging
-      // row of P bytes has P / 16 chunks; chunk c of row r sits in slot
-      // c ^ ((r / (256 / P)) % (P / 16)) and its 8-byte halves are swapped when bit 4 of
-      // r is set: the 32 lanes of a half-wave write 32 distinct bank pairs, and every
-      // 16-lane quarter of a read covers the 64 banks once.
-      stage_barrier();                          // every wave is done with the last stage
-      char* const stg = reinterpret_cast<char*>(lds) + w * 32768;
+      stage_barrier();                          // every wave is done with this tile's LDS
+      // the next tile's B 0 and B 1 now (their HBM latency hides behind the epilogue);
+      // its A 0 after the epilogue, which stages through A buffer 1
+      if constexpr (PERSIST) {
+        if (has_next) {
+          g2 = __builtin_amdgcn_readfirstlane(next_e[0]);
+          m02 = __builtin_amdgcn_readfirstlane(next_e[1]);
+          mv2 = __builtin_amdgcn_readfirstlane(next_e[2]);
+          rsrc_b = rsrc_b_of(g2, nt2);
+          static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(0, P0{}, j); });
+          static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(1, P1{}, j); });
+        }
+      }
+      // bf16 outputs go through LDS: each wave writes one 32-row block at a time into
+      // its own 10 KB of A buffer 1 (8-byte writes of four adjacent columns), then reads
+      // whole rows back 16 bytes per lane and stores them with full-line 16-byte global
+      // stores.  A staging row of P bytes has P / 16 chunks; chunk c of row r sits in
+      // slot c ^ ((r / (256 / P)) % (P / 16)) and its 8-byte halves are swapped when bit
+      // 4 of r is set: the 32 lanes of a half-wave write 32 distinct bank pairs, and
+      // every 16-lane quarter of a read covers the 64 banks once.
+      char* const stg = reinterpret_cast<char*>(lds) + kAOff + ASTAGE + w * 10240;
       uint16_t* const cout = static_cast<uint16_t*>(a.C);
       auto pack = [](float x0, float x1) __attribute__((always_inline)) { return pack_bf16x2(x0, x1); };
       // this lane's write slot base for pitch P: row lr, chunk 0, half lh
@@ -393,32 +440,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
         constexpr int P = decltype(p_tag)::value, CH = P / 16, RPB = 256 / P;
         return uint32_t(lr * P + (((lr / RPB) % CH) << 4) + ((lh ^ ((lr >> 4) & 1)) << 3));
       };
-      auto put8 = [&](uint32_t slot, int rb, int pitch, int c, uint32_t lo, uint32_t hi)
-          __attribute__((always_inline)) {
-        *reinterpret_cast<uint2*>(stg + rb * pitch + (slot ^ uint32_t(c << 4))) = make_uint2(lo, hi);
+      auto put8 = [&](uint32_t slot8, int c, uint32_t lo, uint32_t hi) __attribute__((always_inline)) {
+        *reinterpret_cast<uint2*>(stg + (slot8 ^ uint32_t(c << 4))) = make_uint2(lo, hi);
       };
-      // staged rows [sb, sb + NR) of pitch P (P / 2 columns) to output rows
-      // m0 + rb + (0 .. NR), columns from cb; rows past vrows are not stored
-      auto drain = [&](auto p_tag, auto nr_tag, int sb, int rb, int vrows, int cb)
-          __attribute__((always_inline)) {
+      // the 32 staged rows of pitch P (P / 2 columns) to output rows m0 + rb + (0 .. 31),
+      // columns from cb; rows past vrows are not stored
+      auto drain = [&](auto p_tag, int rb, int vrows, int cb) __attribute__((always_inline)) {
         constexpr int P = decltype(p_tag)::value, CH = P / 16, RPB = 256 / P, RPI = 64 / CH;
-        constexpr int NR = decltype(nr_tag)::value;
+        constexpr int NQ = 32 / RPI, QG = NQ < 4 ? NQ : 4;   // reads in flight per group
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int c = le % CH, col = cb + 8 * c;
-        constexpr int NQ = NR / RPI, QG = NQ < 4 ? NQ : 4;   // reads in flight per group
 #pragma unroll
         for (int q0 = 0; q0 < NQ; q0 += QG) {
           if (q0 * RPI >= vrows) break;
           uint4 v[QG];
 #pragma unroll
           for (int u = 0; u < QG; ++u) {
-            const int rs = sb + (q0 + u) * RPI + le / CH;
-            v[u] = *reinterpret_cast<const uint4*>(stg + rs * P + ((c ^ ((rs / RPB) % CH)) << 4));
+            const int r = (q0 + u) * RPI + le / CH;
+            v[u] = *reinterpret_cast<const uint4*>(stg + r * P + ((c ^ ((r / RPB) % CH)) << 4));
           }
 #pragma unroll
           for (int u = 0; u < QG; ++u) {
-            const int r = (q0 + u) * RPI + le / CH, rs = sb + r;
-            if ((rs >> 4) & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
+            const int r = (q0 + u) * RPI + le / CH;
+            if ((r >> 4) & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
             if (r < vrows && col < a.N)
               *reinterpret_cast<uint4*>(cout + size_t(m0 + rb + r) * a.ldc + col) = v[u];
           }
@@ -426,112 +470,128 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       };
-      const int wrows = min(mvalid - wm * WTM, WTM);      // this wave's valid main rows
+      const int wrows = mvalid - wm * WTM;                  // this wave's valid main rows
+      // the strips go first: their VGPR accumulators are free before the next tile's A
+      // offsets are computed
+      if constexpr (MODE == kGatedBf16) {
+        // strips: 32 columns per wave and strip (gate accx[2 st], up accx[2 st + 1])
+        using PX = std::integral_constant<int, 64>;
+        const uint32_t sx = wslot(PX{});
+        static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+          constexpr int st = decltype(st_tag)::value;
+          constexpr int xh = st == 0 ? XW : 1 - XW;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float hv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              hv[t] = silu_fast(accx[2 * st][4 * g4 + t]) * accx[2 * st + 1][4 * g4 + t];
+            put8(sx, g4, pack(hv[0], hv[1]), pack(hv[2], hv[3]));
+          }
+          drain(PX{}, BMAIN + 32 * st, mvalid - BMAIN - 32 * st, n0 + wn * (WTN / 2) + xh * 32);
+        });
+      } else {
+        // strips: 64 adjacent columns per wave and strip (blocks xb(2 st), xb(2 st) + 1)
+        using PX = std::integral_constant<int, 128>;
+        const uint32_t sx = wslot(PX{});
+        static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
+          constexpr int st = decltype(st_tag)::value;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              put8(sx, 4 * h + g4, pack(accx[2 * st + h][4 * g4], accx[2 * st + h][4 * g4 + 1]),
+                   pack(accx[2 * st + h][4 * g4 + 2], accx[2 * st + h][4 * g4 + 3]));
+          drain(PX{}, BMAIN + 32 * st, mvalid - BMAIN - 32 * st, n0 + wn * WTN + xb(2 * st) * 32);
+        });
+      }
       if constexpr (MODE == kGatedBf16) {
         // h = silu(gate) * up: 64 columns per wave (gate blocks 0, 1 with up blocks 2, 3)
         using PW = std::integral_constant<int, 128>;
         const uint32_t sl = wslot(PW{});
 #pragma unroll
-        for (int i = 0; i < NIV; ++i)
+        for (int i = 0; i < NIV; ++i) {
 #pragma unroll
           for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g4 = 0; g4 < 4; ++g4) {
               float hv[4];
 #pragma unroll
               for (int t = 0; t < 4; ++t)
-                hv[t] = silu_fast(acc[i][j][4 * g + t]) * acc[i][j + NJ / 2][4 * g + t];
-              put8(sl, i * 32, 128, 4 * j + g, pack(hv[0], hv[1]), pack(hv[2], hv[3]));
+                hv[t] = silu_fast(acc[i][j][4 * g4 + t]) * acc[i][j + NJ / 2][4 * g4 + t];
+              put8(sl, 4 * j + g4, pack(hv[0], hv[1]), pack(hv[2], hv[3]));
             }
-        if constexpr (NIV > 0)
-          drain(PW{}, std::integral_constant<int, NIV * 32>{}, 0, wm * WTM, wrows, n0 + wn * (WTN / 2));
-        if constexpr (NX > 0) {
-          // strips: 32 columns per wave and strip (gate accx[2 st], up accx[2 st + 1])
-          using PX = std::integral_constant<int, 64>;
-          const uint32_t sx = wslot(PX{});
-          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
-            constexpr int st = decltype(st_tag)::value;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float hv[4];
-#pragma unroll
-              for (int t = 0; t < 4; ++t)
-                hv[t] = silu_fast(accx[2 * st][4 * g + t]) * accx[2 * st + 1][4 * g + t];
-              put8(sx, st * 32, 64, g, pack(hv[0], hv[1]), pack(hv[2], hv[3]));
-            }
-          });
-          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
-            constexpr int st = decltype(st_tag)::value;
-            constexpr int xh = st == 0 ? XW : 1 - XW;
-            drain(PX{}, std::integral_constant<int, 32>{}, 32 * st, BMAIN + 32 * st,
-                  mvalid - BMAIN - 32 * st, n0 + wn * (WTN / 2) + xh * 32);
-          });
+          drain(PW{}, wm * WTM + i * 32, wrows - i * 32, n0 + wn * (WTN / 2));
         }
       } else {
         // 128 columns per wave
         using PW = std::integral_constant<int, 256>;
         const uint32_t sl = wslot(PW{});
 #pragma unroll
-        for (int i = 0; i < NIV; ++i)
+        for (int i = 0; i < NIV; ++i) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              put8(sl, i * 32, 256, 4 * j + g, pack(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                   pack(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
-        if constexpr (NIV > 0)
-          drain(PW{}, std::integral_constant<int, NIV * 32>{}, 0, wm * WTM, wrows, n0 + wn * WTN);
-        if constexpr (NX > 0) {
-          // strips: 64 adjacent columns per wave and strip (blocks xb(2 st), xb(2 st) + 1)
-          using PX = std::integral_constant<int, 128>;
-          const uint32_t sx = wslot(PX{});
-          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
-            constexpr int st = decltype(st_tag)::value;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int g = 0; g < 4; ++g)
-                put8(sx, st * 32, 128, 4 * h + g, pack(accx[2 * st + h][4 * g], accx[2 * st + h][4 * g + 1]),
-                     pack(accx[2 * st + h][4 * g + 2], accx[2 * st + h][4 * g + 3]));
-          });
-          static_for<0, NX>([&](auto st_tag) __attribute__((always_inline)) {
-            constexpr int st = decltype(st_tag)::value;
-            drain(PX{}, std::integral_constant<int, 32>{}, 32 * st, BMAIN + 32 * st,
-                  mvalid - BMAIN - 32 * st, n0 + wn * WTN + xb(2 * st) * 32);
-          });
+            for (int g4 = 0; g4 < 4; ++g4)
+              put8(sl, 4 * j + g4, pack(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
+                   pack(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
+          drain(PW{}, wm * WTM + i * 32, wrows - i * 32, n0 + wn * WTN);
         }
+      }
+      if constexpr (PERSIST) {
       }
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  if (ni_valid > 2) {
-    if (nx == 2) {
-      if (wm == 0) body(std::integral_constant<int, 4>{}, I2{}, I0{});
-      else body(std::integral_constant<int, 4>{}, I2{}, I1{});
-    } else if (nx == 1) {
-      if (wm == 0) body(std::integral_constant<int, 4>{}, I1{}, I0{});
-      else body(std::integral_constant<int, 4>{}, I1{}, I1{});
-    } else {
-      body(std::integral_constant<int, 4>{}, I0{}, I0{});
-    }
-  } else if (ni_valid > 1) body(std::integral_constant<int, 2>{}, I0{}, I0{});
-  else if (ni_valid > 0) body(std::integral_constant<int, 1>{}, I0{}, I0{});
-  else body(std::integral_constant<int, 0>{}, I0{}, I0{});
+  // the first tile's stage 0 and B 1
+  static_for<0, NDA>([&](auto j) __attribute__((always_inline)) { dma_a(0, I0{}, j); });
+  static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(0, I0{}, j); });
+  static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(1, I1{}, j); });
+  for (;;) {
+    set_frag_bases();
+    has_next = PERSIST && place_of(slot + nwg, pos2, nt2);
+    const int ni_valid = min(4, max(0, (min(mvalid, BMAIN) - wm * WTM + 31) >> 5));
+    // rows 256..319 form two 32-row extra strips; every wave takes two 32-column blocks
+    // of each strip that has rows (nx strips), so the four waves stay balanced
+    const int nx = mvalid > BMAIN + 32 ? 2 : (mvalid > BMAIN ? 1 : 0);
+    if (ni_valid > 2) {
+      if (nx == 2) {
+        if (wm == 0) body(std::integral_constant<int, 4>{}, I2{}, I0{});
+        else body(std::integral_constant<int, 4>{}, I2{}, I1{});
+      } else if (nx == 1) {
+        if (wm == 0) body(std::integral_constant<int, 4>{}, I1{}, I0{});
+        else body(std::integral_constant<int, 4>{}, I1{}, I1{});
+      } else {
+        body(std::integral_constant<int, 4>{}, I0{}, I0{});
+      }
+    } else if (ni_valid > 1) body(std::integral_constant<int, 2>{}, I0{}, I0{});
+    else if (ni_valid > 0) body(std::integral_constant<int, 1>{}, I0{}, I0{});
+    else body(std::integral_constant<int, 0>{}, I0{}, I0{});
+    if (!has_next) break;
+    // the next tile's A 0 (its B 0 and B 1 went out during the epilogue).  Computing
+    // these offsets inside the epilogue makes the register allocator spill.
+    set_voff_a(m02, mv2);
+    static_for<0, NDA>([&](auto j) __attribute__((always_inline)) { dma_a(0, I0{}, j); });
+    slot += nwg;
+    g = g2;
+    m0 = m02;
+    mvalid = mv2;
+    nt = nt2;
+    n0 = nt * BN_OUT;
+  }
 }
 
 // Schedule of the expert GEMMs, one workgroup (G <= 512).  A group's rows split into
-// blocks of bm rows; up to U consecutive blocks of one group form a unit, whose
-// workgroups run side by side (n-tile major, block minor) so the blocks share every
-// weight tile through L2.  Output: the unit prefix over groups and every unit's index
-// ordered by row count, largest first (a counting sort over 32-row classes; the order
-// inside a class is arbitrary and changes no result: each block computes the same
-// values wherever it runs).
+// blocks of bm rows; the output lists every block as {group, first row, rows}, ordered
+// by row count, largest first (a counting sort over 32-row classes; the order inside a
+// class is arbitrary and changes no result: each block computes the same values
+// wherever it runs), and the number of blocks.
 __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict__ offsets, int E,
-                                                      int Ns, int T, int TK, int bm, int U,
-                                                      int32_t* __restrict__ unit_off,
-                                                      int32_t* __restrict__ order) {
+                                                      int Ns, int T, int TK, int bm,
+                                                      int4* __restrict__ sched,
+                                                      int32_t* __restrict__ sched_n) {
   constexpr int kClasses = 64;
   __shared__ int pre[512];
   __shared__ int cls_count[kClasses], cls_next[kClasses];
@@ -540,7 +600,7 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
   if (t < G) {
     int r0, r1;
     group_rows(offsets, t, E, T, TK, r0, r1);
-    c = ceil_div(ceil_div(r1 - r0, bm), U);
+    c = ceil_div(r1 - r0, bm);
   }
   pre[t] = c;
   if (t < kClasses) cls_count[t] = 0;
@@ -551,12 +611,10 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     pre[t] += v;
     __syncthreads();
   }
-  if (t < G) unit_off[t] = pre[t] - c;
-  if (t == G - 1) unit_off[G] = pre[t];
   const int total = pre[G - 1];
-  const int span = U * bm;                                // rows of a full unit
-  // class of a unit: (span - rows) / 32; its group is the first g with pre[g] > id
-  auto cls_of = [&](int id) {
+  if (t == 0) *sched_n = total;
+  // block id -> {group, first row, rows}; its group is the first g with pre[g] > id
+  auto block_of = [&](int id) {
     int lo = -1, hi = G - 1;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -566,10 +624,11 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     const int first = g > 0 ? pre[g - 1] : 0;
     int r0, r1;
     group_rows(offsets, g, E, T, TK, r0, r1);
-    const int rows = min(span, r1 - r0 - (id - first) * span);
-    return min(kClasses - 1, (span - rows) >> 5);
+    const int m0 = r0 + (id - first) * bm;
+    return make_int4(g, m0, min(bm, r1 - m0), 0);
   };
-  for (int id = t; id < total; id += 512) atomicAdd(&cls_count[cls_of(id)], 1);
+  auto cls_of = [&](const int4& blk) { return min(kClasses - 1, (bm - blk.z) >> 5); };
+  for (int id = t; id < total; id += 512) atomicAdd(&cls_count[cls_of(block_of(id))], 1);
   __syncthreads();
   if (t == 0) {
     int acc = 0;
@@ -579,7 +638,10 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  for (int id = t; id < total; id += 512) order[atomicAdd(&cls_next[cls_of(id)], 1)] = id;
+  for (int id = t; id < total; id += 512) {
+    const int4 blk = block_of(id);
+    sched[atomicAdd(&cls_next[cls_of(blk)], 1)] = blk;
+  }
 }
 
 // ---- fp32 path (small fp32 workloads): one thread per output element ---------
@@ -648,8 +710,6 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   a.N = c.num_experts;
   a.K = c.hidden;
   a.T = c.num_tokens;
-  a.G = 1;
-  a.unit = 1;
   a.n_tiles = ceil_div(c.num_experts, 256);
   a.a_rows = c.num_tokens;
   a.k_chunk = router_k_chunk(c);
@@ -661,19 +721,34 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   return hipGetLastError();
 }
 
-hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int unit,
-                                 int32_t* unit_off, int32_t* order, hipStream_t s) {
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int4* sched,
+                                 int32_t* sched_n, hipStream_t s) {
   const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
   hipLaunchKernelGGL(build_schedule, dim3(1), dim3(512), 0, s, offsets, E, Ns, T, T * c.top_k, bm,
-                     unit, unit_off, order);
+                     sched, sched_n);
   return hipGetLastError();
+}
+
+// Workgroups resident at once (one per CU: the expert GEMMs take 144 KB of LDS), a
+// multiple of the XCD count.
+static int resident_workgroups() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  n = n / kXcds * kXcds;
+  if (n < kXcds) n = kXcds;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
 }
 
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
                               const int32_t* row_token, const moe_expert_weights& w,
                               void* y_rows, const Workspace& ws, hipStream_t s) {
   const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
-  const int TK = T * c.top_k, G = E + Ns, rows = TK + T * Ns;
+  const int TK = T * c.top_k, rows = TK + T * Ns;
   const int H = c.hidden, I = c.inter;
   if (c.w_dtype == MOE_F32) {
     hipLaunchKernelGGL(gemm1_f32, dim3(ceil_div(rows * I, 256)), dim3(256), 0, s,
@@ -688,19 +763,20 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   }
   if (c.w_dtype == MOE_E4M3)
     return launch_grouped_ffn_fp8(c, x, offsets, row_token, w, y_rows, ws, s);
-  // one block per unit: 320-row blocks already hold an expert's rows at the prefill shape
-  constexpr int kUnit = 1;
-  hipError_t err = launch_build_schedule(c, offsets, kExpertBM, kUnit, ws.tiles1, ws.order, s);
+  hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
-  // grid: every XCD gets ceil(units / 8) rounds of n_tiles x unit workgroups
-  const int rounds = ceil_div(expert_units_upper(c, kExpertBM, kUnit), kXcds);
+  // persistent workgroups: 8 x nwg, nwg per XCD, each XCD holding up to rounds x n_tiles
+  // slots (rounds = the XCD's share of the row blocks)
+  const int rounds = ceil_div(expert_row_blocks_upper(c, kExpertBM), kXcds);
+  auto persistent_grid = [&](int n_tiles) {
+    const int nwg = std::min(resident_workgroups() / kXcds, rounds * n_tiles);
+    return dim3(unsigned(nwg * kXcds));
+  };
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
   a.row_token = row_token;
-  a.offsets = offsets;
-  a.tile_off = ws.tiles1;
-  a.order = ws.order;
-  a.unit = kUnit;
+  a.sched = ws.sched;
+  a.sched_n = ws.sched_n;
   a.B0 = static_cast<const uint16_t*>(w.w_gate);
   a.B1 = static_cast<const uint16_t*>(w.w_up);
   a.b_stride = 1LL * I * H;
@@ -708,14 +784,12 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   a.ldc = I;
   a.N = I;
   a.K = H;
-  a.E = E;
   a.T = T;
   a.TK = TK;
-  a.G = G;
   a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  const dim3 grid1(rounds * kXcds * a.n_tiles * kUnit);
+  const dim3 grid1 = persistent_grid(a.n_tiles);
   if (H == 128) hipLaunchKernelGGL((grouped_gemm_dma<kGatedBf16, true>), grid1, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((grouped_gemm_dma<kGatedBf16, false>), grid1, dim3(256), 0, s, a);
   GemmArgs d = a;
@@ -731,7 +805,7 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 256);
-  const dim3 grid2(rounds * kXcds * d.n_tiles * kUnit);
+  const dim3 grid2 = persistent_grid(d.n_tiles);
   if (I == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, true>), grid2, dim3(256), 0, s, d);
   else hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, false>), grid2, dim3(256), 0, s, d);
   return hipGetLastError();

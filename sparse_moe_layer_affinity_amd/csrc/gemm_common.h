@@ -10,16 +10,15 @@ namespace moe {
 struct GemmArgs {
   const uint16_t* A;         // bf16 activations: x [T, K] (gather) or [rows, K]
   const int32_t* row_token;  // gather map of routed rows (gather only)
-  const int32_t* offsets;    // [E+1] expert offsets (nullptr: single group of T rows)
-  const int32_t* tile_off;   // [G+1] m-tile (expert GEMMs: unit) prefix per group
-  const int32_t* order;      // units in schedule order (expert GEMMs)
-  int unit;                  // row blocks per unit (expert GEMMs)
+  const int4* sched;         // row blocks {group, first row, rows}, largest first
+                             // (expert GEMMs; nullptr: one group of T rows)
+  const int32_t* sched_n;    // number of row blocks
   const uint16_t* B0;        // weights [G][N][K] bf16 (GEMM1: gate)
   const uint16_t* B1;        // GEMM1: up
   long long b_stride;        // elements per expert
   void* C;                   // output [rows, ldc]
   int ldc, N, K;             // N = output columns (GEMM1: intermediate columns)
-  int E, T, TK, G;           // routed experts, tokens, T*K, groups (E + Ns)
+  int T, TK;                 // tokens, T*K (gather: rows below TK are routed)
   int n_tiles;
   int gather;
   int a_rows;                // rows of A (bounds of the activation buffer)

@@ -34,10 +34,8 @@ struct Fp8Args {
   const uint8_t* A;          // e4m3 activations: xq [T, K] (gather) or hq [rows, K]
   const float* a_scales;     // [K/128, a_rows] (transposed)
   const int32_t* row_token;  // gather map of routed rows (gather only)
-  const int32_t* offsets;    // [E+1]
-  const int32_t* tile_off;   // [G+1] unit prefix per group
-  const int32_t* order;      // units in schedule order
-  int unit;                  // row blocks per unit
+  const int4* sched;         // row blocks {group, first row, rows}, largest first
+  const int32_t* sched_n;    // number of row blocks
   const uint8_t* B0;         // e4m3 weights [G][N][K] (GEMM1: gate)
   const uint8_t* B1;         // GEMM1: up
   const float* S0;           // weight block scales [G][N/128][K/128] (GEMM1: gate)
@@ -46,7 +44,7 @@ struct Fp8Args {
   long long s_stride;        // floats per expert
   uint16_t* C;               // bf16 output [rows, ldc]
   int ldc, N, K;
-  int E, T, TK, G;
+  int T, TK;
   int n_tiles;
   int gather;
   int a_rows;
@@ -66,27 +64,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   constexpr int BN_OUT = MODE == kGatedBf16 ? BW / 2 : BW;
   __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2048) / 16];
 
-  // ---- tile decode: snake-dealt units (see the bf16 expert GEMM) -----------------
+  // ---- tile decode: row blocks dealt to the XCDs in snake order, a block's n-tiles
+  // consecutive on one XCD (see the bf16 expert GEMM) ------------------------------
   const int b = blockIdx.x;
   const int xcd = b % kXcds, slot = b / kXcds;
-  const int per_round = a.n_tiles * a.unit;
-  const int round = slot / per_round, rs = slot % per_round;
-  const int nt = rs / a.unit, u = rs % a.unit;
+  const int round = slot / a.n_tiles, nt = slot % a.n_tiles;
   const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
-  if (pos >= a.tile_off[a.G]) return;
-  const int id = a.order[pos];
-  int lo = 0, hi = a.G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] <= id) lo = mid; else hi = mid;
-  }
-  const int g = lo;
-  const int mt = (id - a.tile_off[g]) * a.unit + u;
-  int r0, r1;
-  group_rows(a.offsets, g, a.E, a.T, a.TK, r0, r1);
-  if (mt * BT >= r1 - r0) return;                        // unit with fewer blocks
-  const int m0 = r0 + mt * BT;
-  const int mvalid = min(BT, r1 - m0);
+  if (pos >= *a.sched_n) return;
+  const int4 blk = a.sched[pos];
+  const int g = blk.x, m0 = blk.y, mvalid = blk.z;
   const int n0 = nt * BN_OUT;
   const int tid = threadIdx.x;
   const int K = a.K, KBLK = a.K / 128;
@@ -273,20 +259,18 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
         for (int ib = 0; ib < 4; ++ib) {
           const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
           if (col >= a.N) continue;
-          uint32_t hh[4];
+          float hv[4];
   #pragma unroll
-          for (int q = 0; q < 4; ++q) hh[q] = f32_to_bf16_bits(silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q]);
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+          for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q];
+          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
       } else {
   #pragma unroll
         for (int ib = 0; ib < 8; ++ib) {
           const int col = n0 + wn * 128 + ib * 16 + 4 * (l >> 4);
           if (col >= a.N) continue;
-          uint32_t hh[4];
-  #pragma unroll
-          for (int q = 0; q < 4; ++q) hh[q] = f32_to_bf16_bits(acc[ib][jb][q]);
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+          const f32x4_t& v = acc[ib][jb];
+          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
     }
@@ -298,31 +282,26 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   else body(std::integral_constant<int, 0>{});
 }
 
-hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int unit,
-                                 int32_t* unit_off, int32_t* order, hipStream_t s);
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int4* sched,
+                                 int32_t* sched_n, hipStream_t s);
 
 hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int32_t* offsets,
                                   const int32_t* row_token, const moe_expert_weights& w,
                                   void* y_rows, const Workspace& ws, hipStream_t s) {
-  const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;
-  const int TK = T * c.top_k, G = E + Ns, rows = TK + T * Ns;
+  const int T = c.num_tokens, Ns = c.num_shared;
+  const int TK = T * c.top_k, rows = TK + T * Ns;
   const int H = c.hidden, I = c.inter;
   hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s, true);
   if (err != hipSuccess) return err;
-  // one block per unit: two blocks of one expert side by side on one XCD (sharing each
-  // weight tile through L2) measured 47% slower than dealing the blocks separately
-  constexpr int kUnit = 1;
-  err = launch_build_schedule(c, offsets, kFp8BT, kUnit, ws.tiles1, ws.order, s);
+  err = launch_build_schedule(c, offsets, kFp8BT, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
-  const int rounds = ceil_div(expert_units_upper(c, kFp8BT, kUnit), kXcds);
+  const int rounds = ceil_div(expert_row_blocks_upper(c, kFp8BT), kXcds);
   Fp8Args a{};
   a.A = ws.xq;
   a.a_scales = ws.x_scales;
   a.row_token = row_token;
-  a.offsets = offsets;
-  a.tile_off = ws.tiles1;
-  a.order = ws.order;
-  a.unit = kUnit;
+  a.sched = ws.sched;
+  a.sched_n = ws.sched_n;
   a.B0 = static_cast<const uint8_t*>(w.w_gate);
   a.B1 = static_cast<const uint8_t*>(w.w_up);
   a.S0 = w.s_gate;
@@ -333,14 +312,12 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.ldc = I;
   a.N = I;
   a.K = H;
-  a.E = E;
   a.T = T;
   a.TK = TK;
-  a.G = G;
   a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles * kUnit), dim3(512),
+  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512),
                      0, s, a);
   err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true);
   if (err != hipSuccess) return err;
@@ -361,7 +338,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 256);
-  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles * kUnit), dim3(512),
+  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512),
                      0, s, d);
   return hipGetLastError();
 }

@@ -13,8 +13,8 @@ struct Workspace {
   int32_t* offsets;    // [E+1] expert offsets (layer forward)
   int32_t* row_token;  // [T*K]
   int32_t* pair_row;   // [T*K]
-  int32_t* tiles1;     // [E+Ns+1] unit prefix per group of the expert GEMMs
-  int32_t* order;      // [row-block bound] the units, largest first
+  int32_t* sched_n;    // [1] row blocks of the expert GEMMs
+  int4* sched;         // [row-block bound] {group, first row, rows}, largest first
   void* h;             // [rows, inter] act dtype (SwiGLU output of the first GEMM)
   uint8_t* hq;         // [rows, inter] e4m3 codes of h (e4m3 weights)
   float* h_scales;     // [inter/128, rows] (e4m3 weights; transposed)
@@ -36,14 +36,6 @@ inline int expert_row_blocks_upper(const moe_config& c, int bm) {
   routed = routed < TK ? routed : TK;
   return int(routed + 1LL * c.num_shared * ((c.num_tokens + bm - 1) / bm));
 }
-// Upper bound on the units of up to `unit` consecutive blocks of one group.
-inline int expert_units_upper(const moe_config& c, int bm, int unit) {
-  const long long blocks = expert_row_blocks_upper(c, bm);
-  const long long groups = 1LL * c.num_experts + c.num_shared;
-  long long u = (blocks + groups * (unit - 1)) / unit;
-  return int(u < blocks ? u : blocks);
-}
-
 Workspace workspace_layout(const moe_config& c, void* base);
 
 // Split-K factor of the bf16 router-logits GEMM: enough row blocks (kExpertBM rows) x

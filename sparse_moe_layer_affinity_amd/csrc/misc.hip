@@ -35,12 +35,9 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__
       const int r = pair_row[size_t(t) * K + k];
       if (r >= 0) add(y_rows + size_t(r) * H, gate[size_t(t) * K + k], true);
     }
-    uint4 o;
-    o.x = f32_to_bf16_bits(acc[0]) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
-    o.y = f32_to_bf16_bits(acc[2]) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
-    o.z = f32_to_bf16_bits(acc[4]) | (uint32_t(f32_to_bf16_bits(acc[5])) << 16);
-    o.w = f32_to_bf16_bits(acc[6]) | (uint32_t(f32_to_bf16_bits(acc[7])) << 16);
-    *reinterpret_cast<uint4*>(y + size_t(t) * H + size_t(v) * 8) = o;
+    *reinterpret_cast<uint4*>(y + size_t(t) * H + size_t(v) * 8) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }
 }
 
