@@ -16,16 +16,17 @@
 // VGPRs (the VALU adds into them), and this file is compiled with MFMA results in
 // VGPRs as well, so no copies out of AGPRs.
 //
-// Tile: 256 weight rows (GEMM1: 128 gate rows over the matching 128 up rows) x 256
-// tokens, 8 waves (two per SIMD: one wave's rescale FMAs run while the other's
-// MFMAs hold the matrix core), each 128 weight rows x 64 tokens = 8 x 4 MFMA blocks.
-// K advances one 128-byte scale block per stage.  Operands and scales go global ->
-// LDS with buffer loads in LDS mode.  Weights (streamed from HBM) cycle through three
-// 32 KB stage buffers, so weight stage k+2 is in flight while stage k is multiplied.
-// Tokens (mostly L2 hits) use one 32 KB buffer: every wave reads all its token
-// fragments of a stage into registers first, and once a barrier confirms that, the
-// next stage's tokens and scales are loaded in its place.  Row blocks come from the
-// same largest-first XCD schedule as the bf16 kernel, 256 tokens each.
+// Tile: 128 weight rows (GEMM1: 64 gate rows over the matching 64 up rows) x 320 tokens
+// (an expert's whole row block, as in the bf16 kernel, so its weights stream from HBM
+// once), 8 waves (two per SIMD: one wave's rescale FMAs run while the other's MFMAs hold
+// the matrix core), each 64 weight rows x 80 tokens = 4 x 5 MFMA blocks.  K advances one
+// 128-byte scale block per stage.  Operands and scales go global -> LDS with buffer
+// loads in LDS mode.  Weights (streamed from HBM) cycle through three 16 KB stage
+// buffers; tokens (mostly L2 hits) and scales through two: every wave reads all its
+// token fragments and scales of a stage into registers first, and once a barrier
+// confirms that, stage k+2's tokens, scales and weights are loaded, so both streams have
+// two stages of lead.  Row blocks come from the same largest-first XCD schedule as the
+// bf16 kernel.
 #include "gemm_common.h"
 
 namespace moe {
@@ -52,17 +53,20 @@ struct Fp8Args {
 
 template <int MODE>
 __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
-  constexpr int BW = 256, BT = kFp8BT, ROWB = 128;
-  constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 32 KB each
+  constexpr int BW = 128, BT = kFp8BT, ROWB = 128;
+  constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 16 KB, 40 KB
   constexpr int SW = 3;                                   // weight stage buffers
-  // LDS: the token buffer first (its fragment reads then take immediate offsets, which
-  // stop at 64 KB), the weight ring, the two scale rings
-  constexpr uint32_t kTOff = 0;                           // token buffer
-  constexpr uint32_t kWOff = TSTAGE;                      // weight ring
-  constexpr uint32_t kSaOff = kWOff + SW * WSTAGE;        // token scales, 2 x 1 KB
-  constexpr uint32_t kSwOff = kSaOff + 2048;              // weight scales, 2 x 1 KB
+  constexpr int NTB = BT / 64;                            // 16-token blocks per wave: 5
+  // LDS: the two token buffers, the weight ring, the two token-scale and the two
+  // weight-scale buffers (waves 5..7 write 256 bytes each, wave 7's are a dummy)
+  constexpr uint32_t kTOff = 0;
+  constexpr uint32_t kWOff = 2 * TSTAGE;
+  constexpr uint32_t kSaOff = kWOff + SW * WSTAGE;
+  constexpr uint32_t kSaStage = 4 * BT;                   // 1280 B
+  constexpr uint32_t kSwOff = kSaOff + 2 * kSaStage;
+  constexpr uint32_t kSwStage = 768;
   constexpr int BN_OUT = MODE == kGatedBf16 ? BW / 2 : BW;
-  __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2048) / 16];
+  __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2 * kSwStage) / 16];
 
   // ---- tile decode: row blocks dealt to the XCDs in snake order, a block's n-tiles
   // consecutive on one XCD (see the bf16 expert GEMM) ------------------------------
@@ -78,101 +82,94 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   const int K = a.K, KBLK = a.K / 128;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
 
-  // ---- this wave's share of every stage: weight rows and token rows 32 w .. 32 w + 31
-  const uint32_t b_bytes = uint32_t(a.N) * uint32_t(K);
+  // ---- this wave's share of every stage: weight rows 16 w .., token rows 40 w .. ----
+  // A tile row lies in the tile's base for every load of this wave, so the lane offsets
+  // are per-wave constants.  Gated: stage rows 0..63 are gate rows n0.., 64..127 the
+  // matching up rows.
+  const bool up = MODE == kGatedBf16 && w >= 4;
+  const int wrow0 = MODE == kGatedBf16 ? n0 + 16 * (w & 3) : n0 + 16 * w;
   const __amdgpu_buffer_rsrc_t rsrc_w =
-      make_rsrc((MODE == kGatedBf16 && w >= 4 ? a.B1 : a.B0) + size_t(g) * a.b_stride, b_bytes);
+      make_rsrc((up ? a.B1 : a.B0) + size_t(g) * a.b_stride, uint32_t(a.N) * uint32_t(K));
   const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(a.A, uint32_t(a.a_rows) * uint32_t(K));
-  uint32_t voff_w[4], voff_t[4];
+  uint32_t voff_w[2], voff_t[NTB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rw = 8 * j + (l >> 3);
-    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
-    // gated: stage rows 0..127 gate rows n0.., 128..255 up rows n0..
-    const int n = MODE == kGatedBf16 ? n0 + 32 * (w & 3) + rw : n0 + 32 * w + rw;
-    voff_w[j] = uint32_t(n) * uint32_t(K) + chunk;         // rows >= N read zero
-    const int trow = 32 * w + rw;
-    uint32_t o = kOob;
-    if (trow < mvalid) {
-      const int r = m0 + trow;
-      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      o = uint32_t(src) * uint32_t(K) + chunk;
-    }
-    voff_t[j] = o;
+  for (int j = 0; j < 2; ++j) {
+    // stage row 16 w + 8 j + (l >> 3): bit 3 of the row is j
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ j) * 16u;
+    voff_w[j] = uint32_t(wrow0 + 8 * j + (l >> 3)) * uint32_t(K) + chunk;   // rows >= N read zero
   }
-  // one scale load per wave per stage: waves 0..3 the token scales of tokens
-  // 64 w + lane, waves 4 and 5 one weight block scale each (lane 0), waves 6 and 7
-  // nothing useful (every lane out of range; they keep the load counts uniform)
+  // shared-expert tiles map rows to consecutive tokens; routed rows gather
+  const bool lookup = a.gather && m0 < a.TK;
+  const int tbase = !a.gather ? m0 : (lookup ? 0 : (m0 - a.TK) % a.T);
+  auto src_of = [&](int row) { return lookup ? a.row_token[m0 + row] : tbase + row; };
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    // stage row 40 w + 8 j + (l >> 3): bit 3 of the row is (5 w + j) & 1
+    const int trow = 40 * w + 8 * j + (l >> 3);
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ ((5 * w + j) & 1)) * 16u;
+    voff_t[j] = trow < mvalid ? uint32_t(src_of(trow)) * uint32_t(K) + chunk : kOob;
+  }
+  // one scale load per wave per stage: waves 0..4 the token scales of tokens
+  // 64 w + lane, waves 5 and 6 one weight block scale each (lane 0; gated: gate and up,
+  // plain: the tile's block and nothing), wave 7 nothing useful (every lane out of range;
+  // the load counts stay uniform)
   __amdgpu_buffer_rsrc_t rsrc_s;
   uint32_t voff_s = kOob;
-  if (w < 4) {
+  if (w < 5) {
     rsrc_s = make_rsrc(a.a_scales, uint32_t(a.a_rows) * KBLK * 4u);
     const int row = 64 * w + l;
-    if (row < mvalid) {
-      const int r = m0 + row;
-      const int src = a.gather ? row_token_of(a.row_token, r, a.T, a.TK) : r;
-      voff_s = uint32_t(src) * 4u;
-    }
+    if (row < mvalid) voff_s = uint32_t(src_of(row)) * 4u;
   } else {
-    // gated: wave 4 the gate block, wave 5 the up block (same block index); plain:
-    // waves 4 and 5 the tile's two 128-row blocks (clamped in range: a block past N
-    // only feeds outputs that are never stored)
-    const bool up = MODE == kGatedBf16 && w == 5;
-    const int blk = min(MODE == kGatedBf16 ? n0 / 128 : n0 / 128 + (w - 4), ceil_div(a.N, 128) - 1);
-    rsrc_s = make_rsrc((up ? a.S1 : a.S0) + size_t(g) * a.s_stride, uint32_t(a.s_stride) * 4u);
-    if (w < 6 && l == 0) voff_s = uint32_t(blk * KBLK) * 4u;
+    const bool sup = MODE == kGatedBf16 && w == 6;
+    rsrc_s = make_rsrc((sup ? a.S1 : a.S0) + size_t(g) * a.s_stride, uint32_t(a.s_stride) * 4u);
+    if (l == 0 && (w == 5 || sup)) voff_s = uint32_t((n0 / 128) * KBLK) * 4u;
   }
   // K block ks of the scales: token scales [K/128, a_rows], weight scales [.., K/128]
-  const uint32_t s_step = w < 4 ? uint32_t(a.a_rows) * 4u : 4u;
+  const uint32_t s_step = w < 5 ? uint32_t(a.a_rows) * 4u : 4u;
   const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
   const uint32_t wave_w = lds_base + kWOff + uint32_t(w) * (WSTAGE / 8);
   const uint32_t wave_t = lds_base + kTOff + uint32_t(w) * (TSTAGE / 8);
-  const uint32_t wave_s = lds_base + (w < 4 ? kSaOff + 256u * w : kSwOff + 256u * (w - 4));
+  const uint32_t wave_s = lds_base + (w < 5 ? kSaOff + 256u * w : kSwOff + 256u * (w - 5));
+  const uint32_t s_par = w < 5 ? kSaStage : kSwStage;
 
   auto load_w = [&](int ks) __attribute__((always_inline)) {
     const uint32_t dst = wave_w + uint32_t(ks % SW) * WSTAGE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // gated: every weight row of the tile is below N (n-tiles of 128 rows, N a
-      // multiple of 128), so rows 16 apart differ by a uniform offset that rides in
-      // the scalar operand and two lane offsets serve all four loads
-      if constexpr (MODE == kGatedBf16)
-        dma16(rsrc_w, voff_w[j & 1], uint32_t(ks) * ROWB + uint32_t(j >> 1) * 16u * uint32_t(K),
-              dst + j * 1024u);
-      else
-        dma16(rsrc_w, voff_w[j], uint32_t(ks) * ROWB, dst + j * 1024u);
-    }
+    dma16(rsrc_w, voff_w[0], uint32_t(ks) * ROWB, dst);
+    dma16(rsrc_w, voff_w[1], uint32_t(ks) * ROWB, dst + 1024u);
   };
-  // token rows of stage ks, then its scales (5 loads)
+  // token rows of stage ks and its scales, into buffer ks & 1 (NTB + 1 loads)
   auto load_t = [&](int ks) __attribute__((always_inline)) {
+    const uint32_t par = uint32_t(ks & 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + j * 1024u);
-    dma4(rsrc_s, voff_s, uint32_t(ks) * s_step, wave_s + uint32_t(ks & 1) * 1024u);
+    for (int j = 0; j < NTB; ++j)
+      dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + par * TSTAGE + j * 1024u);
+    dma4(rsrc_s, voff_s, uint32_t(ks) * s_step, __builtin_amdgcn_readfirstlane(wave_s + par * s_par));
   };
 
   // ---- wave geometry: 2 (weight rows) x 4 (tokens) --------------------------------
   const int wn = w & 1, wt = w >> 1;
-  // LDS row of this lane in weight block ib / token block jb, and its two K chunks
-  int w_row[8];
+  // LDS row of this lane in weight block ib (gated: gate blocks 0, 1, up blocks 2, 3)
+  // and token block jb, and its two K chunks
+  int w_row[4];
 #pragma unroll
-  for (int ib = 0; ib < 8; ++ib) {
+  for (int ib = 0; ib < 4; ++ib) {
     int r;
-    if (MODE == kGatedBf16) r = ib < 4 ? wn * 64 + ib * 16 : 128 + wn * 64 + (ib - 4) * 16;
-    else r = wn * 128 + ib * 16;
+    if (MODE == kGatedBf16) r = ib < 2 ? wn * 32 + ib * 16 : 64 + wn * 32 + (ib - 2) * 16;
+    else r = wn * 64 + ib * 16;
     w_row[ib] = r + (l & 15);
   }
-  const int t_row = wt * 64 + (l & 15);                   // + 16 jb
+  const int t_row = wt * 80 + (l & 15);                   // + 16 jb
   const int c0 = 2 * (l >> 4);
   const uint32_t sl0 = uint32_t(c0 ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
   const uint32_t sl1 = uint32_t((c0 + 1) ^ (l & 7) ^ ((l >> 3) & 1)) * 16u;
 
   // token blocks of this wave that hold rows: the MFMAs of empty ones are skipped
-  const int njb = min(4, max(0, (mvalid - wt * 64 + 15) >> 4));
+  const int njb = min(NTB, max(0, (mvalid - wt * 80 + 15) >> 4));
   auto body = [&](auto njb_tag) __attribute__((always_inline)) {
     constexpr int NJB = decltype(njb_tag)::value;
-    f32x4_t acc[8][NJB > 0 ? NJB : 1];
+    f32x4_t acc[4][NJB > 0 ? NJB : 1];
   #pragma unroll
-    for (int ib = 0; ib < 8; ++ib)
+    for (int ib = 0; ib < 4; ++ib)
   #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) acc[ib][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -187,62 +184,63 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
       return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lds) + byte);
     };
 
-    // prologue: tokens 0 (+ scales), weights 0 and 1; stage 0 published once only
-    // weight stage 1 (4 loads) may be pending.  K is a multiple of 128: nk >= 1.
+    // prologue: tokens (+ scales) and weights of stages 0 and 1.  K is a multiple of
+    // 128: nk >= 1.
     const int nk = KBLK;
     load_t(0);
     load_w(0);
     if (nk > 1) {
+      load_t(1);
       load_w(1);
-      wait_vmcnt<4>();
-    } else {
-      wait_vmcnt<0>();
     }
+    wait_vmcnt<0>();
     stage_barrier();
     for (int k = 0; k < nk; ++k) {
       const uint32_t wb = kWOff + uint32_t(k % SW) * WSTAGE;
-      const uint32_t sp = uint32_t(k & 1) * 1024u;
+      const uint32_t tp = uint32_t(k & 1);
       // token fragments and scales of stage k into registers
       i32x8_t tf[NJB > 0 ? NJB : 1];
   #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) tf[jb] = lds_frag(kTOff + uint32_t(t_row + 16 * jb) * ROWB);
+      for (int jb = 0; jb < NJB; ++jb)
+        tf[jb] = lds_frag(kTOff + tp * TSTAGE + uint32_t(t_row + 16 * jb) * ROWB);
       float s[2][NJB > 0 ? NJB : 1];                                        // s_a * s_w per weight half
       {
-        const float s_w0 = lds_f32(kSwOff + sp + (MODE == kGatedBf16 ? 0u : 256u * wn));
-        const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + sp + 256u) : s_w0;
+        const float s_w0 = lds_f32(kSwOff + tp * kSwStage);
+        const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + tp * kSwStage + 256u) : s_w0;
   #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-          const float s_a = lds_f32(kSaOff + sp + uint32_t(t_row + 16 * jb) * 4u);
+          const float s_a = lds_f32(kSaOff + tp * kSaStage + uint32_t(t_row + 16 * jb) * 4u);
           s[0][jb] = s_a * s_w0;
           s[1][jb] = s_a * s_w1;
         }
       }
+      if (k + 2 < nk) {
+        // every wave holds its stage-k tokens and scales: that buffer takes stage k+2,
+        // and the weight buffer stage k-1 left takes weights k+2
+        stage_barrier();
+        load_t(k + 2);
+        load_w(k + 2);
+      }
       // each product is rescaled as soon as it is back; the other wave on the SIMD
       // keeps the matrix core busy meanwhile
-      auto block_row = [&](int ib) __attribute__((always_inline)) {
-        if constexpr (NJB == 0) return;
-        const i32x8_t wf = lds_frag(wb + uint32_t(w_row[ib]) * ROWB);
-        const int h = (MODE == kGatedBf16 && ib >= 4) ? 1 : 0;
   #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-          const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf, tf[jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      for (int ib = 0; ib < 4; ++ib) {
+        if constexpr (NJB > 0) {
+          const i32x8_t wf = lds_frag(wb + uint32_t(w_row[ib]) * ROWB);
+          const int h = (MODE == kGatedBf16 && ib >= 2) ? 1 : 0;
   #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[h][jb], acc[ib][jb][q]);
+          for (int jb = 0; jb < NJB; ++jb) {
+            const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wf, tf[jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[h][jb], acc[ib][jb][q]);
+          }
         }
-      };
-      block_row(0);
-      if (k + 1 < nk) {
-        // every wave holds its stage-k token fragments and scales: reload that buffer
-        // with stage k+1, then weight stage k+2 into the buffer stage k-1 left
-        stage_barrier();
-        load_t(k + 1);
-        if (k + 2 < nk) load_w(k + 2);
       }
-  #pragma unroll
-      for (int ib = 1; ib < 8; ++ib) block_row(ib);
       if (k + 1 < nk) {
-        if (k + 2 < nk) wait_vmcnt<4>();
+        // publish stage k+1 (its loads went out one stage ago); stage k+2's may stay
+        // in flight
+        if (k + 2 < nk) wait_vmcnt<NTB + 3>();
         else wait_vmcnt<0>();
         stage_barrier();
       }
@@ -251,32 +249,32 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
   #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
-      const int rl = wt * 64 + jb * 16 + (l & 15);
+      const int rl = wt * 80 + jb * 16 + (l & 15);
       if (rl >= mvalid) continue;
       uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
       if (MODE == kGatedBf16) {
   #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-          const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
+        for (int ib = 0; ib < 2; ++ib) {
+          const int col = n0 + wn * 32 + ib * 16 + 4 * (l >> 4);
           if (col >= a.N) continue;
           float hv[4];
   #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q];
+          for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 2][jb][q];
           *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
       } else {
   #pragma unroll
-        for (int ib = 0; ib < 8; ++ib) {
-          const int col = n0 + wn * 128 + ib * 16 + 4 * (l >> 4);
+        for (int ib = 0; ib < 4; ++ib) {
+          const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
           if (col >= a.N) continue;
           const f32x4_t& v = acc[ib][jb];
           *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
     }
-
   };
-  if (njb > 2) body(std::integral_constant<int, 4>{});
+  if (njb >= 5) body(std::integral_constant<int, 5>{});
+  else if (njb >= 3) body(std::integral_constant<int, 4>{});
   else if (njb == 2) body(std::integral_constant<int, 2>{});
   else if (njb == 1) body(std::integral_constant<int, 1>{});
   else body(std::integral_constant<int, 0>{});
@@ -314,7 +312,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.K = H;
   a.T = T;
   a.TK = TK;
-  a.n_tiles = ceil_div(I, 128);
+  a.n_tiles = ceil_div(I, 64);
   a.gather = 1;
   a.a_rows = T;
   hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512),
@@ -337,7 +335,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.ldc = H;
   d.N = H;
   d.K = I;
-  d.n_tiles = ceil_div(H, 256);
+  d.n_tiles = ceil_div(H, 128);
   hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512),
                      0, s, d);
   return hipGetLastError();

@@ -26,7 +26,7 @@ struct Workspace {
 
 constexpr int kTokChunk = 64;   // tokens per permute chunk (one 64-bit mask)
 constexpr int kExpertBM = 320;  // rows per row block of the bf16 expert GEMMs
-constexpr int kFp8BT = 256;     // rows per row block of the FP8 expert GEMMs (<= kExpertBM)
+constexpr int kFp8BT = 320;     // rows per row block of the FP8 expert GEMMs (<= kExpertBM)
 
 // Upper bound on the row blocks (m-tiles of bm rows) over all groups: every routed
 // expert may end in a partial block, the shared experts have T rows each.
