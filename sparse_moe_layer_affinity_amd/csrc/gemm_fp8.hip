@@ -22,11 +22,10 @@
 // the matrix core), each 64 weight rows x 80 tokens = 4 x 5 MFMA blocks.  K advances one
 // 128-byte scale block per stage.  Operands and scales go global -> LDS with buffer
 // loads in LDS mode.  Weights (streamed from HBM) cycle through three 16 KB stage
-// buffers; tokens (mostly L2 hits) and scales through two: every wave reads all its
-// token fragments and scales of a stage into registers first, and once a barrier
-// confirms that, stage k+2's tokens, scales and weights are loaded, so both streams have
-// two stages of lead.  Row blocks come from the same largest-first XCD schedule as the
-// bf16 kernel.
+// buffers, two stages ahead; tokens (mostly L2 hits) and scales through two, one and a
+// half stages ahead, and from there into one of two register sets one stage ahead, so
+// their LDS reads overlap the MFMAs.  Row blocks come from the same largest-first XCD
+// schedule as the bf16 kernel.
 #include "gemm_common.h"
 
 namespace moe {
@@ -184,66 +183,89 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
       return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lds) + byte);
     };
 
-    // prologue: tokens (+ scales) and weights of stages 0 and 1.  K is a multiple of
-    // 128: nk >= 1.
+    // Token fragments and scales of a stage are read into registers one stage early
+    // (two register sets), so the reads of stage k+1 run under stage k's MFMAs.  Per
+    // stage k, two barriers:
+    //   P_k  stage k's weights and stage k+1's tokens and scales are in LDS (loaded two
+    //        stages / one and a half stages ahead); weights k+2 go out into the buffer
+    //        stage k-1 left
+    //   R_k  every wave holds stage k+1's tokens and scales: that buffer takes stage k+3
+    // K is a multiple of 128: nk >= 1.
     const int nk = KBLK;
-    load_t(0);
+    i32x8_t tf[2][NJB > 0 ? NJB : 1];
+    float s[2][2][NJB > 0 ? NJB : 1];                    // per set: s_a * s_w per weight half
+    auto read_tokens = [&](auto set_tag, int ks) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+      const uint32_t tp = uint32_t(ks & 1);
+  #pragma unroll
+      for (int jb = 0; jb < NJB; ++jb)
+        tf[S][jb] = lds_frag(kTOff + tp * TSTAGE + uint32_t(t_row + 16 * jb) * ROWB);
+      const float s_w0 = lds_f32(kSwOff + tp * kSwStage);
+      const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + tp * kSwStage + 256u) : s_w0;
+  #pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const float s_a = lds_f32(kSaOff + tp * kSaStage + uint32_t(t_row + 16 * jb) * 4u);
+        s[S][0][jb] = s_a * s_w0;
+        s[S][1][jb] = s_a * s_w1;
+      }
+    };
+    // weight block ib of stage ks against the stage's tokens (register set S); each
+    // product is rescaled as soon as it is back, the other wave on the SIMD keeping the
+    // matrix core busy meanwhile
+    auto block_row = [&](auto set_tag, int ks, int ib) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+      if constexpr (NJB > 0) {
+        const i32x8_t wf = lds_frag(kWOff + uint32_t(ks % SW) * WSTAGE + uint32_t(w_row[ib]) * ROWB);
+        const int h = (MODE == kGatedBf16 && ib >= 2) ? 1 : 0;
+  #pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf, tf[S][jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[S][h][jb], acc[ib][jb][q]);
+        }
+      }
+    };
+    // prologue: weights and tokens of stages 0 and 1, stage 0's fragments, tokens 2
     load_w(0);
+    load_t(0);
     if (nk > 1) {
-      load_t(1);
       load_w(1);
+      load_t(1);
     }
     wait_vmcnt<0>();
     stage_barrier();
-    for (int k = 0; k < nk; ++k) {
-      const uint32_t wb = kWOff + uint32_t(k % SW) * WSTAGE;
-      const uint32_t tp = uint32_t(k & 1);
-      // token fragments and scales of stage k into registers
-      i32x8_t tf[NJB > 0 ? NJB : 1];
-  #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb)
-        tf[jb] = lds_frag(kTOff + tp * TSTAGE + uint32_t(t_row + 16 * jb) * ROWB);
-      float s[2][NJB > 0 ? NJB : 1];                                        // s_a * s_w per weight half
-      {
-        const float s_w0 = lds_f32(kSwOff + tp * kSwStage);
-        const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + tp * kSwStage + 256u) : s_w0;
-  #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-          const float s_a = lds_f32(kSaOff + tp * kSaStage + uint32_t(t_row + 16 * jb) * 4u);
-          s[0][jb] = s_a * s_w0;
-          s[1][jb] = s_a * s_w1;
-        }
-      }
-      if (k + 2 < nk) {
-        // every wave holds its stage-k tokens and scales: that buffer takes stage k+2,
-        // and the weight buffer stage k-1 left takes weights k+2
+    read_tokens(std::integral_constant<int, 0>{}, 0);
+    if (nk > 2) {
+      stage_barrier();
+      load_t(2);
+    }
+    auto stage = [&](auto set_tag, int k) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+      using N = std::integral_constant<int, 1 - S>;
+      // P_k: pending may stay weights k+1 and tokens k+2
+      if (k + 2 < nk) wait_vmcnt<NTB + 3>();
+      else if (k + 1 < nk) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+      if (k + 2 < nk) load_w(k + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 1 < nk) read_tokens(N{}, k + 1);
+      block_row(set_tag, k, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 3 < nk) {                        // R_k
         stage_barrier();
-        load_t(k + 2);
-        load_w(k + 2);
+        load_t(k + 3);
       }
-      // each product is rescaled as soon as it is back; the other wave on the SIMD
-      // keeps the matrix core busy meanwhile
-  #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        if constexpr (NJB > 0) {
-          const i32x8_t wf = lds_frag(wb + uint32_t(w_row[ib]) * ROWB);
-          const int h = (MODE == kGatedBf16 && ib >= 2) ? 1 : 0;
-  #pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) {
-            const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                wf, tf[jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-  #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[h][jb], acc[ib][jb][q]);
-          }
-        }
-      }
-      if (k + 1 < nk) {
-        // publish stage k+1 (its loads went out one stage ago); stage k+2's may stay
-        // in flight
-        if (k + 2 < nk) wait_vmcnt<NTB + 3>();
-        else wait_vmcnt<0>();
-        stage_barrier();
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      block_row(set_tag, k, 1);
+      block_row(set_tag, k, 2);
+      block_row(set_tag, k, 3);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int k = 0; k < nk; k += 2) {
+      stage(std::integral_constant<int, 0>{}, k);
+      if (k + 1 < nk) stage(std::integral_constant<int, 1>{}, k + 1);
     }
 
     // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
