@@ -27,12 +27,17 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   e4m3 table/RNE   pinned: all 256 codes and a float32 sweep vs torch.float8_e4m3fn
   quantize_1x128   pinned: bound |x - s*q| <= half an e4m3 step, amax maps to 448,
                    zero block gets scale 1, hand-computed golden rows
+  pow2_scale /     pinned: power of two, amax <= 448 s < 2 amax (brute force over a
+  quantize_1x128_pow2      float32 sweep against an integer-exponent search), hand
+                   values (448 -> 1, 449 -> 2, 1 -> 2^-8), blocks of e4m3 values times
+                   a power of two quantise exactly, the half-step bound
 """
 from .moe_layer import (RouteResult, affinities, route, permute, expert_ffn, layer_output,
                         bias_update, silu)
 from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128,
-                   dequantize_blocks_128, expert_ffn_fp8_emulated)
+                   dequantize_blocks_128, expert_ffn_fp8_emulated, pow2_scale,
+                   quantize_1x128_pow2, expert_ffn_fp8_pow2_emulated)
 
 __all__ = ["RouteResult", "affinities", "route", "permute", "expert_ffn", "layer_output",
            "bias_update", "silu", "e4m3_table", "e4m3_encode_rne", "quantize_1x128",
-           "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated"]
+           "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated"]

@@ -16,6 +16,10 @@ Readings (listed in the design notes):
     the sign of a value that rounds to zero is kept (0x80 for negative values)
   * a quantised GEMM equals sum over 128-wide K blocks of (s_a * s_w * sum q_a q_w);
     the oracle computes it as the exact product of dequantised values.
+  * power-of-two variant (scales an 8-bit exponent, E8M0, can hold; the pages give the
+    block shapes, not the scale encoding): s = the smallest power of two with
+    amax <= 448 * s (1 when amax == 0); codes as above, the quotient x / s being exact.
+    Weight block scales of this variant are powers of two as stored.
 """
 from __future__ import annotations
 
@@ -80,6 +84,28 @@ def quantize_1x128(x):
     return e4m3_encode_rne(quot).reshape(rows, cols), scale
 
 
+def pow2_scale(amax) -> np.ndarray:
+    """Smallest power of two s with amax <= 448 s (s = 1 for amax == 0), exact.
+
+    With amax = m 2^E, m in [0.5, 1): 448 = 0.875 2^9, so s = 2^(E-9) when m <= 0.875 and
+    2^(E-8) otherwise.  Returned as float32 (every such power is a normal float32 for
+    float32 inputs below 448 * 2^127)."""
+    a = np.asarray(amax, np.float64)
+    m, e = np.frexp(a)
+    s = np.ldexp(1.0, np.where(m <= 0.875, e - 9, e - 8))
+    return np.where(a > 0, s, 1.0).astype(np.float32)
+
+
+def quantize_1x128_pow2(x):
+    """quantize_1x128 with power-of-two block scales (pow2_scale of the block amax)."""
+    x32 = np.asarray(_f64(x), dtype=np.float32)
+    rows, cols = x32.shape
+    blocks = x32.reshape(rows, cols // 128, 128)
+    scale = pow2_scale(np.abs(blocks).max(axis=2))
+    quot = blocks.astype(np.float64) / scale[:, :, None].astype(np.float64)   # exact
+    return e4m3_encode_rne(quot).reshape(rows, cols), scale
+
+
 def dequantize_1x128(codes, scales) -> np.ndarray:
     codes = np.asarray(codes, dtype=np.uint8)
     rows, cols = codes.shape
@@ -104,15 +130,22 @@ def _round_bf16(a: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
 
 
-def expert_ffn_fp8_emulated(u, w_gate, w_up, w_down) -> np.ndarray:
+def expert_ffn_fp8_emulated(u, w_gate, w_up, w_down, pow2: bool = False) -> np.ndarray:
     """Diagnostic FP8 expert: u and the SwiGLU output h are each quantised per 1x128
-    along their own K dimension before the GEMM that consumes them; weights are
-    already dequantised float64 arrays.  Products and sums in float64.
+    along their own K dimension before the GEMM that consumes them (power-of-two
+    scales if pow2); weights are already dequantised float64 arrays.  Products and
+    sums in float64.
 
     The pages fix no storage precision for h between the two GEMMs; the kernels
     hold it in bf16, so the FP8 codes of h are decided on the bf16-rounded value
     (a code is decided in the kernel's precision where the pages are silent)."""
-    uq = dequantize_1x128(*quantize_1x128(np.asarray(_f64(u), np.float32)))
+    quant = quantize_1x128_pow2 if pow2 else quantize_1x128
+    uq = dequantize_1x128(*quant(np.asarray(_f64(u), np.float32)))
     h = silu(uq @ _f64(w_gate).T) * (uq @ _f64(w_up).T)
-    hq = dequantize_1x128(*quantize_1x128(_round_bf16(h)))
+    hq = dequantize_1x128(*quant(_round_bf16(h)))
     return hq @ _f64(w_down).T
+
+
+def expert_ffn_fp8_pow2_emulated(u, w_gate, w_up, w_down) -> np.ndarray:
+    """expert_ffn_fp8_emulated with power-of-two activation scales."""
+    return expert_ffn_fp8_emulated(u, w_gate, w_up, w_down, pow2=True)

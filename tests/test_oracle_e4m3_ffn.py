@@ -164,3 +164,75 @@ def test_fp8_emulated_close_to_exact():
     emu = oracle.expert_ffn_fp8_emulated(u, wg, wu, wd)
     rel = np.abs(emu - exact).max() / np.abs(exact).max()
     assert 1e-4 < rel < 0.1
+
+
+def _pow2_brute(a: float) -> float:
+    """The smallest 2^k (integer k) with a <= 448 * 2^k, found by scanning k."""
+    if a == 0.0:
+        return 1.0
+    for k in range(-150, 140):
+        if a <= 448.0 * 2.0 ** k:
+            return 2.0 ** k
+    raise AssertionError(a)
+
+
+def test_pow2_scale_hand_values_and_brute_force():
+    # hand values: 448 = 448 * 2^0; 449 needs 2^1; 1 <= 448 * 2^-8 = 1.75 but > 0.875
+    assert oracle.pow2_scale([448.0, 449.0, 1.0, 224.0, 0.0]).tolist() == [1.0, 2.0, 2.0 ** -8, 0.5, 1.0]
+    rng = np.random.default_rng(11)
+    a = np.concatenate([
+        np.exp(rng.uniform(-40, 40, 3000)).astype(np.float32),
+        np.float32(448.0) * np.ldexp(np.float32(1.0), rng.integers(-30, 30, 200)).astype(np.float32),
+        np.nextafter(np.float32(448.0) * np.ldexp(np.float32(1.0), rng.integers(-30, 30, 200)).astype(np.float32),
+                     np.float32(np.inf)),
+    ]).astype(np.float32)
+    s = oracle.pow2_scale(a)
+    assert s.dtype == np.float32
+    for ai, si in zip(a.tolist(), s.tolist()):
+        assert si == _pow2_brute(ai), (ai, si)
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)                                  # powers of two
+    assert np.all(a <= 448.0 * s.astype(np.float64)) and np.all(a > 224.0 * s.astype(np.float64))
+
+
+def test_quantize_1x128_pow2_exact_and_bounded():
+    rng = np.random.default_rng(12)
+    tab = oracle.e4m3_table()
+    # blocks made of e4m3 values times a power of two quantise exactly when the block
+    # amax is a power-of-two multiple of 448 (then the scale is that power)
+    codes = rng.integers(0, 0x7E, (4, 256)).astype(np.uint8) | (rng.integers(0, 2, (4, 256)) * 0x80).astype(np.uint8)
+    codes[:, 0] = 0x7E
+    codes[:, 128] = 0xFE
+    p = np.ldexp(1.0, rng.integers(-10, 10, (4, 2)))
+    x = (tab[codes].reshape(4, 2, 128) * p[:, :, None]).reshape(4, 256).astype(np.float32)
+    q, s = oracle.quantize_1x128_pow2(x)
+    assert np.array_equal(s.astype(np.float64), p)
+    assert np.array_equal(q, codes)
+    # random data: power-of-two scales, the half-step bound, magnitudes <= 448
+    x = (rng.standard_normal((16, 512)) * rng.uniform(0.01, 10, (16, 1))).astype(np.float32)
+    x[5, :128] = 0.0
+    q, s = oracle.quantize_1x128_pow2(x)
+    assert s[5, 0] == 1.0 and np.all(q[5, :128] == 0)
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)
+    deq = oracle.dequantize_1x128(q, s)
+    err = np.abs(deq - x) / np.repeat(s, 128, axis=1)
+    step = np.abs(tab[q]) * 2.0 ** -3
+    assert np.all(np.abs(tab[q]) <= 448.0)
+    assert np.all(err <= np.maximum(step, 2.0 ** -9) / 2 * (1 + 1e-6) + 1e-12)
+    # differs from the amax / 448 rule: the block maximum usually no longer maps to 448
+    q2, _ = oracle.quantize_1x128(x)
+    assert not np.array_equal(q, q2)
+
+
+def test_fp8_pow2_emulated_close_to_exact():
+    rng = np.random.default_rng(13)
+    h, inter = 256, 128
+    u = rng.standard_normal((8, h)).astype(np.float32)
+    wg, wu, wd = (rng.standard_normal((inter, h)) * 0.05, rng.standard_normal((inter, h)) * 0.05,
+                  rng.standard_normal((h, inter)) * 0.05)
+    exact = oracle.expert_ffn(u, wg, wu, wd)
+    emu = oracle.expert_ffn_fp8_pow2_emulated(u, wg, wu, wd)
+    rel = np.abs(emu - exact).max() / np.abs(exact).max()
+    assert 1e-4 < rel < 0.1
+    assert not np.array_equal(emu, oracle.expert_ffn_fp8_emulated(u, wg, wu, wd))
