@@ -26,7 +26,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}   # dense TFLOP/s, MI355X
+PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "e4m3_pow2": 5000.0, "f32": 157.3}   # dense TFLOP/s, MI355X
 HBM_PEAK = 8000.0                                         # GB/s
 METRIC = "MoE layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), T=8192 h=7168 E=256 k=8"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -71,7 +71,7 @@ def cpu_baseline(cfg, d, n_tokens: int):
     w_r = d["w_router"].cpu()
 
     def get(e):
-        if cfg.w == "e4m3":
+        if workloads.is_fp8(cfg.w):
             return tuple(oracle.dequantize_blocks_128(d[n][e], d["s" + n[1:]][e])
                          for n in ("w_gate", "w_up", "w_down"))
         return tuple(d[n][e].to("cpu").double().numpy() for n in ("w_gate", "w_up", "w_down"))
@@ -99,7 +99,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_bf16",
-                    choices=["prefill_bf16", "decode_bf16", "prefill_fp8", "skewed_bf16"])
+                    choices=["prefill_bf16", "decode_bf16", "prefill_fp8", "prefill_fp8_pow2", "skewed_bf16"])
     ap.add_argument("--cpu-tokens", type=int, default=48,
                     help="tokens in the oracle's bounded sample (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,9 +183,9 @@ def main():
     ffn_ms = stage_ms["grouped_ffn"]
     gemm_tflops = ffn_flops / (ffn_ms * 1e-3) / 1e12
     touched = int((load > 0).sum().item()) + cfg.Ns
-    wbytes_per_elem = 1 if cfg.w == "e4m3" else (4 if cfg.w == "f32" else 2)
+    wbytes_per_elem = 1 if workloads.is_fp8(cfg.w) else (4 if cfg.w == "f32" else 2)
     weight_bytes = touched * 3 * cfg.hidden * cfg.inter * wbytes_per_elem
-    if cfg.w == "e4m3":
+    if workloads.is_fp8(cfg.w):
         weight_bytes += touched * 3 * (cfg.hidden // 128) * (cfg.inter // 128) * 4
     ffn_bytes = weight_bytes + 2 * T * cfg.hidden * (4 if cfg.act == "f32" else 2)
     decode = cfg.T <= 512
@@ -204,7 +204,7 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if cfg.w != "e4m3" else "e4m3",
+        "dtype": "e4m3" if workloads.is_fp8(cfg.w) else "bf16",
         "data": "synthetic (seeded; weights N(0, 0.02^2), x N(0, 1))",
         "config": {"workload": cfg.name, "T": T, "hidden": cfg.hidden, "inter": cfg.inter,
                    "E": E, "K": K, "G": cfg.G, "M": cfg.M, "group_topn": cfg.topn,

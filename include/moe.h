@@ -54,7 +54,13 @@ typedef enum {
   MOE_ERR_HIP = 4                  /* a HIP launch failed                          */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+/* MOE_E4M3_POW2 (expert weights only): E4M3 with every block scale a power of two
+ * (what an 8-bit exponent, E8M0, holds); activations are then quantised with
+ * power-of-two scales too, and the expert GEMMs apply both in the matrix cores'
+ * block-scaled mode.  A cheaper FP8 variant than the pages' arbitrary fp32 block
+ * scales (devpress page, section 2, gives the 128x128 / 1x128 block shapes only):
+ * its numerics differ from MOE_E4M3's. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2, MOE_E4M3_POW2 = 3 } moe_dtype;
 
 typedef struct {
   int32_t num_tokens;   /* T >= 1                                                  */
@@ -67,7 +73,7 @@ typedef struct {
   int32_t top_groups;   /* M groups kept per token, 1..G                           */
   int32_t group_topn;   /* biased affinities summed into a group score, 1..E/G     */
   moe_dtype act_dtype;  /* F32 | BF16: u, router weight, y_rows and the output     */
-  moe_dtype w_dtype;    /* F32 | BF16 | E4M3: expert weights                       */
+  moe_dtype w_dtype;    /* F32 | BF16 | E4M3 | E4M3_POW2: expert weights           */
 } moe_config;
 
 /* Expert weights (device pointers), experts stacked routed-first.
@@ -75,8 +81,9 @@ typedef struct {
  * in w_dtype.  For E4M3 (OCP e4m3fn codes, one byte each) every 128x128 block
  * carries one fp32 scale, the weight being code_value * scale:
  *   s_gate, s_up : [E+Ns, inter/128, hidden/128]   s_down : [E+Ns, hidden/128, inter/128]
- * (devpress page, section 2: per-128x128-block weight quantisation).  The scale
- * pointers must be NULL unless w_dtype == E4M3. */
+ * (devpress page, section 2: per-128x128-block weight quantisation).  For E4M3_POW2
+ * each scale must be a power of two in [2^-126, 2^127] (only its exponent field is
+ * used).  The scale pointers must be NULL unless w_dtype is E4M3 or E4M3_POW2. */
 typedef struct {
   const void  *w_gate, *w_up, *w_down;
   const float *s_gate, *s_up, *s_down;
@@ -118,7 +125,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* 
 /* FP8 activation quantisation (devpress page section 2, 1x128 activation tiles;
  * largest e4m3 value 448 from the stapisi blog section 6.2): for every row r and
  * every 128-column block j of x [rows, cols] (act_dtype BF16, cols % 128 == 0)
- *   scales[r, j] = amax / 448 in fp32 (1 when amax == 0)
+ *   scales[r, j] = amax / 448 in fp32 (1 when amax == 0); for w_dtype E4M3_POW2
+ *                  the smallest power of two s with amax <= 448 s (1 when amax == 0)
  *   q[r, c]      = e4m3 code of round-to-nearest-even(x[r, c] / scales[r, j]),
  *                  saturated to +-448
  * q [rows, cols] uint8 out; scales [rows, cols/128] fp32 out.  Used inside

@@ -16,8 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
-DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
+MOE_F32, MOE_BF16, MOE_E4M3, MOE_E4M3_POW2 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3, "e4m3_pow2": MOE_E4M3_POW2}
 
 
 class MoeConfig(ctypes.Structure):

@@ -15,7 +15,7 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   const size_t H = c.hidden, I = c.inter;
   const size_t TK = T * K, rows = TK + T * Ns;
   const size_t chunks = (T + kTokChunk - 1) / kTokChunk;
-  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const bool fp8 = is_fp8(c.w_dtype);
   Workspace w{};
   char* p = static_cast<char*>(base);
   size_t off = 0;
@@ -42,7 +42,9 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   return w;
 }
 
-static bool valid_dtype(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_E4M3; }
+static bool valid_dtype(moe_dtype d) {
+  return d == MOE_F32 || d == MOE_BF16 || d == MOE_E4M3 || d == MOE_E4M3_POW2;
+}
 
 static moe_status validate(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARGUMENT;
@@ -61,7 +63,7 @@ static moe_status validate(const moe_config* c) {
     return MOE_ERR_UNSUPPORTED;
   const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32;
   const bool bf16 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_BF16;
-  const bool fp8 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_E4M3;
+  const bool fp8 = c->act_dtype == MOE_BF16 && is_fp8(c->w_dtype);
   if (!(f32 || bf16 || fp8)) return MOE_ERR_UNSUPPORTED;
   if (f32 && (c->hidden % 4 || c->inter % 4)) return MOE_ERR_UNSUPPORTED;
   if (!f32 && (c->hidden % 128 || c->inter % 128)) return MOE_ERR_UNSUPPORTED;
@@ -88,7 +90,7 @@ static moe_status check_ws(const moe_config& c, const void* ws, size_t ws_bytes)
 
 static moe_status check_weights(const moe_config& c, const moe_expert_weights* w) {
   if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARGUMENT;
-  const bool fp8 = c.w_dtype == MOE_E4M3;
+  const bool fp8 = is_fp8(c.w_dtype);
   const bool have = w->s_gate && w->s_up && w->s_down;
   const bool none = !w->s_gate && !w->s_up && !w->s_down;
   if (fp8 ? !have : !none) return MOE_ERR_INVALID_ARGUMENT;
@@ -148,7 +150,8 @@ moe_status moe_act_quant_e4m3(const moe_config* cfg, const void* x, int32_t rows
   if (cfg->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!x || !q || !scales || rows < 1 || cols < 128 || cols % 128)
     return MOE_ERR_INVALID_ARGUMENT;
-  return from_hip(launch_act_quant(x, rows, cols, q, scales, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_act_quant(x, rows, cols, q, scales, static_cast<hipStream_t>(stream), false,
+                                   cfg->w_dtype == MOE_E4M3_POW2));
 }
 
 moe_status moe_grouped_ffn(const moe_config* cfg, const void* x, const int32_t* expert_offsets,

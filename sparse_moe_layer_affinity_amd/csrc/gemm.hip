@@ -761,7 +761,7 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
                        static_cast<float*>(y_rows));
     return hipGetLastError();
   }
-  if (c.w_dtype == MOE_E4M3)
+  if (is_fp8(c.w_dtype))
     return launch_grouped_ffn_fp8(c, x, offsets, row_token, w, y_rows, ws, s);
   hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;

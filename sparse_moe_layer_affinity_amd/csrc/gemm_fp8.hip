@@ -50,7 +50,10 @@ struct Fp8Args {
   int a_rows;
 };
 
-template <int MODE>
+// POW2: every block scale is a power of two; the MFMAs apply them in block-scaled mode
+// (an 8-bit exponent per lane for the 32 K values it supplies; all four 32-wide parts of
+// a 128-wide block carry the same one) and accumulate in place: no rescale on the VALU.
+template <int MODE, bool POW2>
 __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   constexpr int BW = 128, BT = kFp8BT, ROWB = 128;
   constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 16 KB, 40 KB
@@ -194,6 +197,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     const int nk = KBLK;
     i32x8_t tf[2][NJB > 0 ? NJB : 1];
     float s[2][2][NJB > 0 ? NJB : 1];                    // per set: s_a * s_w per weight half
+    int ea[2][NJB > 0 ? NJB : 1], ew[2][2];              // POW2: exponent codes (4 copies)
+    // 8-bit exponent code of a power-of-two float32, in every byte of the operand
+    auto e8 = [](float v) { return int(((__float_as_uint(v) >> 23) & 0xffu) * 0x01010101u); };
     auto read_tokens = [&](auto set_tag, int ks) __attribute__((always_inline)) {
       constexpr int S = decltype(set_tag)::value;
       const uint32_t tp = uint32_t(ks & 1);
@@ -202,11 +208,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
         tf[S][jb] = lds_frag(kTOff + tp * TSTAGE + uint32_t(t_row + 16 * jb) * ROWB);
       const float s_w0 = lds_f32(kSwOff + tp * kSwStage);
       const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + tp * kSwStage + 256u) : s_w0;
+      if constexpr (POW2) {
+        ew[S][0] = e8(s_w0);
+        ew[S][1] = e8(s_w1);
+      }
   #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const float s_a = lds_f32(kSaOff + tp * kSaStage + uint32_t(t_row + 16 * jb) * 4u);
-        s[S][0][jb] = s_a * s_w0;
-        s[S][1][jb] = s_a * s_w1;
+        if constexpr (POW2) {
+          ea[S][jb] = e8(s_a);
+        } else {
+          s[S][0][jb] = s_a * s_w0;
+          s[S][1][jb] = s_a * s_w1;
+        }
       }
     };
     // weight block ib of stage ks against the stage's tokens (register set S); each
@@ -219,10 +233,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
         const int h = (MODE == kGatedBf16 && ib >= 2) ? 1 : 0;
   #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-          const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf, tf[S][jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          if constexpr (POW2) {
+            acc[ib][jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wf, tf[S][jb], acc[ib][jb], 0, 0, 0, ew[S][h], 0, ea[S][jb]);
+          } else {
+            const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wf, tf[S][jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
   #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[S][h][jb], acc[ib][jb][q]);
+            for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[S][h][jb], acc[ib][jb][q]);
+          }
         }
       }
     };
@@ -311,7 +330,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   const int T = c.num_tokens, Ns = c.num_shared;
   const int TK = T * c.top_k, rows = TK + T * Ns;
   const int H = c.hidden, I = c.inter;
-  hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s, true);
+  const bool pow2 = c.w_dtype == MOE_E4M3_POW2;
+  hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s, true, pow2);
   if (err != hipSuccess) return err;
   err = launch_build_schedule(c, offsets, kFp8BT, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
@@ -337,9 +357,11 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.n_tiles = ceil_div(I, 64);
   a.gather = 1;
   a.a_rows = T;
-  hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512),
-                     0, s, a);
-  err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true);
+  if (pow2)
+    hipLaunchKernelGGL((grouped_gemm_fp8<kGatedBf16, true>), dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_fp8<kGatedBf16, false>), dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
+  err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true, pow2);
   if (err != hipSuccess) return err;
   Fp8Args d = a;
   d.A = ws.hq;
@@ -358,8 +380,10 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 128);
-  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512),
-                     0, s, d);
+  if (pow2)
+    hipLaunchKernelGGL((grouped_gemm_fp8<kPlainBf16, true>), dim3(rounds * kXcds * d.n_tiles), dim3(512), 0, s, d);
+  else
+    hipLaunchKernelGGL((grouped_gemm_fp8<kPlainBf16, false>), dim3(rounds * kXcds * d.n_tiles), dim3(512), 0, s, d);
   return hipGetLastError();
 }
 

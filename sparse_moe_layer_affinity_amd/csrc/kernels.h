@@ -24,6 +24,9 @@ struct Workspace {
   size_t bytes;        // total bytes of the layout
 };
 
+// E4M3 expert weights, with fp32 or power-of-two block scales
+inline bool is_fp8(moe_dtype d) { return d == MOE_E4M3 || d == MOE_E4M3_POW2; }
+
 constexpr int kTokChunk = 64;   // tokens per permute chunk (one 64-bit mask)
 constexpr int kExpertBM = 320;  // rows per row block of the bf16 expert GEMMs
 constexpr int kFp8BT = 320;     // rows per row block of the FP8 expert GEMMs (<= kExpertBM)
@@ -69,7 +72,7 @@ hipError_t launch_permute(const moe_config& c, const int32_t* idx, int32_t* load
                           int32_t* offsets, int32_t* row_token, int32_t* pair_row,
                           const Workspace& ws, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
-                            hipStream_t s, bool transposed = false);
+                            hipStream_t s, bool transposed = false, bool pow2 = false);
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,
                               const int32_t* row_token, const moe_expert_weights& w,
                               void* y_rows, const Workspace& ws, hipStream_t s);

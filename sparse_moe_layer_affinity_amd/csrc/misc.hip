@@ -114,10 +114,14 @@ hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float ga
 // lanes; scale = amax / 448 (1 if amax == 0); code = RNE-saturate(x / scale).
 // Scales go to [rows, cols/128] (the C ABI's layout) or, transposed, to [cols/128, rows]
 // (the expert GEMM's workspace copies: one K block's scales of consecutive rows are
-// then adjacent).
+// then adjacent).  pow2: scale = the smallest power of two s with amax <= 448 s, and
+// at least 2^-126 (a normal float32, whose exponent field is its 8-bit exponent code):
+// with amax = m 2^e, m in [0.5, 1), and 448 = 0.875 2^9, s = 2^(e-9) if m <= 0.875,
+// else 2^(e-8); the quotient x / s is then exact.
 __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x, int rows,
                                                       int cols, uint8_t* __restrict__ q,
-                                                      float* __restrict__ scales, int transposed) {
+                                                      float* __restrict__ scales, int transposed,
+                                                      int pow2) {
   const int bpr = cols / 128;                                   // blocks per row
   const long long blk = (1LL * blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + ((threadIdx.x >> 4) & 3);
   const bool valid = blk < 1LL * rows * bpr;
@@ -140,7 +144,16 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   if (!valid) return;
-  const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  float s = 1.0f;
+  if (amax > 0.f) {
+    if (pow2) {
+      int e;
+      const float m = frexpf(amax, &e);
+      s = ldexpf(1.0f, max(m <= 0.875f ? e - 9 : e - 8, -126));
+    } else {
+      s = __fdiv_rn(amax, 448.0f);
+    }
+  }
   uint32_t c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) c[i] = f32_to_e4m3_rne_sat(__fdiv_rn(v[i], s));
@@ -151,10 +164,11 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
 }
 
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
-                            hipStream_t s, bool transposed) {
+                            hipStream_t s, bool transposed, bool pow2) {
   const long long blocks = 1LL * rows * (cols / 128);
   hipLaunchKernelGGL(act_quant_e4m3, dim3(unsigned((blocks + 15) / 16)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), rows, cols, q, scales, transposed ? 1 : 0);
+                     static_cast<const uint16_t*>(x), rows, cols, q, scales, transposed ? 1 : 0,
+                     pow2 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ import oracle
 import sparse_moe_layer_affinity_amd as moe
 import workloads
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2, "e4m3_pow2": 6e-2}
 
 
 def log(msg: str):
@@ -92,7 +92,7 @@ def permute(cfg, idx, ws=None):
 def expert_getter(cfg, d):
     """Oracle-side access to one expert's weights as float64 arrays (streamed from the GPU)."""
     def get(e):
-        if cfg.w == "e4m3":
+        if workloads.is_fp8(cfg.w):
             return tuple(oracle.dequantize_blocks_128(d[n][e], d["s" + n[1:]][e])
                          for n in ("w_gate", "w_up", "w_down"))
         return tuple(d[n][e].to("cpu", torch.float64).numpy() for n in ("w_gate", "w_up", "w_down"))

@@ -61,6 +61,8 @@ def test_status_strings():
     (dict(topn=9), B.MOE_ERR_UNSUPPORTED),
     (dict(w="e4m3", hidden=7000), B.MOE_ERR_UNSUPPORTED),  # FP8 needs 128-multiples
     (dict(w="e4m3", inter=2000), B.MOE_ERR_UNSUPPORTED),
+    (dict(w="e4m3_pow2", hidden=7000), B.MOE_ERR_UNSUPPORTED),
+    (dict(act="e4m3_pow2", w="e4m3_pow2"), B.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", w="bf16"), B.MOE_ERR_UNSUPPORTED),  # dtype combination
     (dict(act="e4m3", w="e4m3"), B.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", w="f32", hidden=258), B.MOE_ERR_UNSUPPORTED),
@@ -74,13 +76,14 @@ def test_invalid_configs(kw, expected):
 
 
 def test_valid_configs_have_workspace():
-    for kw in [dict(), dict(T=128), dict(w="e4m3"), dict(T=16384),
+    for kw in [dict(), dict(T=128), dict(w="e4m3"), dict(w="e4m3_pow2"), dict(T=16384),
                dict(T=64, hidden=256, inter=128, E=16, K=4, G=4, M=2, act="f32", w="f32")]:
         c = cfg(**kw)
         n = moe.moe_workspace_bytes(c)
         assert n > 0 and n % 256 == 0
     # y_rows and h (T*(K+Ns) rows each) dominate; FP8 adds one-byte codes of x and h
     assert moe.moe_workspace_bytes(cfg()) < moe.moe_workspace_bytes(cfg(w="e4m3")) < 2 * 10 ** 9
+    assert moe.moe_workspace_bytes(cfg(w="e4m3")) == moe.moe_workspace_bytes(cfg(w="e4m3_pow2"))
 
 
 def test_null_pointers_and_workspace_checks():

@@ -1,5 +1,6 @@
-"""GPU parity of the FP8 path (e4m3 weights with 128x128 fp32 block scales, activations
-quantised per 1x128 on the fly) against the float64 oracle.
+"""GPU parity of the FP8 paths (e4m3 weights with 128x128 block scales, activations
+quantised per 1x128 on the fly; the block scales arbitrary fp32 values or powers of
+two) against the float64 oracle.
 
 Two references: the fp32 oracle (dequantised weights, unquantised activations: the
 6e-2 bound of the FP8 workload) and the oracle's FP8-emulating expert (x and h
@@ -43,10 +44,11 @@ def _check(cfg, d, out, rows=None):
     got = out["y"].float().cpu().numpy()[rows]
     ref = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows)
     err = rel_err(got, ref)
-    emu = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows,
-                              ffn=oracle.expert_ffn_fp8_emulated)
+    emu_ffn = (oracle.expert_ffn_fp8_pow2_emulated if cfg.w == "e4m3_pow2"
+               else oracle.expert_ffn_fp8_emulated)
+    emu = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows, ffn=emu_ffn)
     err_emu = rel_err(got, emu)
-    log(f"  {cfg.name}: rows {len(rows)}, near-ties {ties}, rel err vs fp32 {err:.3e}, "
+    log(f"  {cfg.name} ({cfg.w}): rows {len(rows)}, near-ties {ties}, rel err vs fp32 {err:.3e}, "
         f"vs fp8-emulating {err_emu:.3e}")
     assert err <= fp32_tol(len(rows)), err
     assert err_emu <= EMU_TOL, err_emu
@@ -55,17 +57,19 @@ def _check(cfg, d, out, rows=None):
 @pytest.mark.parametrize("over", [dict(T=37), dict(T=1), dict(T=300, seed=1), dict(T=64, Ns=0),
                                   dict(T=129, Ns=2, bias="uniform", bias_range=0.02),
                                   dict(T=200, E=64, G=8, M=4, K=6, inter=384, hidden=384)])
-def test_layer_small_fp8(over):
-    cfg = workloads.get("prefill_fp8").replace(**{**SMALL, **over})
-    log(f"layer small fp8 {over}")
+@pytest.mark.parametrize("w", ["e4m3", "e4m3_pow2"])
+def test_layer_small_fp8(over, w):
+    cfg = workloads.get("prefill_fp8").replace(**{**SMALL, **over, "w": w})
+    log(f"layer small fp8 {w} {over}")
     d = inputs_on_gpu(cfg)
     _check(cfg, d, layer_forward(cfg, d))
 
 
-def test_fp8_decode_shape():
+@pytest.mark.parametrize("w", ["e4m3", "e4m3_pow2"])
+def test_fp8_decode_shape(w):
     cfg = workloads.get("prefill_fp8").replace(T=128, bias="uniform", bias_range=0.01,
-                                               compare_rows=None)
-    log("layer fp8 decode shape (T=128, h=7168, E=256)")
+                                               compare_rows=None, w=w)
+    log(f"layer fp8 decode shape (T=128, h=7168, E=256, {w})")
     d = inputs_on_gpu(cfg)
     out = layer_forward(cfg, d)
     _check(cfg, d, out)
@@ -74,9 +78,10 @@ def test_fp8_decode_shape():
 
 
 @pytest.mark.slow
-def test_layer_prefill_fp8():
-    cfg = workloads.get("prefill_fp8")
-    log("layer prefill_fp8 (T=8192): routing on all tokens, output on 512 sampled rows")
+@pytest.mark.parametrize("name", ["prefill_fp8", "prefill_fp8_pow2"])
+def test_layer_prefill_fp8(name):
+    cfg = workloads.get(name)
+    log(f"layer {name} (T=8192): routing on all tokens, output on 512 sampled rows")
     d = inputs_on_gpu(cfg)
     out = layer_forward(cfg, d)
     _check(cfg, d, out, rows=workloads.sample_rows(cfg.T, cfg.compare_rows).numpy())

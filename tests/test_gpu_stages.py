@@ -78,21 +78,26 @@ def test_bias_update_bit_exact(E, T, K, seed):
     assert got.tobytes() == ref.tobytes()
 
 
+@pytest.mark.parametrize("w", ["e4m3", "e4m3_pow2"])
 @pytest.mark.parametrize("rows,cols", [(1, 128), (7, 7168), (300, 2048), (64, 256)])
-def test_act_quant_bit_exact(rows, cols):
-    log(f"act_quant rows={rows} cols={cols}")
+def test_act_quant_bit_exact(rows, cols, w):
+    log(f"act_quant rows={rows} cols={cols} weights={w}")
     g = torch.Generator().manual_seed(rows * 7 + cols)
     x = torch.randn((rows, cols), generator=g) * torch.exp(torch.randn((rows, 1), generator=g) * 3)
     x[0, :128] = 0.0                                       # zero block -> scale 1
     if cols >= 256:
         x[0, 128] = 448.0 * 2 ** -20                        # tiny block (subnormal codes)
     x = x.to(torch.bfloat16)
-    cfg = workloads.get("prefill_fp8")
+    if w == "e4m3_pow2" and rows > 1:
+        x[1, :128] = 448.0 * 2.0 ** -130                   # scale floor 2^-126
+        x[1, 128 % cols] = -448.0 * 2.0 ** 3               # amax exactly 448 * 2^3
+    cfg = workloads.get("prefill_fp8").replace(w=w)
     q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
     s = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")
     moe.moe_act_quant_e4m3(config_of(cfg), x.cuda(), rows, cols, q, s)
     torch.cuda.synchronize()
-    rq, rs = oracle.quantize_1x128(x.float().numpy())
+    quant = oracle.quantize_1x128_pow2 if w == "e4m3_pow2" else oracle.quantize_1x128
+    rq, rs = quant(x.float().numpy())
     assert s.cpu().numpy().tobytes() == rs.tobytes()
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
 

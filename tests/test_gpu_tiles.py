@@ -80,16 +80,18 @@ def _emu_tol(inter):
     return 2e-2 * max(1.0, (256 / inter) ** 0.5)
 
 
+@pytest.mark.parametrize("w", ["e4m3", "e4m3_pow2"])
 @pytest.mark.parametrize("dims", [(256, 256), (128, 128), (128, 2048)])
-def test_row_block_edges_fp8(dims):
+def test_row_block_edges_fp8(dims, w):
     hidden, inter = dims
     cfg = workloads.get("prefill_fp8").replace(T=1000, hidden=hidden, inter=inter, E=16, K=4,
-                                               G=4, M=2, topn=2, Ns=1)
-    log(f"fp8 row-block edges, hidden {hidden}, inter {inter}")
+                                               G=4, M=2, topn=2, Ns=1, w=w)
+    log(f"fp8 row-block edges, hidden {hidden}, inter {inter}, {w}")
     d = inputs_on_gpu(cfg)
     idx = workloads.topk_with_loads(cfg.T, cfg.K, LOADS).numpy()
     off, row_token, ref32 = _grouped_rows_oracle(cfg, d, idx, oracle.expert_ffn)
-    _, _, emu = _grouped_rows_oracle(cfg, d, idx, oracle.expert_ffn_fp8_emulated)
+    emu_ffn = oracle.expert_ffn_fp8_pow2_emulated if w == "e4m3_pow2" else oracle.expert_ffn_fp8_emulated
+    _, _, emu = _grouped_rows_oracle(cfg, d, idx, emu_ffn)
     got = _run(cfg, d, off, row_token)
     errs = _per_expert_errors(cfg, off, got, ref32)
     errs_emu = _per_expert_errors(cfg, off, got, emu)

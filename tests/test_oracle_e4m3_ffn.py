@@ -167,10 +167,10 @@ def test_fp8_emulated_close_to_exact():
 
 
 def _pow2_brute(a: float) -> float:
-    """The smallest 2^k (integer k) with a <= 448 * 2^k, found by scanning k."""
+    """The smallest 2^k (integer k >= -126) with a <= 448 * 2^k, found by scanning k."""
     if a == 0.0:
         return 1.0
-    for k in range(-150, 140):
+    for k in range(-126, 140):
         if a <= 448.0 * 2.0 ** k:
             return 2.0 ** k
     raise AssertionError(a)
@@ -179,6 +179,8 @@ def _pow2_brute(a: float) -> float:
 def test_pow2_scale_hand_values_and_brute_force():
     # hand values: 448 = 448 * 2^0; 449 needs 2^1; 1 <= 448 * 2^-8 = 1.75 but > 0.875
     assert oracle.pow2_scale([448.0, 449.0, 1.0, 224.0, 0.0]).tolist() == [1.0, 2.0, 2.0 ** -8, 0.5, 1.0]
+    assert oracle.pow2_scale([1e-40, 448.0 * 2.0 ** -126, 448.0 * 2.0 ** -125]).tolist() == \
+        [2.0 ** -126, 2.0 ** -126, 2.0 ** -125]
     rng = np.random.default_rng(11)
     a = np.concatenate([
         np.exp(rng.uniform(-40, 40, 3000)).astype(np.float32),

@@ -14,6 +14,8 @@ Workloads (the layer of the DeepSeek-V3 technical report summary, section 2.2
 * ``prefill_bf16`` T=8192,  same shapes, bf16, bias = 0
 * ``prefill_fp8``  T=8192,  expert weights stored as OCP e4m3 codes with one fp32
                    scale per 128x128 block; activations bf16
+* ``prefill_fp8_pow2`` the same with power-of-two block scales (each scale above
+                   rounded down to a power of two: 2^-13 or 2^-12)
 * ``skewed_bf16``  T=16384, 8 hot experts (router logit offset +2.0 on experts
                    0..7, realised as input channel 0 == 1.0 and W_r[e, 0] = 2.0
                    for hot experts, 0 otherwise), 50 steps with gamma = 1e-3
@@ -55,7 +57,7 @@ class MoeShape:
     topn: int           # experts summed into a group score
     Ns: int             # shared experts
     act: str            # "f32" | "bf16"   (x, router weight, output)
-    w: str              # "f32" | "bf16" | "e4m3"   (expert weights)
+    w: str              # "f32" | "bf16" | "e4m3" | "e4m3_pow2"   (expert weights)
     bias: str           # "zero" | "uniform"
     bias_range: float = 0.0
     hot: int = 0        # number of hot experts (skewed workload)
@@ -86,12 +88,21 @@ WORKLOADS: Dict[str, MoeShape] = {
     "prefill_fp8": MoeShape("prefill_fp8", T=8192, hidden=7168, inter=2048, E=256, K=8,
                             G=8, M=4, topn=2, Ns=1, act="bf16", w="e4m3", bias="zero",
                             compare_rows=512),
+    "prefill_fp8_pow2": MoeShape("prefill_fp8_pow2", T=8192, hidden=7168, inter=2048, E=256,
+                                 K=8, G=8, M=4, topn=2, Ns=1, act="bf16", w="e4m3_pow2",
+                                 bias="zero", compare_rows=512),
     "skewed_bf16": MoeShape("skewed_bf16", T=16384, hidden=7168, inter=2048, E=256, K=8,
                             G=8, M=4, topn=2, Ns=1, act="bf16", w="bf16", bias="zero",
                             hot=8, hot_offset=2.0, steps=50, gamma=1e-3, compare_rows=512),
 }
 
-_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
+           "e4m3_pow2": torch.float8_e4m3fn}
+
+
+def is_fp8(w: str) -> bool:
+    """Expert weights stored as e4m3 codes with 128x128 block scales."""
+    return w in ("e4m3", "e4m3_pow2")
 FP8_CODE_STD = 100.0   # std of the values whose e4m3 cast gives the stored codes
 
 
@@ -157,12 +168,14 @@ def _expert_matrix(cfg: MoeShape, name: str, e: int, rows: int, cols: int, devic
     case it is the fp32 block-scale grid [rows/128, cols/128].
     """
     seed = tensor_seed(cfg.seed, name, e)
-    if cfg.w != "e4m3":
+    if not is_fp8(cfg.w):
         return _normal((rows, cols), 0.02, seed, device, _DTYPES[cfg.w]), None
     v = _normal((rows, cols), FP8_CODE_STD, seed, device, torch.float32)
     codes = v.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
     s = _uniform((rows // 128, cols // 128), 0.5, 1.5, tensor_seed(cfg.seed, name + "/scale", e),
                  device).mul_(0.02 / FP8_CODE_STD)
+    if cfg.w == "e4m3_pow2":          # stored scales are powers of two: 2^-13 or 2^-12
+        s = torch.exp2(torch.floor(torch.log2(s)))
     return codes, s
 
 
@@ -183,7 +196,7 @@ def make_layer_inputs(cfg: MoeShape, device="cpu", step: int = 0) -> dict:
         "w_up": torch.empty((n_exp, cfg.inter, cfg.hidden), dtype=wdt, device=device),
         "w_down": torch.empty((n_exp, cfg.hidden, cfg.inter), dtype=wdt, device=device),
     }
-    if cfg.w == "e4m3":
+    if is_fp8(cfg.w):
         out["s_gate"] = torch.empty((n_exp, cfg.inter // 128, cfg.hidden // 128),
                                     dtype=torch.float32, device=device)
         out["s_up"] = torch.empty_like(out["s_gate"])
