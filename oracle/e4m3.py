@@ -18,7 +18,8 @@ Readings (listed in the design notes):
     the oracle computes it as the exact product of dequantised values.
   * power-of-two variant (scales an 8-bit exponent, E8M0, can hold; the pages give the
     block shapes, not the scale encoding): s = the smallest power of two with
-    amax <= 448 * s (1 when amax == 0); codes as above, the quotient x / s being exact.
+    amax <= 448 * s, at least 2^-126 (1 when amax == 0); codes as above, the quotient
+    x / s being exact.
     Weight block scales of this variant are powers of two as stored.
 """
 from __future__ import annotations
@@ -85,14 +86,14 @@ def quantize_1x128(x):
 
 
 def pow2_scale(amax) -> np.ndarray:
-    """Smallest power of two s with amax <= 448 s (s = 1 for amax == 0), exact.
+    """Smallest power of two s >= 2^-126 with amax <= 448 s (s = 1 for amax == 0), exact.
 
     With amax = m 2^E, m in [0.5, 1): 448 = 0.875 2^9, so s = 2^(E-9) when m <= 0.875 and
-    2^(E-8) otherwise.  Returned as float32 (every such power is a normal float32 for
-    float32 inputs below 448 * 2^127)."""
+    2^(E-8) otherwise.  The floor 2^-126 keeps s a normal float32 (its exponent field
+    is then its 8-bit exponent code).  Returned as float32."""
     a = np.asarray(amax, np.float64)
     m, e = np.frexp(a)
-    s = np.ldexp(1.0, np.where(m <= 0.875, e - 9, e - 8))
+    s = np.ldexp(1.0, np.maximum(np.where(m <= 0.875, e - 9, e - 8), -126))
     return np.where(a > 0, s, 1.0).astype(np.float32)
 
 
