@@ -427,18 +427,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       }
       // bf16 outputs go through LDS: each wave writes one 32-row block at a time into
       // its own 10 KB of A buffer 1 (8-byte writes of four adjacent columns), then reads
-      // whole rows back 16 bytes per lane and stores them with full-line 16-byte global
+      // whole rows back 16 bytes per lane and stores them with full-line 16-byte buffer
       // stores.  A staging row of P bytes has P / 16 chunks; chunk c of row r sits in
-      // slot c ^ ((r / (256 / P)) % (P / 16)) and its 8-byte halves are swapped when bit
-      // 4 of r is set: the 32 lanes of a half-wave write 32 distinct bank pairs, and
-      // every 16-lane quarter of a read covers the 64 banks once.
+      // slot c ^ ((r / (256 / P)) % (P / 16)): every 16-lane quarter of a read covers the
+      // 64 banks once, a half-wave's writes hit each bank pair at most twice.  The store
+      // buffer spans the tile's valid rows, so stores of rows past them are dropped by
+      // the hardware's range check; columns past N get an offset past the range.
       char* const stg = reinterpret_cast<char*>(lds) + kAOff + ASTAGE + w * 10240;
-      uint16_t* const cout = static_cast<uint16_t*>(a.C);
+      const uint32_t ldc2 = uint32_t(a.ldc) * 2u;
+      const __amdgpu_buffer_rsrc_t rsrc_c =
+          make_rsrc(static_cast<uint16_t*>(a.C) + size_t(m0) * a.ldc, uint32_t(mvalid) * ldc2);
       auto pack = [](float x0, float x1) __attribute__((always_inline)) { return pack_bf16x2(x0, x1); };
       // this lane's write slot base for pitch P: row lr, chunk 0, half lh
       auto wslot = [&](auto p_tag) __attribute__((always_inline)) {
         constexpr int P = decltype(p_tag)::value, CH = P / 16, RPB = 256 / P;
-        return uint32_t(lr * P + (((lr / RPB) % CH) << 4) + ((lh ^ ((lr >> 4) & 1)) << 3));
+        return uint32_t(lr * P + (((lr / RPB) % CH) << 4) + (lh << 3));
       };
       auto put8 = [&](uint32_t slot8, int c, uint32_t lo, uint32_t hi) __attribute__((always_inline)) {
         *reinterpret_cast<uint2*>(stg + (slot8 ^ uint32_t(c << 4))) = make_uint2(lo, hi);
@@ -450,6 +453,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
         constexpr int NQ = 32 / RPI, QG = NQ < 4 ? NQ : 4;   // reads in flight per group
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int c = le % CH, col = cb + 8 * c;
+        const uint32_t voff = col < a.N ? (uint32_t(rb + le / CH) * uint32_t(a.ldc) + uint32_t(col)) * 2u : kOob;
 #pragma unroll
         for (int q0 = 0; q0 < NQ; q0 += QG) {
           if (q0 * RPI >= vrows) break;
@@ -460,12 +464,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
             v[u] = *reinterpret_cast<const uint4*>(stg + r * P + ((c ^ ((r / RPB) % CH)) << 4));
           }
 #pragma unroll
-          for (int u = 0; u < QG; ++u) {
-            const int r = (q0 + u) * RPI + le / CH;
-            if ((r >> 4) & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
-            if (r < vrows && col < a.N)
-              *reinterpret_cast<uint4*>(cout + size_t(m0 + rb + r) * a.ldc + col) = v[u];
-          }
+          for (int u = 0; u < QG; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v[u]), rsrc_c, voff,
+                                                   uint32_t((q0 + u) * RPI) * ldc2, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
