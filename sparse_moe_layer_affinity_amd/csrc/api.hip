@@ -37,6 +37,7 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   w.h_scales = fp8 ? static_cast<float*>(take(rows * (I / 128) * 4)) : nullptr;
   w.xq = fp8 ? static_cast<uint8_t*>(take(T * H)) : nullptr;
   w.x_scales = fp8 ? static_cast<float*>(take(T * (H / 128) * 4)) : nullptr;
+  w.xg_scales = fp8 ? static_cast<float*>(take(rows * (H / 128) * 4)) : nullptr;
   w.y_rows = take(rows * H * act_bytes(c));
   w.bytes = off;
   return w;

@@ -32,7 +32,7 @@ namespace moe {
 
 struct Fp8Args {
   const uint8_t* A;          // e4m3 activations: xq [T, K] (gather) or hq [rows, K]
-  const float* a_scales;     // [K/128, a_rows] (transposed)
+  const float* a_scales;     // [K/128, scale_rows] (transposed), in the GEMM's row order
   const int32_t* row_token;  // gather map of routed rows (gather only)
   const int4* sched;         // row blocks {group, first row, rows}, largest first
   const int32_t* sched_n;    // number of row blocks
@@ -48,6 +48,7 @@ struct Fp8Args {
   int n_tiles;
   int gather;
   int a_rows;
+  int scale_rows;            // rows of a_scales (the grouped rows)
 };
 
 // POW2: every block scale is a power of two; the MFMAs apply them in block-scaled mode
@@ -118,16 +119,16 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   __amdgpu_buffer_rsrc_t rsrc_s;
   uint32_t voff_s = kOob;
   if (w < 5) {
-    rsrc_s = make_rsrc(a.a_scales, uint32_t(a.a_rows) * KBLK * 4u);
+    rsrc_s = make_rsrc(a.a_scales, uint32_t(a.scale_rows) * KBLK * 4u);
     const int row = 64 * w + l;
-    if (row < mvalid) voff_s = uint32_t(src_of(row)) * 4u;
+    if (row < mvalid) voff_s = uint32_t(m0 + row) * 4u;
   } else {
     const bool sup = MODE == kGatedBf16 && w == 6;
     rsrc_s = make_rsrc((sup ? a.S1 : a.S0) + size_t(g) * a.s_stride, uint32_t(a.s_stride) * 4u);
     if (l == 0 && (w == 5 || sup)) voff_s = uint32_t((n0 / 128) * KBLK) * 4u;
   }
-  // K block ks of the scales: token scales [K/128, a_rows], weight scales [.., K/128]
-  const uint32_t s_step = w < 5 ? uint32_t(a.a_rows) * 4u : 4u;
+  // K block ks of the scales: token scales [K/128, scale_rows], weight scales [.., K/128]
+  const uint32_t s_step = w < 5 ? uint32_t(a.scale_rows) * 4u : 4u;
   const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
   const uint32_t wave_w = lds_base + kWOff + uint32_t(w) * (WSTAGE / 8);
   const uint32_t wave_t = lds_base + kTOff + uint32_t(w) * (TSTAGE / 8);
@@ -333,12 +334,15 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   const bool pow2 = c.w_dtype == MOE_E4M3_POW2;
   hipError_t err = launch_act_quant(x, T, H, ws.xq, ws.x_scales, s, true, pow2);
   if (err != hipSuccess) return err;
+  // the x scales in grouped-row order, so each stage's scale loads are contiguous
+  err = launch_gather_scales(c, ws.x_scales, row_token, H / 128, ws.xg_scales, s);
+  if (err != hipSuccess) return err;
   err = launch_build_schedule(c, offsets, kFp8BT, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
   const int rounds = ceil_div(expert_row_blocks_upper(c, kFp8BT), kXcds);
   Fp8Args a{};
   a.A = ws.xq;
-  a.a_scales = ws.x_scales;
+  a.a_scales = ws.xg_scales;
   a.row_token = row_token;
   a.sched = ws.sched;
   a.sched_n = ws.sched_n;
@@ -357,6 +361,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.n_tiles = ceil_div(I, 64);
   a.gather = 1;
   a.a_rows = T;
+  a.scale_rows = rows;
   if (pow2)
     hipLaunchKernelGGL((grouped_gemm_fp8<kGatedBf16, true>), dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
   else
@@ -369,6 +374,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.row_token = nullptr;
   d.gather = 0;
   d.a_rows = rows;
+  d.scale_rows = rows;
   d.B0 = static_cast<const uint8_t*>(w.w_down);
   d.B1 = nullptr;
   d.S0 = w.s_down;

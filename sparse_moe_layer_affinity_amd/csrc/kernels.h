@@ -20,6 +20,7 @@ struct Workspace {
   float* h_scales;     // [inter/128, rows] (e4m3 weights; transposed)
   uint8_t* xq;         // [T, hidden] e4m3 codes
   float* x_scales;     // [hidden/128, T] (transposed)
+  float* xg_scales;    // [hidden/128, rows] x_scales in grouped-row order
   void* y_rows;        // [rows, hidden] act dtype (layer forward)
   size_t bytes;        // total bytes of the layout
 };
@@ -79,6 +80,8 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
 hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int32_t* offsets,
                                   const int32_t* row_token, const moe_expert_weights& w,
                                   void* y_rows, const Workspace& ws, hipStream_t s);
+hipError_t launch_gather_scales(const moe_config& c, const float* scales, const int32_t* row_token,
+                                int kblocks, float* out, hipStream_t s);
 hipError_t launch_combine(const moe_config& c, const void* y_rows, const int32_t* pair_row,
                           const float* gate, const void* residual, void* y, hipStream_t s);
 hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float gamma,

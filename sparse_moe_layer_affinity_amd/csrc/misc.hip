@@ -87,6 +87,27 @@ hipError_t launch_combine(const moe_config& c, const void* y_rows, const int32_t
   return hipGetLastError();
 }
 
+// ---- scale gather: [kblocks, T] token-order scales to grouped-row order -------
+// out[kb, r] = scales[kb, token of r]: routed rows (below T*K) through row_token, the
+// shared experts' rows in token order.
+__global__ __launch_bounds__(256) void gather_scales(const float* __restrict__ scales,
+                                                     const int32_t* __restrict__ row_token,
+                                                     int T, int TK, int rows,
+                                                     float* __restrict__ out) {
+  const int r = blockIdx.x * 256 + threadIdx.x, kb = blockIdx.y;
+  if (r >= rows) return;
+  const int t = r < TK ? row_token[r] : (r - TK) % T;
+  out[size_t(kb) * rows + r] = scales[size_t(kb) * T + t];
+}
+
+hipError_t launch_gather_scales(const moe_config& c, const float* scales, const int32_t* row_token,
+                                int kblocks, float* out, hipStream_t s) {
+  const int T = c.num_tokens, TK = T * c.top_k, rows = TK + T * c.num_shared;
+  hipLaunchKernelGGL(gather_scales, dim3(unsigned(ceil_div(rows, 256)), unsigned(kblocks)), dim3(256),
+                     0, s, scales, row_token, T, TK, rows, out);
+  return hipGetLastError();
+}
+
 // ---- bias update ("深度解读报告" section 2.3) ---------------------------------
 // Mean load is T*K/E; compared in integers.  Plain fp32 add / subtract.
 __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ load,
