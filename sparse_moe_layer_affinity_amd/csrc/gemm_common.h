@@ -26,6 +26,28 @@ struct GemmArgs {
   long long c_split_stride;  // split-K: elements between the partial outputs
 };
 
+// Arguments of the FP8 expert GEMMs (e4m3 operands, 128x128 / 1x128 block scales).
+struct Fp8Args {
+  const uint8_t* A;          // e4m3 activations: xq [T, K] (gather) or hq [rows, K]
+  const float* a_scales;     // [K/128, scale_rows] (transposed), in the GEMM's row order
+  const int32_t* row_token;  // gather map of routed rows (gather only)
+  const int4* sched;         // row blocks {group, first row, rows}, largest first
+  const int32_t* sched_n;    // number of row blocks
+  const uint8_t* B0;         // e4m3 weights [G][N][K] (GEMM1: gate)
+  const uint8_t* B1;         // GEMM1: up
+  const float* S0;           // weight block scales [G][N/128][K/128] (GEMM1: gate)
+  const float* S1;           // GEMM1: up
+  long long b_stride;        // bytes per expert (N*K)
+  long long s_stride;        // floats per expert
+  uint16_t* C;               // bf16 output [rows, ldc]
+  int ldc, N, K;
+  int T, TK;
+  int n_tiles;
+  int gather;
+  int a_rows;
+  int scale_rows;            // rows of a_scales (the grouped rows)
+};
+
 enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };
 
 

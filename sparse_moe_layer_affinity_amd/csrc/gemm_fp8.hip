@@ -30,31 +30,8 @@
 
 namespace moe {
 
-struct Fp8Args {
-  const uint8_t* A;          // e4m3 activations: xq [T, K] (gather) or hq [rows, K]
-  const float* a_scales;     // [K/128, scale_rows] (transposed), in the GEMM's row order
-  const int32_t* row_token;  // gather map of routed rows (gather only)
-  const int4* sched;         // row blocks {group, first row, rows}, largest first
-  const int32_t* sched_n;    // number of row blocks
-  const uint8_t* B0;         // e4m3 weights [G][N][K] (GEMM1: gate)
-  const uint8_t* B1;         // GEMM1: up
-  const float* S0;           // weight block scales [G][N/128][K/128] (GEMM1: gate)
-  const float* S1;           // GEMM1: up
-  long long b_stride;        // bytes per expert (N*K)
-  long long s_stride;        // floats per expert
-  uint16_t* C;               // bf16 output [rows, ldc]
-  int ldc, N, K;
-  int T, TK;
-  int n_tiles;
-  int gather;
-  int a_rows;
-  int scale_rows;            // rows of a_scales (the grouped rows)
-};
 
-// POW2: every block scale is a power of two; the MFMAs apply them in block-scaled mode
-// (an 8-bit exponent per lane for the 32 K values it supplies; all four 32-wide parts of
-// a 128-wide block carry the same one) and accumulate in place: no rescale on the VALU.
-template <int MODE, bool POW2>
+template <int MODE>
 __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
   constexpr int BW = 128, BT = kFp8BT, ROWB = 128;
   constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 16 KB, 40 KB
@@ -198,9 +175,6 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     const int nk = KBLK;
     i32x8_t tf[2][NJB > 0 ? NJB : 1];
     float s[2][2][NJB > 0 ? NJB : 1];                    // per set: s_a * s_w per weight half
-    int ea[2][NJB > 0 ? NJB : 1], ew[2][2];              // POW2: exponent codes (4 copies)
-    // 8-bit exponent code of a power-of-two float32, in every byte of the operand
-    auto e8 = [](float v) { return int(((__float_as_uint(v) >> 23) & 0xffu) * 0x01010101u); };
     auto read_tokens = [&](auto set_tag, int ks) __attribute__((always_inline)) {
       constexpr int S = decltype(set_tag)::value;
       const uint32_t tp = uint32_t(ks & 1);
@@ -209,19 +183,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
         tf[S][jb] = lds_frag(kTOff + tp * TSTAGE + uint32_t(t_row + 16 * jb) * ROWB);
       const float s_w0 = lds_f32(kSwOff + tp * kSwStage);
       const float s_w1 = MODE == kGatedBf16 ? lds_f32(kSwOff + tp * kSwStage + 256u) : s_w0;
-      if constexpr (POW2) {
-        ew[S][0] = e8(s_w0);
-        ew[S][1] = e8(s_w1);
-      }
   #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const float s_a = lds_f32(kSaOff + tp * kSaStage + uint32_t(t_row + 16 * jb) * 4u);
-        if constexpr (POW2) {
-          ea[S][jb] = e8(s_a);
-        } else {
-          s[S][0][jb] = s_a * s_w0;
-          s[S][1][jb] = s_a * s_w1;
-        }
+        s[S][0][jb] = s_a * s_w0;
+        s[S][1][jb] = s_a * s_w1;
       }
     };
     // weight block ib of stage ks against the stage's tokens (register set S); each
@@ -234,15 +200,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
         const int h = (MODE == kGatedBf16 && ib >= 2) ? 1 : 0;
   #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-          if constexpr (POW2) {
-            acc[ib][jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                wf, tf[S][jb], acc[ib][jb], 0, 0, 0, ew[S][h], 0, ea[S][jb]);
-          } else {
-            const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                wf, tf[S][jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf, tf[S][jb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
   #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[S][h][jb], acc[ib][jb][q]);
-          }
+          for (int q = 0; q < 4; ++q) acc[ib][jb][q] = fmaf(p[q], s[S][h][jb], acc[ib][jb][q]);
         }
       }
     };
@@ -325,6 +286,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
 hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int4* sched,
                                  int32_t* sched_n, hipStream_t s);
 
+// the power-of-two-scale kernel (gemm_fp8p2.hip): 256 weight rows x 320 tokens per tile
+hipError_t launch_gemm_fp8p2(const Fp8Args& a, bool gated, int n_tiles_blocks, hipStream_t s);
+
 hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int32_t* offsets,
                                   const int32_t* row_token, const moe_expert_weights& w,
                                   void* y_rows, const Workspace& ws, hipStream_t s) {
@@ -362,10 +326,14 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.gather = 1;
   a.a_rows = T;
   a.scale_rows = rows;
-  if (pow2)
-    hipLaunchKernelGGL((grouped_gemm_fp8<kGatedBf16, true>), dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((grouped_gemm_fp8<kGatedBf16, false>), dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
+  if (pow2) {
+    Fp8Args p = a;
+    p.n_tiles = ceil_div(I, 128);
+    err = launch_gemm_fp8p2(p, true, rounds * kXcds * p.n_tiles, s);
+    if (err != hipSuccess) return err;
+  } else {
+    hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
+  }
   err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true, pow2);
   if (err != hipSuccess) return err;
   Fp8Args d = a;
@@ -386,10 +354,12 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.N = H;
   d.K = I;
   d.n_tiles = ceil_div(H, 128);
-  if (pow2)
-    hipLaunchKernelGGL((grouped_gemm_fp8<kPlainBf16, true>), dim3(rounds * kXcds * d.n_tiles), dim3(512), 0, s, d);
-  else
-    hipLaunchKernelGGL((grouped_gemm_fp8<kPlainBf16, false>), dim3(rounds * kXcds * d.n_tiles), dim3(512), 0, s, d);
+  if (pow2) {
+    Fp8Args p = d;
+    p.n_tiles = ceil_div(H, 256);
+    return launch_gemm_fp8p2(p, false, rounds * kXcds * p.n_tiles, s);
+  }
+  hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512), 0, s, d);
   return hipGetLastError();
 }
 
