@@ -123,6 +123,10 @@ def test_weight_scale_pointer_rules():
         B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_grouped_ffn, cfg(w="e4m3"), A, A, A, dense, A, A, need8, stream=0) == \
         B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_grouped_ffn, cfg(w="e4m3_pow2"), A, A, A, dense, A, A, need8,
+                   stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_grouped_ffn, cfg(w="e4m3_pow2"), A, A, A, dict(scaled, s_up=0), A, A, need8,
+                   stream=0) == B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_grouped_ffn, cfg(), A, A, A, dict(dense, w_up=0), A, A, need8,
                    stream=0) == B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_layer_forward, cfg(), A, A, A, dense, None, A, A, A, 0, A, need8,
