@@ -27,8 +27,9 @@
  *    error nothing is enqueued.  Return codes only (no global error state);
  *    moe_status_string() names a code.  MOE_ERR_HIP reports a failed launch;
  *    faults inside kernels surface at the caller's next synchronisation.
- *  - Calls are thread-safe (no mutable global state).  Results are
- *    deterministic: no floating-point atomics and no split-K anywhere.
+ *  - Calls are thread-safe (the only global state is a per-device cache of the
+ *    CU count, stored atomically).  Results are deterministic: no floating-point
+ *    atomics; the router's split-K partials are summed in a fixed order.
  *  - Row-major layouts throughout.  Experts are stacked routed-first: experts
  *    0..E-1 are routed, E..E+Ns-1 are the shared experts.
  *

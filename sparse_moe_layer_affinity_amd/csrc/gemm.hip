@@ -17,6 +17,7 @@
 // SwiGLU epilogue runs in registers; accumulation is fp32.
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -731,17 +732,22 @@ hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, in
 }
 
 // Workgroups resident at once (one per CU: the expert GEMMs take 144 KB of LDS), a
-// multiple of the XCD count.
+// multiple of the XCD count.  Cached per device; concurrent first calls store the same
+// value.
 static int resident_workgroups() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  const bool cacheable = dev >= 0 && dev < 64;
+  if (cacheable) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
   n = n / kXcds * kXcds;
   if (n < kXcds) n = kXcds;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (cacheable) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
