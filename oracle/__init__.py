@@ -31,13 +31,20 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   quantize_1x128_pow2      float32 sweep against an integer-exponent search), hand
                    values (448 -> 1, 449 -> 2, 1 -> 2^-8), blocks of e4m3 values times
                    a power of two quantise exactly, the half-step bound
+  balance_loss /   formula is a reading (the pages name the sequence-wise loss but
+  balance_loss_    print no formula): pinned by hand-computed cases, the closed
+  grad_logits      forms of perfect balance, uniform affinities and full
+                   concentration, sum f = E and sum P = 1, relabelling and
+                   per-sequence locality, and central finite differences
 """
 from .moe_layer import (RouteResult, affinities, route, permute, expert_ffn, layer_output,
                         bias_update, silu)
+from .balance import balance_loss, balance_loss_grad_logits
 from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128,
                    dequantize_blocks_128, expert_ffn_fp8_emulated, pow2_scale,
                    quantize_1x128_pow2, expert_ffn_fp8_pow2_emulated)
 
 __all__ = ["RouteResult", "affinities", "route", "permute", "expert_ffn", "layer_output",
            "bias_update", "silu", "e4m3_table", "e4m3_encode_rne", "quantize_1x128",
-           "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated"]
+           "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated",
+           "balance_loss", "balance_loss_grad_logits"]
