@@ -164,6 +164,39 @@ moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t*
 moe_status moe_bias_update(const moe_config* cfg, const int32_t* expert_load, float gamma,
                            float* bias, void* stream);
 
+/* Router affinities ("深度解读报告" section 2.2): for every token t and expert e
+ *   scores[t, e] = sigmoid(<x_t, w_router[e]>)     (fp32)
+ * bit-identical to the affinities moe_route selects on (same logits, same
+ * summation order, same sigmoid).  x [T, hidden] act_dtype; w_router [E, hidden]
+ * act_dtype; scores [T, E] fp32 out.  The input of moe_balance_loss. */
+moe_status moe_router_scores(const moe_config* cfg, const void* x, const void* w_router,
+                             float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* Sequence-wise balance loss ("深度解读报告" section 2.3: beside the bias rule, a
+ * sequence-level balance loss L_Bal with a very small coefficient alpha; section 4.4
+ * compares sequence-wise with batch-wise auxiliary losses).  The pages print no
+ * formula; this is the usual form.  Tokens [q*seq_len, (q+1)*seq_len) form
+ * sequence q; for each q and expert e
+ *   s'_{t,e} = scores[t, e] / sum_j scores[t, j]
+ *   f_e = E / (K * seq_len) * #{t in q : e in topk_idx[t, :]}
+ *   P_e = (1 / seq_len) * sum_{t in q} s'_{t,e}
+ *   seq_loss[q] = alpha * sum_e f_e P_e
+ * seq_len = T gives the batch-wise variant (the step's batch as one sequence).
+ * scores [T, E] fp32 (moe_router_scores); topk_idx [T, K] int32 (moe_route;
+ * entries outside [0, E) are not counted); seq_loss [T/seq_len] fp32 out;
+ * expert_frac [T/seq_len, E] fp32 out (f; nullable); expert_prob [T/seq_len, E]
+ * fp32 out (P; nullable); grad_logits [T, E] fp32 out (nullable): the gradient of
+ * sum_q seq_loss[q] with respect to the router logits z (scores = sigmoid(z)) with
+ * the selection held fixed (it is piecewise constant in z):
+ *   alpha / seq_len * (f_e - sum_i f_i s'_{t,i}) / sum_j scores[t, j]
+ *     * scores[t, e] * (1 - scores[t, e]).
+ * seq_len >= 1 must divide T; alpha >= 0 and finite.  Every sum runs in a fixed
+ * order (deterministic). */
+moe_status moe_balance_loss(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
+                            int32_t seq_len, float alpha, float* seq_loss, float* expert_frac,
+                            float* expert_prob, float* grad_logits, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.
  * residual (nullable) is u of "out = u + ..." in section 2.2; NULL gives the MoE

@@ -55,6 +55,9 @@ _SIGS = {
     "moe_bias_update": (ctypes.c_int, [_CFG, _P, ctypes.c_float, _P, _P]),
     "moe_layer_forward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.POINTER(MoeExpertWeights), _P,
                                          _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_router_scores": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_balance_loss": (ctypes.c_int, [_CFG, _P, _P, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
+                                        _P, _P, ctypes.c_size_t, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -181,6 +184,23 @@ def moe_layer_forward(cfg, x, w_router, bias, weights: dict, residual, y, topk_i
         ctypes.byref(w), _dev(residual, "residual", True), _dev(y, "y"),
         _dev(topk_idx, "topk_idx"), _dev(topk_gate, "topk_gate"),
         _dev(expert_load, "expert_load"), _dev(ws, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_router_scores(cfg, x, w_router, scores, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_router_scores", lib().moe_router_scores(
+        ctypes.byref(cfg), _dev(x, "x"), _dev(w_router, "w_router"), _dev(scores, "scores"),
+        _dev(ws, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_balance_loss(cfg, scores, topk_idx, seq_len, alpha, seq_loss, expert_frac, expert_prob,
+                     grad_logits, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_balance_loss", lib().moe_balance_loss(
+        ctypes.byref(cfg), _dev(scores, "scores"), _dev(topk_idx, "topk_idx"), int(seq_len),
+        float(alpha), _dev(seq_loss, "seq_loss"), _dev(expert_frac, "expert_frac", True),
+        _dev(expert_prob, "expert_prob", True), _dev(grad_logits, "grad_logits", True),
+        _dev(ws, "ws"), ws_bytes, _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

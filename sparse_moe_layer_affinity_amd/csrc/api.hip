@@ -39,6 +39,9 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   w.x_scales = fp8 ? static_cast<float*>(take(T * (H / 128) * 4)) : nullptr;
   w.xg_scales = fp8 ? static_cast<float*>(take(rows * (H / 128) * 4)) : nullptr;
   w.y_rows = take(rows * H * act_bytes(c));
+  w.bal_p = static_cast<float*>(take(T * E * 4));
+  w.bal_c = static_cast<int32_t*>(take(T * E * 4));
+  w.bal_f = static_cast<float*>(take(T * E * 4));
   w.bytes = off;
   return w;
 }
@@ -131,6 +134,32 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(from_hip(launch_router_logits(*cfg, x, w_router, w.z, s)));
   return from_hip(launch_router_select(*cfg, w.z, bias, topk_idx, topk_gate, s));
+}
+
+moe_status moe_router_scores(const moe_config* cfg, const void* x, const void* w_router,
+                             float* scores, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  if (!x || !w_router || !scores) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(*cfg, ws, ws_bytes));
+  const Workspace w = workspace_layout(*cfg, ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(from_hip(launch_router_logits(*cfg, x, w_router, w.z, s)));
+  return from_hip(launch_router_scores(*cfg, w.z, scores, s));
+}
+
+moe_status moe_balance_loss(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
+                            int32_t seq_len, float alpha, float* seq_loss, float* expert_frac,
+                            float* expert_prob, float* grad_logits, void* ws, size_t ws_bytes,
+                            void* stream) {
+  MOE_TRY(validate(cfg));
+  if (!scores || !topk_idx || !seq_loss) return MOE_ERR_INVALID_ARGUMENT;
+  if (seq_len < 1 || cfg->num_tokens % seq_len != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(alpha >= 0.0f) || isinf(alpha)) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(*cfg, ws, ws_bytes));
+  const Workspace w = workspace_layout(*cfg, ws);
+  return from_hip(launch_balance_loss(*cfg, scores, topk_idx, seq_len, alpha, seq_loss,
+                                      expert_frac, expert_prob, grad_logits, w,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* expert_load,

@@ -22,6 +22,9 @@ struct Workspace {
   float* x_scales;     // [hidden/128, T] (transposed)
   float* xg_scales;    // [hidden/128, rows] x_scales in grouped-row order
   void* y_rows;        // [rows, hidden] act dtype (layer forward)
+  float* bal_p;        // [chunks <= T, E] balance loss: partial sums of s' per chunk
+  int32_t* bal_c;      // [chunks <= T, E] balance loss: selections per chunk
+  float* bal_f;        // [sequences <= T, E] balance loss: f when the caller keeps none
   size_t bytes;        // total bytes of the layout
 };
 
@@ -72,6 +75,11 @@ hipError_t launch_router_select(const moe_config& c, const float* z, const float
 hipError_t launch_permute(const moe_config& c, const int32_t* idx, int32_t* load,
                           int32_t* offsets, int32_t* row_token, int32_t* pair_row,
                           const Workspace& ws, hipStream_t s);
+hipError_t launch_router_scores(const moe_config& c, const float* z, float* scores,
+                                hipStream_t s);
+hipError_t launch_balance_loss(const moe_config& c, const float* scores, const int32_t* idx,
+                               int seq_len, float alpha, float* loss, float* frac, float* prob,
+                               float* grad, const Workspace& w, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
                             hipStream_t s, bool transposed = false, bool pow2 = false);
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     names = B.header_symbols()
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_act_quant_e4m3",
                           "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
-                          "moe_status_string"}
+                          "moe_router_scores", "moe_balance_loss", "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -111,6 +111,37 @@ def test_null_pointers_and_workspace_checks():
         B.MOE_ERR_INVALID_ARGUMENT                             # cols not a multiple of 128
     assert code_of(B.moe_act_quant_e4m3, cfg(act="f32", w="f32"), A, 4, 128, A, A, stream=0) == \
         B.MOE_ERR_UNSUPPORTED
+
+
+def test_balance_loss_argument_checks():
+    c = cfg()
+    need = moe.moe_workspace_bytes(c)
+    A = ALIGNED
+
+    def loss(seq_len=4096, alpha=1e-4, scores=A, idx=A, out=A, ws_bytes=need, ws=A):
+        return code_of(B.moe_balance_loss, c, scores, idx, seq_len, alpha, out, None, None, None,
+                       ws, ws_bytes, stream=0)
+
+    assert loss(seq_len=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(seq_len=-8) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(seq_len=3000) == B.MOE_ERR_INVALID_ARGUMENT      # does not divide T = 8192
+    assert loss(seq_len=16384) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(alpha=-1e-4) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(alpha=float("nan")) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(alpha=float("inf")) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(scores=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(idx=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(out=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert loss(ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert loss(ws=A + 64) == B.MOE_ERR_INVALID_ARGUMENT          # misaligned workspace
+    assert code_of(B.moe_balance_loss, cfg(E=250), A, A, 10, 1e-4, A, None, None, None, A, need,
+                   stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_router_scores, c, A, A, 0, A, need, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_router_scores, c, 0, A, A, A, need, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_router_scores, c, A, A, A, A, need - 1, stream=0) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_weight_scale_pointer_rules():

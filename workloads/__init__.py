@@ -234,6 +234,12 @@ def make_topk_indices(T: int, E: int, K: int, hot: int = 0, hot_weight: float = 
     return torch.topk(keys, K, dim=1).indices.to(torch.int32)
 
 
+def make_affinities(T: int, E: int, seed: int = 0) -> torch.Tensor:
+    """Seeded [T, E] float32 affinities, uniform in (0.02, 0.98) (a balance-loss-stage
+    input: any values a sigmoid can produce)."""
+    return _uniform((T, E), 0.02, 0.98, tensor_seed(seed, "affinities", T, E), "cpu")
+
+
 def make_loads(E: int, T: int, K: int, seed: int = 0, at_mean: int = 4) -> torch.Tensor:
     """Seeded per-expert loads summing to T*K, the first ``at_mean`` exactly at the mean
     when T*K is a multiple of E (a bias-update-stage input)."""
