@@ -12,7 +12,9 @@ HIP events recorded on the same stream time every stage of every timed step.
 Prints ONE JSON line: layer tokens/s as ``value``, plus the grouped-GEMM TFLOP/s
 and the roofline of the grouped expert GEMM (moe_grouped_ffn: the gated GEMM1 and
 GEMM2 kernels, 99.5% of the layer's FLOPs) and the CPU oracle's rate on a bounded
-sample (``cpu_baseline``).
+sample (``cpu_baseline``).  After the timed steps, and outside them, the
+training-side extras are timed on their own (``balance_loss``): the router
+affinities and the sequence-wise balance loss with its logit gradient.
 """
 from __future__ import annotations
 
@@ -91,6 +93,43 @@ def cpu_baseline(cfg, d, n_tokens: int):
             "sample": f"{n_tokens} seeded tokens of the {cfg.T}-token batch: float64 routing and "
                       f"the full layer output (shared + {cfg.K} routed SwiGLU experts, weights "
                       f"streamed from HBM and widened to float64); {dt:.1f} s"}
+
+
+def balance_loss_leg(moe, cfg, c, d, idx, ws, stream, reps: int = 20):
+    """Time the training-side extras outside the layer step: moe_router_scores and
+    moe_balance_loss (two sequences of T/2 tokens, with f, P and the logit gradient),
+    each over ``reps`` back-to-back calls between HIP events on the bench stream.
+    The loss's algorithmic bytes: affinities and selections read once, the gradient
+    written once, plus the per-sequence f, P and loss."""
+    import torch
+    T, E, K = cfg.T, cfg.E, cfg.K
+    L = T // 2
+    S = T // L
+    scores = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    loss = torch.empty(S, dtype=torch.float32, device="cuda")
+    frac = torch.empty((S, E), dtype=torch.float32, device="cuda")
+    prob = torch.empty((S, E), dtype=torch.float32, device="cuda")
+    grad = torch.empty((T, E), dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    us_scores = timed(lambda: moe.moe_router_scores(c, d["x"], d["w_router"], scores, ws))
+    us_loss = timed(lambda: moe.moe_balance_loss(c, scores, idx, L, 1e-4, loss, frac, prob, grad,
+                                                 ws))
+    nbytes = T * E * 4 + T * K * 4 + T * E * 4 + S * E * 8 + S * 4
+    gbps = nbytes / (us_loss * 1e-6) / 1e9
+    return {"seq_len": L, "alpha": 1e-4, "router_scores_us": round(us_scores, 2),
+            "loss_and_grad_us": round(us_loss, 2), "loss_bytes": nbytes,
+            "loss_GBps": round(gbps, 1), "loss_frac_hbm": round(gbps / HBM_PEAK, 4),
+            "loss_value": [round(float(v), 9) for v in loss.cpu()]}
 
 
 def main():
@@ -215,6 +254,7 @@ def main():
         "max_over_mean_load": round(float(load.max().item()) / (T * K / E), 3),
         "roofline": roof,
     }
+    result["balance_loss"] = balance_loss_leg(moe, cfg, c, d, idx, ws, stream)
     if args.cpu_tokens > 0:
         log(f"[bench] oracle baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_tokens)
