@@ -34,8 +34,8 @@
  *    0..E-1 are routed, E..E+Ns-1 are the shared experts.
  *
  * Supported dtype combinations (act_dtype, w_dtype): (F32, F32), (BF16, BF16),
- * (BF16, E4M3).  Limits: E <= 256, K <= 8, G <= 64; hidden and inter multiples of
- * 128 for BF16/E4M3 weights, of 4 for F32.
+ * (BF16, E4M3), (BF16, E4M3_POW2).  Limits: E <= 256, K <= 8, G <= 64; hidden and
+ * inter multiples of 128 for BF16/E4M3 weights, of 4 for F32.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -2,8 +2,9 @@
 
 moe_router_scores against the float64 affinities of the oracle, and bit-identical
 to the affinities moe_route selected on (its gates are reproduced exactly from
-them).  moe_balance_loss stage-wise on the GPU's own inputs (seeded affinities and
-selections, or the router's own outputs), against the float64 oracle: f within one
+them).  moe_balance_loss on seeded affinities and selections (both sides), and on
+the GPU's own affinities with the oracle's selection against the oracle's own
+affinities, logits and selection, to the float64 oracle's bar: f within one
 rounding, P and the loss within 2e-5 relative, the logit gradient within 2e-5 of
 its largest magnitude (fp32 sums of up to 8192 terms; the gradient's f_e minus
 sum_i f_i s'_i cancels).  Sizes span one chunk, several chunks with a ragged last
@@ -42,17 +43,25 @@ def _run_loss(c, s, idx, L, alpha=ALPHA, ws=None, full=True):
     return {k: v.cpu().double().numpy() for k, v in out.items()}
 
 
-def _check_against_oracle(got, s_cpu, idx_cpu, L, K, alpha=ALPHA):
-    s64 = s_cpu.double().numpy()
-    idx = idx_cpu.numpy()
+def _oracle(s64, z64, idx, L, K, alpha=ALPHA):
     loss, f, P = oracle.balance_loss(s64, idx, L, alpha, K)
-    grad = oracle.balance_loss_grad_logits(_logit(s64), idx, L, alpha, K)
-    np.testing.assert_allclose(got["f"], f, rtol=1e-7, atol=0)
-    np.testing.assert_allclose(got["P"], P, rtol=2e-5, atol=0)
-    np.testing.assert_allclose(got["loss"], loss, rtol=2e-5, atol=0)
-    gerr = np.abs(got["grad"] - grad).max() / np.abs(grad).max()
-    log(f"  loss[0] {got['loss'][0]:.6e} (oracle {loss[0]:.6e}); grad rel err {gerr:.2e}")
+    return {"loss": loss, "f": f, "P": P,
+            "grad": oracle.balance_loss_grad_logits(z64, idx, L, alpha, K)}
+
+
+def _compare(got, want):
+    np.testing.assert_allclose(got["f"], want["f"], rtol=1e-7, atol=0)
+    np.testing.assert_allclose(got["P"], want["P"], rtol=2e-5, atol=0)
+    np.testing.assert_allclose(got["loss"], want["loss"], rtol=2e-5, atol=0)
+    gerr = np.abs(got["grad"] - want["grad"]).max() / np.abs(want["grad"]).max()
+    log(f"  loss[0] {got['loss'][0]:.6e} (oracle {want['loss'][0]:.6e}); grad rel err {gerr:.2e}")
     assert gerr <= 2e-5
+
+
+def _check_against_oracle(got, s_cpu, idx_cpu, L, K):
+    """Both sides on the same seeded generator outputs (affinities, selections)."""
+    s64 = s_cpu.double().numpy()
+    _compare(got, _oracle(s64, _logit(s64), idx_cpu.numpy(), L, K))
 
 
 def _cfg(T, E, K, G):
@@ -130,6 +139,9 @@ def test_out_of_range_selections_are_not_counted():
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_bf16"])
 def test_router_scores_and_loss_on_the_router_outputs(name):
+    """moe_router_scores against the oracle's affinities; then the loss of the whole
+    chain: the GPU on its own affinities with the oracle's selection (an oracle value
+    handed to the GPU), the oracle on its own affinities, logits and selection."""
     cfg = workloads.get(name)
     log(f"router scores + balance loss on {name}")
     c = config_of(cfg)
@@ -144,16 +156,17 @@ def test_router_scores_and_loss_on_the_router_outputs(name):
     moe.moe_route(c, x.cuda(), w_r.cuda(), bias.cuda(), idx, gate, ws)
     torch.cuda.synchronize()
     s = scores.cpu()
-    _, s64 = oracle.affinities(x, w_r)
+    z64, s64 = oracle.affinities(x, w_r)
     err = np.abs(s.double().numpy() - s64).max()
     log(f"  max |s - oracle| = {err:.2e}")
     assert err <= (1e-6 if cfg.act == "f32" else 1e-5)
-    # the gates of moe_route are these very affinities normalised in k order
+    # property: the gates of moe_route are these very affinities normalised in k order
     sel = torch.gather(s, 1, idx.cpu().long())
     total = sel[:, 0].clone()
     for k in range(1, cfg.K):
         total = total + sel[:, k]
     assert torch.equal(gate.cpu(), sel / total[:, None])
+    r = oracle.route(x, w_r, bias.numpy(), cfg.G, cfg.M, cfg.topn, cfg.K)
     L = cfg.T // 2
-    got = _run_loss(c, scores, idx, L, ws=ws)
-    _check_against_oracle(got, s, idx.cpu(), L, cfg.K)
+    got = _run_loss(c, scores, torch.from_numpy(r.idx).cuda(), L, ws=ws)
+    _compare(got, _oracle(s64, z64, r.idx, L, cfg.K))
