@@ -38,12 +38,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the files the counted expert-GEMM kernels are compiled from, and their build flags
+GEMM_SOURCES = ["sparse_moe_layer_affinity_amd/csrc/gemm.hip",
+                "sparse_moe_layer_affinity_amd/csrc/gemm_fp8.hip",
+                "sparse_moe_layer_affinity_amd/csrc/gemm_fp8p2.hip",
+                "sparse_moe_layer_affinity_amd/csrc/gemm_common.h",
+                "sparse_moe_layer_affinity_amd/csrc/kernels.h",
+                "sparse_moe_layer_affinity_amd/csrc/common.h",
+                "include/moe.h",
+                "sparse_moe_layer_affinity_amd/build.py"]
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources, to tell whether stored counter figures still apply."""
+    """Hash of the expert-GEMM kernels' sources, to tell whether stored counter
+    figures of those kernels still apply."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_moe_layer_affinity_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 

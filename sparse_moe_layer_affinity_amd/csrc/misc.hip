@@ -6,7 +6,21 @@ namespace moe {
 // ---- combine ("深度解读报告" section 2.2) -------------------------------------
 // y[t] = [u_t] + sum_s y_rows[shared row of t] + sum_k g_tk * y_rows[pair_row[t,k]],
 // fp32 in that order, one rounding at the end.  One workgroup per token; each
-// thread owns 16-byte column vectors, so every row read is fully coalesced.
+// thread owns 16-byte column vectors, so every row read is fully coalesced.  The
+// token's K routed rows (K <= 8) are loaded together before any is added, so a
+// thread has all its row loads in flight at once; the additions keep the order.
+constexpr int kCombineMaxK = 8;
+
+__device__ __forceinline__ void add_bf16x8(float acc[8], uint4 p, float g, bool scaled) {
+  const uint32_t wds[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_bits_to_f32(wds[i] & 0xffffu), hi = bf16_bits_to_f32(wds[i] >> 16);
+    acc[2 * i] = scaled ? fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
+    acc[2 * i + 1] = scaled ? fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__ y_rows,
                                                     const int32_t* __restrict__ pair_row,
                                                     const float* __restrict__ gate,
@@ -15,27 +29,31 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__
                                                     int Ns, int H) {
   const int t = blockIdx.x;
   const size_t TK = size_t(T) * K;
+  int row[kCombineMaxK];
+  float g[kCombineMaxK];
+#pragma unroll
+  for (int k = 0; k < kCombineMaxK; ++k) {
+    row[k] = k < K ? pair_row[size_t(t) * K + k] : -1;
+    g[k] = k < K ? gate[size_t(t) * K + k] : 0.f;
+  }
   for (int v = threadIdx.x; v < H / 8; v += 256) {
+    const size_t col = size_t(v) * 8;
+    uint4 p[kCombineMaxK];
+#pragma unroll
+    for (int k = 0; k < kCombineMaxK; ++k)
+      if (row[k] >= 0) p[k] = *reinterpret_cast<const uint4*>(y_rows + size_t(row[k]) * H + col);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    auto add = [&](const uint16_t* src, float g, bool scaled) {
-      uint4 p = *reinterpret_cast<const uint4*>(src + size_t(v) * 8);
-      uint32_t wds[4] = {p.x, p.y, p.z, p.w};
+    if (residual)
+      add_bf16x8(acc, *reinterpret_cast<const uint4*>(residual + size_t(t) * H + col), 1.f, false);
+    for (int s = 0; s < Ns; ++s)
+      add_bf16x8(acc, *reinterpret_cast<const uint4*>(y_rows + (TK + size_t(s) * T + t) * H + col),
+                 1.f, false);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float lo = bf16_bits_to_f32(wds[i] & 0xffffu), hi = bf16_bits_to_f32(wds[i] >> 16);
-        acc[2 * i] = scaled ? fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
-        acc[2 * i + 1] = scaled ? fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
-      }
-    };
-    if (residual) add(residual + size_t(t) * H, 1.f, false);
-    for (int s = 0; s < Ns; ++s) add(y_rows + (TK + size_t(s) * T + t) * H, 1.f, false);
-    for (int k = 0; k < K; ++k) {
-      const int r = pair_row[size_t(t) * K + k];
-      if (r >= 0) add(y_rows + size_t(r) * H, gate[size_t(t) * K + k], true);
-    }
-    *reinterpret_cast<uint4*>(y + size_t(t) * H + size_t(v) * 8) =
+    for (int k = 0; k < kCombineMaxK; ++k)
+      if (row[k] >= 0) add_bf16x8(acc, p[k], g[k], true);
+    *reinterpret_cast<uint4*>(y + size_t(t) * H + col) =
         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }

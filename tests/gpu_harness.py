@@ -138,6 +138,6 @@ def rel_err(y, ref):
 
 
 def oracle_layer(cfg, d, idx, gate, rows=None, residual=None):
-    """Oracle output on ``rows`` for the given routing (the GPU's own or the oracle's)."""
+    """Oracle output on ``rows`` for a routing the oracle computed."""
     return oracle.layer_output(d["x"], idx, gate, expert_getter(cfg, d), cfg.E, cfg.Ns,
                                rows=rows, residual=residual)
