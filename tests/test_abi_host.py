@@ -86,6 +86,20 @@ def test_valid_configs_have_workspace():
     assert moe.moe_workspace_bytes(cfg(w="e4m3")) == moe.moe_workspace_bytes(cfg(w="e4m3_pow2"))
 
 
+def test_largest_token_count():
+    # the MFMA kernels address h through 32-bit buffer offsets: 2 * T*(K+Ns) * inter bytes
+    # must not exceed 2^31 - 2^20, so T = 58225 is the largest bf16 batch at this shape
+    lim = (1 << 31) - (1 << 20)
+    t_max = lim // (2 * 9 * 2048)
+    assert t_max == 58225
+    for w in ("bf16", "e4m3", "e4m3_pow2"):
+        assert moe.moe_workspace_bytes(cfg(T=t_max, w=w)) > 0
+        assert moe.moe_workspace_bytes(cfg(T=t_max + 1, w=w)) == 0
+        got = code_of(B.moe_route, cfg(T=t_max + 1, w=w), ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                      ALIGNED, ALIGNED, 1 << 40, stream=0)
+        assert got == B.MOE_ERR_UNSUPPORTED
+
+
 def test_null_pointers_and_workspace_checks():
     c = cfg()
     need = moe.moe_workspace_bytes(c)

@@ -110,3 +110,18 @@ def test_layer_prefill_bf16():
     d = inputs_on_gpu(cfg)
     out = layer_forward(cfg, d)
     _check_layer(cfg, d, out, rows=workloads.sample_rows(cfg.T, cfg.compare_rows).numpy())
+
+
+@pytest.mark.slow
+def test_layer_largest_batch_bf16():
+    """The largest batch the 32-bit buffer offsets allow at the prefill shape (T = 58225,
+    524025 grouped rows): routing on all tokens, output on sampled rows plus the last
+    tokens (the ragged end of the token range and of the shared expert's rows)."""
+    T = 58225
+    cfg = workloads.get("prefill_bf16").replace(T=T)
+    log(f"layer bf16 at the largest batch T={T}")
+    d = inputs_on_gpu(cfg)
+    out = layer_forward(cfg, d)
+    rows = np.union1d(workloads.sample_rows(T, 96, seed=3).numpy(), np.arange(T - 8, T))
+    _check_layer(cfg, d, out, rows=rows)
+
