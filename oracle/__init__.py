@@ -36,9 +36,15 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   grad_logits      forms of perfect balance, uniform affinities and full
                    concentration, sum f = E and sum P = 1, relabelling and
                    per-sequence locality, and central finite differences
+  combine_backward pinned: the adjoint identity of the combine (linear in the rows
+                   and in the gates), a hand-computed case
+  gate_backward    pinned: central finite differences of the gates, a hand-computed
+                   case, zero gradient for a dgate equal over the selection and for
+                   unselected experts
 """
 from .moe_layer import (RouteResult, affinities, route, permute, expert_ffn, layer_output,
                         bias_update, silu)
+from .backward import combine_backward, gate_backward
 from .balance import balance_loss, balance_loss_grad_logits
 from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128,
                    dequantize_blocks_128, expert_ffn_fp8_emulated, pow2_scale,
@@ -47,4 +53,4 @@ from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128
 __all__ = ["RouteResult", "affinities", "route", "permute", "expert_ffn", "layer_output",
            "bias_update", "silu", "e4m3_table", "e4m3_encode_rne", "quantize_1x128",
            "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated",
-           "balance_loss", "balance_loss_grad_logits"]
+           "balance_loss", "balance_loss_grad_logits", "combine_backward", "gate_backward"]

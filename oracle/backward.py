@@ -1,0 +1,73 @@
+"""Plain float64 oracle of the combine and gate backward (test infrastructure only).
+
+Source (the pages): "DeepSeek-V3 Technical Report 深度解读报告", section 2.2: the
+layer output is the token's input plus the shared experts' outputs plus the routed
+experts' outputs weighted by gates g_k = s_k / sum_j s_j (s the sigmoid affinities
+of the selected experts); section 2.3: the bias b only decides the selection and
+does not enter the gates.  The backward is the adjoint of these formulas (the pages
+state no backward; differentiating them is the plain reading):
+
+  combine      y_t = [u_t] + sum_s Y[shared row of t] + sum_k g_tk Y[pair_row(t, k)]
+  adjoint      dg_tk = <dy_t, Y[pair_row(t, k)]>
+               dY[pair_row(t, k)] = g_tk dy_t ;  dY[shared row of t] = dy_t
+  gates        g_k = s_k / S,  S = sum_j s_{idx_j}
+               dL/ds_j = (dg_j - sum_k dg_k g_k) / S     for the selected j, 0 elsewhere
+               dL/dz_j = dL/ds_j * s_j (1 - s_j)          (s = sigmoid(z))
+  bias         no gradient: the selection is piecewise constant in b.
+
+Parity status: pinned by mathematics.  The combine adjoint by the adjoint identity
+<dy, C(Y, g)> = <dY, Y> + <dg, g> (C is linear in Y for fixed g and in g for fixed Y)
+and by a hand-computed case; the gate backward by central finite differences of the
+gates, a hand-computed case, and a closed form (a dg equal over k gives no gradient,
+because the gates sum to one).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        return a.detach().to("cpu").double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def combine_backward(dy, y_rows, pair_row, gate, num_tokens: int, top_k: int,
+                     num_shared: int):
+    """Adjoint of the combine.  dy [T, h]; y_rows [T*K + T*Ns, h] (routed rows, then
+    each shared expert's T rows in token order); pair_row [T*K]; gate [T, K].
+    Returns (dgate [T, K], dy_rows [T*K + T*Ns, h]) in float64."""
+    dy = _f64(dy)
+    Y = _f64(y_rows)
+    g = _f64(gate)
+    pair_row = np.asarray(pair_row, dtype=np.int64)
+    T, K, Ns = num_tokens, top_k, num_shared
+    TK = T * K
+    dgate = np.zeros((T, K))
+    dY = np.zeros_like(Y)
+    for t in range(T):
+        for k in range(K):
+            r = pair_row[t * K + k]
+            dgate[t, k] = np.dot(dy[t], Y[r])
+            dY[r] = g[t, k] * dy[t]
+        for s in range(Ns):
+            dY[TK + s * T + t] = dy[t]
+    return dgate, dY
+
+
+def gate_backward(z, idx, dgate) -> np.ndarray:
+    """Gradient with respect to the router logits z [T, E] of a loss whose gradient
+    with respect to the gates is dgate [T, K], the selection idx [T, K] held fixed."""
+    z = _f64(z)
+    s = 1.0 / (1.0 + np.exp(-z))
+    idx = np.asarray(idx, dtype=np.int64)
+    dg = _f64(dgate)
+    T, _ = z.shape
+    grad = np.zeros_like(z)
+    for t in range(T):
+        sel = s[t, idx[t]]
+        total = sel.sum()
+        g = sel / total
+        ds = (dg[t] - np.dot(dg[t], g)) / total
+        grad[t, idx[t]] = ds * sel * (1.0 - sel)
+    return grad

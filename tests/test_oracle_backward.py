@@ -1,0 +1,94 @@
+"""Pins for the combine and gate backward oracle (mathematics: the pages state the
+forward formulas only)."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _combine(Y, g, pair_row, T, K, Ns):
+    """The forward combine written as plain loops (the map whose adjoint is pinned)."""
+    out = np.zeros((T, Y.shape[1]))
+    for t in range(T):
+        for s in range(Ns):
+            out[t] += Y[T * K + s * T + t]
+        for k in range(K):
+            out[t] += g[t, k] * Y[pair_row[t * K + k]]
+    return out
+
+
+def _case(seed, T=7, K=3, Ns=2, E=8, h=5):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    _, _, _, pair_row = oracle.permute(idx, E)
+    rows = T * K + T * Ns
+    return (rng.normal(size=(T, h)), rng.normal(size=(rows, h)), pair_row,
+            rng.uniform(0.05, 1, size=(T, K)))
+
+
+@pytest.mark.parametrize("seed,Ns", [(0, 2), (1, 0), (2, 1)])
+def test_combine_adjoint_identity(seed, Ns):
+    T, K = 7, 3
+    dy, Y, pair_row, g = _case(seed, T=T, K=K, Ns=Ns)
+    dgate, dY = oracle.combine_backward(dy, Y, pair_row, g, T, K, Ns)
+    # C is linear in Y for fixed g: <dy, C(Y', g)> = <dY, Y'> for any Y'
+    Y2 = np.random.default_rng(seed + 50).normal(size=Y.shape)
+    np.testing.assert_allclose(np.sum(dy * _combine(Y2, g, pair_row, T, K, Ns)), np.sum(dY * Y2),
+                               rtol=1e-12)
+    # and its routed part is linear in g for fixed Y: <dy, C(Y, g') - C(Y, 0)> = <dg, g'>
+    g2 = np.random.default_rng(seed + 60).normal(size=g.shape)
+    lhs = np.sum(dy * (_combine(Y, g2, pair_row, T, K, Ns) - _combine(Y, 0 * g2, pair_row, T, K, Ns)))
+    np.testing.assert_allclose(lhs, np.sum(dgate * g2), rtol=1e-12)
+
+
+def test_combine_backward_hand_computed():
+    # T = 1, K = 2, Ns = 1, h = 2: rows 0, 1 routed (pair (0,0) -> row 1, (0,1) -> row 0),
+    # row 2 shared.  dy = [1, 2]; Y[0] = [3, -1], Y[1] = [0.5, 4]; g = [0.25, 0.75]
+    # dg = [<dy, Y[1]>, <dy, Y[0]>] = [8.5, 1]; dY[1] = 0.25 dy, dY[0] = 0.75 dy, dY[2] = dy
+    dy = np.array([[1.0, 2.0]])
+    Y = np.array([[3.0, -1.0], [0.5, 4.0], [9.0, 9.0]])
+    dgate, dY = oracle.combine_backward(dy, Y, np.array([1, 0]), np.array([[0.25, 0.75]]), 1, 2, 1)
+    np.testing.assert_array_equal(dgate, [[8.5, 1.0]])
+    np.testing.assert_array_equal(dY, [[0.75, 1.5], [0.25, 0.5], [1.0, 2.0]])
+
+
+@pytest.mark.parametrize("seed,T,E,K", [(3, 5, 8, 3), (4, 4, 16, 4), (5, 3, 4, 1)])
+def test_gate_backward_matches_central_differences(seed, T, E, K):
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0, 1.5, size=(T, E))
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    dg = rng.normal(size=(T, K))
+
+    def loss(zz):
+        s = 1.0 / (1.0 + np.exp(-zz))
+        sel = np.take_along_axis(s, idx, 1)
+        return np.sum(dg * sel / sel.sum(1, keepdims=True))
+
+    grad = oracle.gate_backward(z, idx, dg)
+    h = 1e-6
+    fd = np.zeros_like(z)
+    for t in range(T):
+        for e in range(E):
+            zp, zm = z.copy(), z.copy()
+            zp[t, e] += h
+            zm[t, e] -= h
+            fd[t, e] = (loss(zp) - loss(zm)) / (2 * h)
+    np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-10)
+    # unselected experts get exactly zero (no path from their logits to the gates)
+    mask = np.ones_like(z, bool)
+    np.put_along_axis(mask, idx, False, axis=1)
+    assert np.all(grad[mask] == 0.0)
+
+
+def test_gate_backward_hand_computed_and_closed_form():
+    # K = 2, z = 0 on both selected experts: s = 1/2, S = 1, g = [1/2, 1/2];
+    # dg = [1, 0]: ds = (dg - <dg, g>) / S = [1/2, -1/2]; dz = ds * s (1 - s) = [1/8, -1/8]
+    z = np.zeros((1, 4))
+    grad = oracle.gate_backward(z, np.array([[2, 0]]), np.array([[1.0, 0.0]]))
+    np.testing.assert_allclose(grad, [[-0.125, 0.0, 0.125, 0.0]], rtol=0, atol=1e-15)
+    # a gradient equal over the selection moves nothing: the gates always sum to one
+    rng = np.random.default_rng(9)
+    z = rng.normal(size=(6, 16))
+    idx = np.stack([rng.choice(16, 4, replace=False) for _ in range(6)])
+    g = oracle.gate_backward(z, idx, np.full((6, 4), 3.7))
+    np.testing.assert_allclose(g, 0.0, atol=1e-15)
