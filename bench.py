@@ -13,8 +13,9 @@ Prints ONE JSON line: layer tokens/s as ``value``, plus the grouped-GEMM TFLOP/s
 and the roofline of the grouped expert GEMM (moe_grouped_ffn: the gated GEMM1 and
 GEMM2 kernels, 99.5% of the layer's FLOPs) and the CPU oracle's rate on a bounded
 sample (``cpu_baseline``).  After the timed steps, and outside them, the
-training-side extras are timed on their own (``balance_loss``): the router
-affinities and the sequence-wise balance loss with its logit gradient.
+training-side extras are timed on their own: the router affinities and the
+sequence-wise balance loss with its logit gradient (``balance_loss``), and the
+combine and gate backward (``backward``).
 """
 from __future__ import annotations
 
@@ -143,6 +144,45 @@ def balance_loss_leg(moe, cfg, c, d, idx, ws, stream, reps: int = 20):
             "loss_value": [round(float(v), 9) for v in loss.cpu()]}
 
 
+def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, reps: int = 20):
+    """Time the combine and gate backward outside the layer step, on the step's own
+    y_rows, routing and permutation, with the layer output standing in for the output
+    gradient.  Algorithmic bytes: combine backward reads dy and the routed rows once
+    and writes every row gradient once (plus dgate, pair_row and the gates); gate
+    backward reads K affinities, indices and gate gradients per token and writes the
+    [T, E] logit gradient."""
+    import torch
+    T, E, K, H = cfg.T, cfg.E, cfg.K, cfg.hidden
+    eb = 4 if cfg.act == "f32" else 2
+    dgate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    dy_rows = torch.empty_like(y_rows)
+    scores = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    grad = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    moe.moe_router_scores(c, d["x"], d["w_router"], scores, ws)
+
+    def timed(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    us_comb = timed(lambda: moe.moe_combine_backward(c, y, y_rows, pair_row, gate, dgate, dy_rows))
+    us_gate = timed(lambda: moe.moe_gate_backward(c, scores, idx, dgate, grad))
+    b_comb = T * H * eb + T * K * H * eb + cfg.rows * H * eb + T * K * (4 + 8)
+    b_gate = T * K * 12 + T * E * 4
+    gb_comb = b_comb / (us_comb * 1e-6) / 1e9
+    gb_gate = b_gate / (us_gate * 1e-6) / 1e9
+    return {"combine_backward_us": round(us_comb, 2), "combine_backward_bytes": b_comb,
+            "combine_backward_GBps": round(gb_comb, 1),
+            "combine_backward_frac_hbm": round(gb_comb / HBM_PEAK, 4),
+            "gate_backward_us": round(us_gate, 2), "gate_backward_bytes": b_gate,
+            "gate_backward_GBps": round(gb_gate, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +306,7 @@ def main():
         "roofline": roof,
     }
     result["balance_loss"] = balance_loss_leg(moe, cfg, c, d, idx, ws, stream)
+    result["backward"] = backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream)
     if args.cpu_tokens > 0:
         log(f"[bench] oracle baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_tokens)

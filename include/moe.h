@@ -197,6 +197,33 @@ moe_status moe_balance_loss(const moe_config* cfg, const float* scores, const in
                             float* expert_prob, float* grad_logits, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* Backward of the combine ("深度解读报告" section 2.2, differentiated): for every
+ * token t, with Y = y_rows of the forward
+ *   dgate[t, k] = <dy[t], Y[pair_row[t*K+k]]>            (fp32, fixed summation order)
+ *   dy_rows[pair_row[t*K+k]] = topk_gate[t, k] * dy[t]    (fp32 product, one rounding)
+ *   dy_rows[T*K + s*T + t]   = dy[t]                      (each shared expert s)
+ * The residual's gradient is dy itself.  dy [T, hidden] act_dtype; y_rows
+ * [T*K + T*Ns, hidden] act_dtype; pair_row [T*K] int32 as written by moe_permute
+ * (negative entries are skipped); topk_gate [T, K] fp32; dgate [T, K] fp32 out;
+ * dy_rows [T*K + T*Ns, hidden] act_dtype out (the gradient of y_rows, same layout). */
+moe_status moe_combine_backward(const moe_config* cfg, const void* dy, const void* y_rows,
+                                const int32_t* pair_row, const float* topk_gate, float* dgate,
+                                void* dy_rows, void* stream);
+
+/* Backward of the gates into the router logits ("深度解读报告" sections 2.2-2.3,
+ * differentiated): with the selection held fixed, S = sum_k scores[t, idx_k] and
+ * g_k = scores[t, idx_k] / S,
+ *   grad_logits[t, idx_j] = (dgate[t, j] - sum_k dgate[t, k] g_k) / S
+ *                           * scores[t, idx_j] * (1 - scores[t, idx_j])
+ * and 0 for the experts not selected; the selection bias gets no gradient (it only
+ * decides the selection).  scores [T, E] fp32 (moe_router_scores); topk_idx [T, K]
+ * int32 (entries outside [0, E) take no part); dgate [T, K] fp32
+ * (moe_combine_backward); grad_logits [T, E] fp32 out, overwritten, or added to when
+ * accumulate != 0 (e.g. onto the balance loss's gradient). */
+moe_status moe_gate_backward(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
+                             const float* dgate, float* grad_logits, int32_t accumulate,
+                             void* stream);
+
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.
  * residual (nullable) is u of "out = u + ..." in section 2.2; NULL gives the MoE

@@ -58,6 +58,8 @@ _SIGS = {
     "moe_router_scores": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_balance_loss": (ctypes.c_int, [_CFG, _P, _P, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
                                         _P, _P, ctypes.c_size_t, _P]),
+    "moe_combine_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_gate_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -201,6 +203,20 @@ def moe_balance_loss(cfg, scores, topk_idx, seq_len, alpha, seq_loss, expert_fra
         float(alpha), _dev(seq_loss, "seq_loss"), _dev(expert_frac, "expert_frac", True),
         _dev(expert_prob, "expert_prob", True), _dev(grad_logits, "grad_logits", True),
         _dev(ws, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_combine_backward(cfg, dy, y_rows, pair_row, topk_gate, dgate, dy_rows, stream=None):
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        ctypes.byref(cfg), _dev(dy, "dy"), _dev(y_rows, "y_rows"), _dev(pair_row, "pair_row"),
+        _dev(topk_gate, "topk_gate"), _dev(dgate, "dgate"), _dev(dy_rows, "dy_rows"),
+        _stream(stream)))
+
+
+def moe_gate_backward(cfg, scores, topk_idx, dgate, grad_logits, accumulate=False, stream=None):
+    _check("moe_gate_backward", lib().moe_gate_backward(
+        ctypes.byref(cfg), _dev(scores, "scores"), _dev(topk_idx, "topk_idx"),
+        _dev(dgate, "dgate"), _dev(grad_logits, "grad_logits"), int(bool(accumulate)),
+        _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

@@ -162,6 +162,25 @@ moe_status moe_balance_loss(const moe_config* cfg, const float* scores, const in
                                       static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_combine_backward(const moe_config* cfg, const void* dy, const void* y_rows,
+                                const int32_t* pair_row, const float* topk_gate, float* dgate,
+                                void* dy_rows, void* stream) {
+  MOE_TRY(validate(cfg));
+  if (!dy || !y_rows || !pair_row || !topk_gate || !dgate || !dy_rows)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_combine_backward(*cfg, dy, y_rows, pair_row, topk_gate, dgate, dy_rows,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_gate_backward(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
+                             const float* dgate, float* grad_logits, int32_t accumulate,
+                             void* stream) {
+  MOE_TRY(validate(cfg));
+  if (!scores || !topk_idx || !dgate || !grad_logits) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_gate_backward(*cfg, scores, topk_idx, dgate, grad_logits, accumulate != 0,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* expert_load,
                        int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, void* ws,
                        size_t ws_bytes, void* stream) {

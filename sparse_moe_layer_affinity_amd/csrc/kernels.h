@@ -80,6 +80,11 @@ hipError_t launch_router_scores(const moe_config& c, const float* z, float* scor
 hipError_t launch_balance_loss(const moe_config& c, const float* scores, const int32_t* idx,
                                int seq_len, float alpha, float* loss, float* frac, float* prob,
                                float* grad, const Workspace& w, hipStream_t s);
+hipError_t launch_combine_backward(const moe_config& c, const void* dy, const void* y_rows,
+                                   const int32_t* pair_row, const float* gate, float* dgate,
+                                   void* dy_rows, hipStream_t s);
+hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
+                                const float* dgate, float* grad, int accumulate, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
                             hipStream_t s, bool transposed = false, bool pow2 = false);
 hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t* offsets,

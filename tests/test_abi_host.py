@@ -32,7 +32,8 @@ def test_library_exports_every_declared_symbol():
     names = B.header_symbols()
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_act_quant_e4m3",
                           "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
-                          "moe_router_scores", "moe_balance_loss", "moe_status_string"}
+                          "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
+                          "moe_gate_backward", "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -156,6 +157,24 @@ def test_balance_loss_argument_checks():
         B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_router_scores, c, A, A, A, A, need - 1, stream=0) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_backward_argument_checks():
+    c = cfg()
+    A = ALIGNED
+    args = [A] * 6
+    for i in range(6):
+        bad = list(args)
+        bad[i] = 0
+        assert code_of(B.moe_combine_backward, c, *bad, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    for i in range(4):
+        bad = [A] * 4
+        bad[i] = 0
+        assert code_of(B.moe_gate_backward, c, *bad, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_gate_backward, cfg(E=250), A, A, A, A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_combine_backward, cfg(act="f32", w="bf16"), *args, stream=0) == \
+        B.MOE_ERR_UNSUPPORTED
 
 
 def test_weight_scale_pointer_rules():

@@ -240,6 +240,21 @@ def make_affinities(T: int, E: int, seed: int = 0) -> torch.Tensor:
     return _uniform((T, E), 0.02, 0.98, tensor_seed(seed, "affinities", T, E), "cpu")
 
 
+def make_dense(shape, dtype: str = "bf16", std: float = 1.0, seed: int = 0,
+               name: str = "dense") -> torch.Tensor:
+    """Seeded N(0, std^2) tensor of any shape, drawn in float32 and rounded to
+    ``dtype`` (stand-in activations and output gradients for the backward stages)."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return _normal(tuple(shape), std, tensor_seed(seed, name, n), "cpu", _DTYPES[dtype])
+
+
+def make_gates(T: int, K: int, seed: int = 0) -> torch.Tensor:
+    """Seeded [T, K] float32 gate-like weights, uniform in (0.05, 1)."""
+    return _uniform((T, K), 0.05, 1.0, tensor_seed(seed, "gates", T, K), "cpu")
+
+
 def make_loads(E: int, T: int, K: int, seed: int = 0, at_mean: int = 4) -> torch.Tensor:
     """Seeded per-expert loads summing to T*K, the first ``at_mean`` exactly at the mean
     when T*K is a multiple of E (a bias-update-stage input)."""
