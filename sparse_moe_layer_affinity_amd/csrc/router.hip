@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 }
 
 constexpr int kSelWaves = 4;
+constexpr int kSelBatch = 8;    // split-K partials loaded per round trip
 
 // (value desc, index asc) ordering used for every selection decision.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -55,8 +56,8 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
   const int n = E / G;
 
   // logits = the split-K partials summed in split order (one partial unless split);
-  // the lane's four experts load four partials each ahead of the in-order adds, so
-  // sixteen loads are in flight per round trip
+  // up to kSelBatch partials of the lane's four experts are loaded together ahead of
+  // the in-order adds, so one round trip covers the usual split counts
   float zz[4];
   const size_t stride = size_t(T) * E;
   const size_t tofs = size_t(active ? t : 0) * E;
@@ -66,21 +67,19 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
   };
 #pragma unroll
   for (int j = 0; j < 4; ++j) zz[j] = part(0, j);
-  int p = 1;
-  for (; p + 4 <= splits; p += 4) {
-    float pv[4][4];
+  for (int p0 = 1; p0 < splits; p0 += kSelBatch) {
+    float pv[kSelBatch][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kSelBatch; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pv[i][j] = part(p + i, j);
+      for (int j = 0; j < 4; ++j) pv[i][j] = p0 + i < splits ? part(p0 + i, j) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kSelBatch; ++i)
+      if (p0 + i < splits) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) zz[j] += pv[i][j];
+        for (int j = 0; j < 4; ++j) zz[j] += pv[i][j];
+      }
   }
-  for (; p < splits; ++p)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zz[j] += part(p, j);
 
   // affinities and biased affinities (fp32)
   float v[4];
@@ -99,9 +98,18 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select(
   __syncthreads();
   if (!active) return;
 
-  // stage 1: group score = sum of the topn largest biased affinities (largest first)
+  // stage 1: group score = sum of the topn largest biased affinities (largest first);
+  // a two-slot running maximum when topn <= 2 (the same two values, duplicates kept)
   float gscore = -INFINITY;
-  if (l < G) {
+  if (l < G && topn <= 2) {
+    float t0 = -INFINITY, t1 = -INFINITY;
+    for (int i = 0; i < n; ++i) {
+      const float x = sb_lds[w][l * n + i];
+      t1 = x > t0 ? t0 : (x > t1 ? x : t1);
+      t0 = x > t0 ? x : t0;
+    }
+    gscore = topn == 2 ? 0.0f + t0 + t1 : 0.0f + t0;
+  } else if (l < G) {
     float top[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) top[i] = -INFINITY;
