@@ -1,5 +1,7 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward, with the
+ * training-side pieces next to it: router affinities, the sequence-wise balance loss
+ * and its gradient, and the backward of the combine and of the gates.
  *
  * The layer (DeepSeek-V3 technical report summary "深度解读报告", section 2.2):
  *
