@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: full-size workload (minutes on the GPU box host)")
+    config.addinivalue_line("markers", "slow: full-size workload (a minute or more of oracle work on the host)")
 
 
 def pytest_collection_modifyitems(config, items):
