@@ -41,10 +41,11 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   gate_backward    pinned: central finite differences of the gates, a hand-computed
                    case, zero gradient for a dgate equal over the selection and for
                    unselected experts
+  swiglu_backward  pinned: central finite differences, the closed forms at a = 0
 """
 from .moe_layer import (RouteResult, affinities, route, permute, expert_ffn, layer_output,
                         bias_update, silu)
-from .backward import combine_backward, gate_backward
+from .backward import combine_backward, gate_backward, swiglu_backward
 from .balance import balance_loss, balance_loss_grad_logits
 from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128,
                    dequantize_blocks_128, expert_ffn_fp8_emulated, pow2_scale,
@@ -53,4 +54,5 @@ from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128
 __all__ = ["RouteResult", "affinities", "route", "permute", "expert_ffn", "layer_output",
            "bias_update", "silu", "e4m3_table", "e4m3_encode_rne", "quantize_1x128",
            "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated",
-           "balance_loss", "balance_loss_grad_logits", "combine_backward", "gate_backward"]
+           "balance_loss", "balance_loss_grad_logits", "combine_backward", "gate_backward",
+           "swiglu_backward"]

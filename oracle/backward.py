@@ -15,11 +15,18 @@ state no backward; differentiating them is the plain reading):
                dL/dz_j = dL/ds_j * s_j (1 - s_j)          (s = sigmoid(z))
   bias         no gradient: the selection is piecewise constant in b.
 
+SwiGLU expert ("深度解读报告" section 2.2 with SwiGLU experts, the reading of the
+garbled activation passage): h = silu(a) * b with a = W_gate u, b = W_up u and
+silu(a) = a sigmoid(a); its backward for an upstream gradient dh is
+  da = dh * b * silu'(a),  silu'(a) = sigmoid(a) (1 + a (1 - sigmoid(a)))
+  db = dh * silu(a).
+
 Parity status: pinned by mathematics.  The combine adjoint by the adjoint identity
 <dy, C(Y, g)> = <dY, Y> + <dg, g> (C is linear in Y for fixed g and in g for fixed Y)
 and by a hand-computed case; the gate backward by central finite differences of the
 gates, a hand-computed case, and a closed form (a dg equal over k gives no gradient,
-because the gates sum to one).
+because the gates sum to one); the SwiGLU backward by central finite differences of
+sum(dh * h) and the closed forms at a = 0 (silu' = 1/2, silu = 0).
 """
 from __future__ import annotations
 
@@ -71,3 +78,16 @@ def gate_backward(z, idx, dgate) -> np.ndarray:
         ds = (dg[t] - np.dot(dg[t], g)) / total
         grad[t, idx[t]] = ds * sel * (1.0 - sel)
     return grad
+
+
+def swiglu_backward(a, b, dh):
+    """Gradients (da, db) of sum(dh * silu(a) * b) with respect to the gate and up
+    pre-activations a and b (any equal shapes), float64."""
+    a = _f64(a)
+    b = _f64(b)
+    dh = _f64(dh)
+    sig = 1.0 / (1.0 + np.exp(-a))
+    silu = a * sig
+    dsilu = sig * (1.0 + a * (1.0 - sig))
+    return dh * b * dsilu, dh * silu
+

@@ -1,4 +1,4 @@
-"""Pins for the combine and gate backward oracle (mathematics: the pages state the
+"""Pins for the combine, gate and SwiGLU backward oracle (mathematics: the pages state the
 forward formulas only)."""
 import numpy as np
 import pytest
@@ -92,3 +92,38 @@ def test_gate_backward_hand_computed_and_closed_form():
     idx = np.stack([rng.choice(16, 4, replace=False) for _ in range(6)])
     g = oracle.gate_backward(z, idx, np.full((6, 4), 3.7))
     np.testing.assert_allclose(g, 0.0, atol=1e-15)
+
+
+def test_swiglu_backward_matches_central_differences():
+    rng = np.random.default_rng(11)
+    a = rng.normal(0, 2, size=(4, 6))
+    b = rng.normal(size=(4, 6))
+    dh = rng.normal(size=(4, 6))
+
+    def loss(aa, bb):
+        return np.sum(dh * aa / (1.0 + np.exp(-aa)) * bb)
+
+    da, db = oracle.swiglu_backward(a, b, dh)
+    h = 1e-6
+    for i in range(4):
+        for j in range(6):
+            e = np.zeros_like(a)
+            e[i, j] = h
+            np.testing.assert_allclose(da[i, j], (loss(a + e, b) - loss(a - e, b)) / (2 * h),
+                                       rtol=1e-6, atol=1e-9)
+            np.testing.assert_allclose(db[i, j], (loss(a, b + e) - loss(a, b - e)) / (2 * h),
+                                       rtol=1e-6, atol=1e-9)
+
+
+def test_swiglu_backward_closed_forms():
+    # at a = 0: sigmoid = 1/2, silu = 0, silu' = 1/2 -> da = dh b / 2, db = 0
+    b = np.array([[2.0, -3.0]])
+    dh = np.array([[0.5, 4.0]])
+    da, db = oracle.swiglu_backward(np.zeros((1, 2)), b, dh)
+    np.testing.assert_array_equal(da, [[0.5, -6.0]])
+    np.testing.assert_array_equal(db, [[0.0, 0.0]])
+    # far positive a: silu(a) -> a and silu'(a) -> 1
+    da, db = oracle.swiglu_backward(np.array([[40.0]]), np.array([[3.0]]), np.array([[2.0]]))
+    np.testing.assert_allclose(da, [[6.0]], rtol=1e-12)
+    np.testing.assert_allclose(db, [[80.0]], rtol=1e-12)
+
