@@ -15,7 +15,7 @@ GEMM2 kernels, 99.5% of the layer's FLOPs) and the CPU oracle's rate on a bounde
 sample (``cpu_baseline``).  After the timed steps, and outside them, the
 training-side extras are timed on their own: the router affinities and the
 sequence-wise balance loss with its logit gradient (``balance_loss``), and the
-combine and gate backward (``backward``).
+combine, gate and SwiGLU backward (``backward``).
 """
 from __future__ import annotations
 
@@ -145,12 +145,13 @@ def balance_loss_leg(moe, cfg, c, d, idx, ws, stream, reps: int = 20):
 
 
 def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, reps: int = 20):
-    """Time the combine and gate backward outside the layer step, on the step's own
-    y_rows, routing and permutation, with the layer output standing in for the output
-    gradient.  Algorithmic bytes: combine backward reads dy and the routed rows once
-    and writes every row gradient once (plus dgate, pair_row and the gates); gate
-    backward reads K affinities, indices and gate gradients per token and writes the
-    [T, E] logit gradient."""
+    """Time the combine, gate and SwiGLU backward outside the layer step: the first two
+    on the step's own y_rows, routing and permutation, with the layer output standing
+    in for the output gradient.  Algorithmic bytes: combine backward reads dy and the
+    routed rows once and writes every row gradient once (plus dgate, pair_row and the
+    gates); gate backward reads K affinities, indices and gate gradients per token and
+    writes the [T, E] logit gradient; SwiGLU backward reads three [rows, inter] arrays
+    and writes two."""
     import torch
     T, E, K, H = cfg.T, cfg.E, cfg.K, cfg.hidden
     eb = 4 if cfg.act == "f32" else 2
@@ -172,6 +173,19 @@ def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, rep
 
     us_comb = timed(lambda: moe.moe_combine_backward(c, y, y_rows, pair_row, gate, dgate, dy_rows))
     us_gate = timed(lambda: moe.moe_gate_backward(c, scores, idx, dgate, grad))
+    # SwiGLU backward over every grouped row: seeded stand-ins for the pre-activations
+    # and the gradient of h (the forward does not keep the pre-activations)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    shape = (cfg.rows, cfg.inter)
+    adt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    pre_a = (2.0 * torch.randn(shape, generator=g, device="cuda")).to(adt)
+    pre_b = torch.randn(shape, generator=g, device="cuda").to(adt)
+    dh = torch.randn(shape, generator=g, device="cuda").to(adt)
+    da, db = torch.empty_like(pre_a), torch.empty_like(pre_a)
+    us_swi = timed(lambda: moe.moe_swiglu_backward(c, pre_a, pre_b, dh, cfg.rows, da, db))
+    b_swi = 5 * cfg.rows * cfg.inter * eb
+    gb_swi = b_swi / (us_swi * 1e-6) / 1e9
     b_comb = T * H * eb + T * K * H * eb + cfg.rows * H * eb + T * K * (4 + 8)
     b_gate = T * K * 12 + T * E * 4
     gb_comb = b_comb / (us_comb * 1e-6) / 1e9
@@ -180,7 +194,10 @@ def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, rep
             "combine_backward_GBps": round(gb_comb, 1),
             "combine_backward_frac_hbm": round(gb_comb / HBM_PEAK, 4),
             "gate_backward_us": round(us_gate, 2), "gate_backward_bytes": b_gate,
-            "gate_backward_GBps": round(gb_gate, 1)}
+            "gate_backward_GBps": round(gb_gate, 1),
+            "swiglu_backward_us": round(us_swi, 2), "swiglu_backward_bytes": b_swi,
+            "swiglu_backward_GBps": round(gb_swi, 1),
+            "swiglu_backward_frac_hbm": round(gb_swi / HBM_PEAK, 4)}
 
 
 def main():

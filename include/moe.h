@@ -1,7 +1,8 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward, with the
  * training-side pieces next to it: router affinities, the sequence-wise balance loss
- * and its gradient, and the backward of the combine and of the gates.
+ * and its gradient, and the backward of the combine, of the gates and of the SwiGLU
+ * activation.
  *
  * The layer (DeepSeek-V3 technical report summary "深度解读报告", section 2.2):
  *
@@ -225,6 +226,17 @@ moe_status moe_combine_backward(const moe_config* cfg, const void* dy, const voi
 moe_status moe_gate_backward(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
                              const float* dgate, float* grad_logits, int32_t accumulate,
                              void* stream);
+
+/* Backward of the SwiGLU activation of the experts ("深度解读报告" section 2.2,
+ * SwiGLU experts h = silu(a) * b with a = W_gate u and b = W_up u, differentiated):
+ * for every element of the [rows, inter] arrays
+ *   da = dh * b * silu'(a),  silu'(a) = sigmoid(a) * (1 + a * (1 - sigmoid(a)))
+ *   db = dh * silu(a)
+ * in fp32, one rounding per output.  a, b, dh [rows, inter] act_dtype in (the gate
+ * and up pre-activations and the gradient of h); da, db [rows, inter] act_dtype out.
+ * rows >= 1.  The forward does not keep a and b: the caller provides them. */
+moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,
+                               const void* dh, int32_t rows, void* da, void* db, void* stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.

@@ -60,6 +60,7 @@ _SIGS = {
                                         _P, _P, ctypes.c_size_t, _P]),
     "moe_combine_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
     "moe_gate_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_int32, _P]),
+    "moe_swiglu_backward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -217,6 +218,12 @@ def moe_gate_backward(cfg, scores, topk_idx, dgate, grad_logits, accumulate=Fals
         ctypes.byref(cfg), _dev(scores, "scores"), _dev(topk_idx, "topk_idx"),
         _dev(dgate, "dgate"), _dev(grad_logits, "grad_logits"), int(bool(accumulate)),
         _stream(stream)))
+
+
+def moe_swiglu_backward(cfg, a, b, dh, rows, da, db, stream=None):
+    _check("moe_swiglu_backward", lib().moe_swiglu_backward(
+        ctypes.byref(cfg), _dev(a, "a"), _dev(b, "b"), _dev(dh, "dh"), int(rows), _dev(da, "da"),
+        _dev(db, "db"), _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

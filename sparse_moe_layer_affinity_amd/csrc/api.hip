@@ -172,6 +172,15 @@ moe_status moe_combine_backward(const moe_config* cfg, const void* dy, const voi
                                           static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,
+                               const void* dh, int32_t rows, void* da, void* db, void* stream) {
+  MOE_TRY(validate(cfg));
+  if (!a || !b || !dh || !da || !db || rows < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (1LL * rows * cfg->inter >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return from_hip(launch_swiglu_backward(*cfg, a, b, dh, rows, da, db,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_gate_backward(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
                              const float* dgate, float* grad_logits, int32_t accumulate,
                              void* stream) {

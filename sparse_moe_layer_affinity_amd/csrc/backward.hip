@@ -1,4 +1,4 @@
-// Backward of the combine and of the gates.
+// Backward of the combine, of the gates and of the SwiGLU activation.
 //
 // "DeepSeek-V3 Technical Report 深度解读报告", section 2.2: the layer output adds the
 // shared experts' outputs and the routed experts' outputs weighted by the gates
@@ -13,7 +13,8 @@
 // bytes of bf16 or fp32) v = tid, tid + 256, ...; the token's K routed rows are
 // loaded together; the K dot products are summed per thread in column order, then
 // over each wave by a fixed butterfly and over the four waves in order (fixed order,
-// deterministic).  gate_backward: one wave per token.
+// deterministic).  gate_backward: one wave per token.  swiglu_backward: elementwise
+// over the [rows, inter] pre-activations of the SwiGLU experts.
 #include "kernels.h"
 
 namespace moe {
@@ -42,6 +43,10 @@ struct Vec<uint16_t> {                      // 8 bf16
   __device__ static void store_copy(uint16_t* p, const Vec& v) {
     *reinterpret_cast<uint4*>(p) = v.raw;
   }
+  __device__ static void store_vals(uint16_t* p, const float f[8]) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                              pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  }
 };
 template <>
 struct Vec<float> {                         // 4 fp32
@@ -57,6 +62,9 @@ struct Vec<float> {                         // 4 fp32
   }
   __device__ static void store_copy(float* p, const Vec& v) {
     *reinterpret_cast<float4*>(p) = v.raw;
+  }
+  __device__ static void store_vals(float* p, const float f[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   }
 };
 
@@ -154,6 +162,56 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_backward(
       *p = accumulate ? *p + out[j] : out[j];
     }
   }
+}
+
+// SwiGLU backward, elementwise over contiguous [rows, inter] arrays: for h = silu(a) b,
+//   da = dh b silu'(a),  silu'(a) = sigmoid(a) (1 + a (1 - sigmoid(a))),  db = dh silu(a)
+// in fp32, one rounding per output; 16-byte vectors, grid-stride.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_backward(const T* __restrict__ a,
+                                                       const T* __restrict__ b,
+                                                       const T* __restrict__ dh,
+                                                       T* __restrict__ da, T* __restrict__ db,
+                                                       size_t n_vec) {
+  using V = Vec<T>;
+  for (size_t v = size_t(blockIdx.x) * 256 + threadIdx.x; v < n_vec;
+       v += size_t(gridDim.x) * 256) {
+    const size_t at = v * V::N;
+    V av, bv, hv;
+    av.load(a + at);
+    bv.load(b + at);
+    hv.load(dh + at);
+    float fa[V::N], fb[V::N];
+#pragma unroll
+    for (int i = 0; i < V::N; ++i) {
+      const float x = av.get(i);
+      const float sg = 1.0f / (1.0f + expf(-x));
+      const float dsilu = sg * (1.0f + x * (1.0f - sg));
+      fa[i] = hv.get(i) * bv.get(i) * dsilu;
+      fb[i] = hv.get(i) * (x * sg);
+    }
+    V::store_vals(da + at, fa);
+    V::store_vals(db + at, fb);
+  }
+}
+
+hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void* b,
+                                  const void* dh, int rows, void* da, void* db, hipStream_t st) {
+  const bool f32 = c.act_dtype == MOE_F32;
+  const size_t n_vec = size_t(rows) * c.inter / (f32 ? 4 : 8);
+  const size_t want = (n_vec + 255) / 256;
+  const unsigned blocks = unsigned(want < 8192 ? want : 8192);
+  if (f32)
+    hipLaunchKernelGGL(swiglu_backward<float>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const float*>(a), static_cast<const float*>(b),
+                       static_cast<const float*>(dh), static_cast<float*>(da),
+                       static_cast<float*>(db), n_vec);
+  else
+    hipLaunchKernelGGL(swiglu_backward<uint16_t>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+                       static_cast<const uint16_t*>(dh), static_cast<uint16_t*>(da),
+                       static_cast<uint16_t*>(db), n_vec);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine_backward(const moe_config& c, const void* dy, const void* y_rows,

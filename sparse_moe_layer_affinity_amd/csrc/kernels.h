@@ -83,6 +83,8 @@ hipError_t launch_balance_loss(const moe_config& c, const float* scores, const i
 hipError_t launch_combine_backward(const moe_config& c, const void* dy, const void* y_rows,
                                    const int32_t* pair_row, const float* gate, float* dgate,
                                    void* dy_rows, hipStream_t s);
+hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void* b,
+                                  const void* dh, int rows, void* da, void* db, hipStream_t s);
 hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
                                 const float* dgate, float* grad, int accumulate, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,

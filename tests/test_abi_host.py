@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_act_quant_e4m3",
                           "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
                           "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
-                          "moe_gate_backward", "moe_status_string"}
+                          "moe_gate_backward", "moe_swiglu_backward", "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -175,6 +175,13 @@ def test_backward_argument_checks():
         B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_combine_backward, cfg(act="f32", w="bf16"), *args, stream=0) == \
         B.MOE_ERR_UNSUPPORTED
+    for i in range(5):
+        bad = [A] * 5
+        bad[i] = 0
+        assert code_of(B.moe_swiglu_backward, c, bad[0], bad[1], bad[2], 16, bad[3], bad[4],
+                       stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(B.moe_swiglu_backward, c, A, A, A, 0, A, A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_weight_scale_pointer_rules():
