@@ -26,7 +26,9 @@ Parity status: pinned by mathematics.  The combine adjoint by the adjoint identi
 and by a hand-computed case; the gate backward by central finite differences of the
 gates, a hand-computed case, and a closed form (a dg equal over k gives no gradient,
 because the gates sum to one); the SwiGLU backward by central finite differences of
-sum(dh * h) and the closed forms at a = 0 (silu' = 1/2, silu = 0).
+sum(dh * h) and the closed forms at a = 0 (silu' = 1/2, silu = 0); the expert input
+gradient by central finite differences of sum_r <dy_r, FFN_e(x_t)> with respect to x
+and by linearity in dy.
 """
 from __future__ import annotations
 
@@ -90,4 +92,37 @@ def swiglu_backward(a, b, dh):
     silu = a * sig
     dsilu = sig * (1.0 + a * (1.0 - sig))
     return dh * b * dsilu, dh * silu
+
+
+def expert_input_backward(x, row_token, num_tokens: int, top_k: int, num_shared: int,
+                          dy_rows, get_expert, expert_of_row):
+    """Input gradient of the grouped SwiGLU experts: for every grouped row r of expert
+    e = expert_of_row[r] (token t = row_token[r] for routed rows, r - T*K mod T for
+    the shared rows), with u = x[t], a = W_gate u, b = W_up u, h = silu(a) * b and
+    y_r = W_down h,
+      dh = W_down^T dy_rows[r],  (da, db) = swiglu_backward(a, b, dh),
+      dX[r] = W_gate^T da + W_up^T db,   dx[t] = sum of dX over the token's rows.
+    get_expert(e) -> (w_gate [I, H], w_up [I, H], w_down [H, I]).  Returns
+    (dX [rows, H], dx [T, H]) in float64; rows of experts never named are skipped."""
+    x = _f64(x)
+    dY = _f64(dy_rows)
+    T, K, Ns = num_tokens, top_k, num_shared
+    TK = T * K
+    rows = dY.shape[0]
+    tok = np.array([row_token[r] if r < TK else (r - TK) % T for r in range(rows)])
+    expert_of_row = np.asarray(expert_of_row)
+    dX = np.zeros((rows, x.shape[1]))
+    for e in np.unique(expert_of_row):
+        rs = np.nonzero(expert_of_row == e)[0]
+        wg, wu, wd = (_f64(m) for m in get_expert(int(e)))
+        u = x[tok[rs]]
+        a = u @ wg.T
+        b = u @ wu.T
+        dh = dY[rs] @ wd
+        da, db = swiglu_backward(a, b, dh)
+        dX[rs] = da @ wg + db @ wu
+    dx = np.zeros((T, x.shape[1]))
+    for r in range(rows):
+        dx[tok[r]] += dX[r]
+    return dX, dx
 

@@ -127,3 +127,43 @@ def test_swiglu_backward_closed_forms():
     np.testing.assert_allclose(da, [[6.0]], rtol=1e-12)
     np.testing.assert_allclose(db, [[80.0]], rtol=1e-12)
 
+
+def _ffn_case(seed, T=4, K=2, Ns=1, E=3, H=5, I=4):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    _, off, row_token, _ = oracle.permute(idx, E)
+    experts = [(rng.normal(size=(I, H)), rng.normal(size=(I, H)), rng.normal(size=(H, I)))
+               for _ in range(E + Ns)]
+    rows = T * K + T * Ns
+    expert_of_row = np.concatenate([np.repeat(np.arange(E), np.diff(off)),
+                                    np.repeat(np.arange(E, E + Ns), T)])
+    return rng.normal(size=(T, H)), row_token, experts, expert_of_row, rng.normal(size=(rows, H))
+
+
+def test_expert_input_backward_matches_central_differences():
+    T, K, Ns = 4, 2, 1
+    x, row_token, experts, eor, dY = _ffn_case(12, T=T, K=K, Ns=Ns)
+    tok = [row_token[r] if r < T * K else (r - T * K) % T for r in range(len(eor))]
+
+    def loss(xx):
+        total = 0.0
+        for r, e in enumerate(eor):
+            total += np.dot(dY[r], oracle.expert_ffn(xx[tok[r]][None, :], *experts[e])[0])
+        return total
+
+    dX, dx = oracle.expert_input_backward(x, row_token, T, K, Ns, dY, lambda e: experts[e], eor)
+    h = 1e-6
+    for t in range(T):
+        for c in range(x.shape[1]):
+            xp, xm = x.copy(), x.copy()
+            xp[t, c] += h
+            xm[t, c] -= h
+            np.testing.assert_allclose(dx[t, c], (loss(xp) - loss(xm)) / (2 * h), rtol=1e-6,
+                                       atol=1e-8)
+    # linear in dy: doubling one row's gradient doubles that row's dX only
+    dY2 = dY.copy()
+    dY2[3] *= 2
+    dX2, _ = oracle.expert_input_backward(x, row_token, T, K, Ns, dY2, lambda e: experts[e], eor)
+    np.testing.assert_allclose(dX2[3], 2 * dX[3], rtol=1e-12)
+    np.testing.assert_allclose(np.delete(dX2, 3, 0), np.delete(dX, 3, 0), rtol=0, atol=0)
+
