@@ -1,8 +1,8 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward, with the
  * training-side pieces next to it: router affinities, the sequence-wise balance loss
- * and its gradient, and the backward of the combine, of the gates and of the SwiGLU
- * activation.
+ * and its gradient, the backward of the combine, of the gates and of the SwiGLU
+ * activation, and the input gradient of the experts.
  *
  * The layer (DeepSeek-V3 technical report summary "深度解读报告", section 2.2):
  *
@@ -237,6 +237,30 @@ moe_status moe_gate_backward(const moe_config* cfg, const float* scores, const i
  * rows >= 1.  The forward does not keep a and b: the caller provides them. */
 moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,
                                const void* dh, int32_t rows, void* da, void* db, void* stream);
+
+/* Bytes of device workspace moe_expert_backward_input needs for `cfg` (its own: it
+ * holds transposed copies of all expert weights, as large as the weights).  Host-only;
+ * 0 when cfg is invalid or not supported by the backward (BF16 activations and weights
+ * only, and T*(K+Ns)*hidden*2 and T*(K+Ns)*inter*4 bytes each below 2^31 - 2^20). */
+size_t moe_backward_workspace_bytes(const moe_config* cfg);
+
+/* Input gradient of the grouped SwiGLU experts ("深度解读报告" section 2.2,
+ * differentiated), on the forward's row layout: for every grouped row r of expert e
+ * (token t as in moe_grouped_ffn), with u = x[t], a = W_gate,e u, b = W_up,e u,
+ *   dh = W_down,e^T dy_rows[r];  (da, db) as in moe_swiglu_backward;
+ *   dX[r] = W_gate,e^T da + W_up,e^T db;   dx[t] = sum of dX over the token's rows
+ * (its K routed rows through pair_row, then its shared rows).  a and b are recomputed
+ * (the forward does not keep them); the pre-activations, dh, da | db and dX are held
+ * in bf16; fp32 accumulation; dx rounded once.  x [T, hidden], dy_rows [T*K + T*Ns,
+ * hidden] (e.g. from moe_combine_backward), dx [T, hidden] out, all BF16;
+ * expert_offsets, row_token, pair_row as written by moe_permute; weights as for
+ * moe_grouped_ffn (BF16, no scales).  Workspace: moe_backward_workspace_bytes(cfg),
+ * 256-byte aligned.  The weight gradients are not computed here. */
+moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
+                                     const int32_t* expert_offsets, const int32_t* row_token,
+                                     const int32_t* pair_row, const moe_expert_weights* weights,
+                                     const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.

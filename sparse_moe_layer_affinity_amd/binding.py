@@ -61,6 +61,10 @@ _SIGS = {
     "moe_combine_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
     "moe_gate_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "moe_swiglu_backward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
+    "moe_backward_workspace_bytes": (ctypes.c_size_t, [_CFG]),
+    "moe_expert_backward_input": (ctypes.c_int, [_CFG, _P, _P, _P, _P,
+                                                 ctypes.POINTER(MoeExpertWeights), _P, _P, _P,
+                                                 ctypes.c_size_t, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -224,6 +228,20 @@ def moe_swiglu_backward(cfg, a, b, dh, rows, da, db, stream=None):
     _check("moe_swiglu_backward", lib().moe_swiglu_backward(
         ctypes.byref(cfg), _dev(a, "a"), _dev(b, "b"), _dev(dh, "dh"), int(rows), _dev(da, "da"),
         _dev(db, "db"), _stream(stream)))
+
+
+def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def moe_expert_backward_input(cfg, x, expert_offsets, row_token, pair_row, weights: dict, dy_rows,
+                              dx, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    w = _weights(weights)
+    _check("moe_expert_backward_input", lib().moe_expert_backward_input(
+        ctypes.byref(cfg), _dev(x, "x"), _dev(expert_offsets, "expert_offsets"),
+        _dev(row_token, "row_token"), _dev(pair_row, "pair_row"), ctypes.byref(w),
+        _dev(dy_rows, "dy_rows"), _dev(dx, "dx"), _dev(ws, "ws"), ws_bytes, _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

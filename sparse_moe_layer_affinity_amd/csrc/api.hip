@@ -46,6 +46,31 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   return w;
 }
 
+BackwardWorkspace backward_workspace_layout(const moe_config& c, void* base) {
+  const size_t T = c.num_tokens, K = c.top_k, Ns = c.num_shared, E = c.num_experts;
+  const size_t H = c.hidden, I = c.inter;
+  const size_t rows = T * K + T * Ns, G = E + Ns;
+  BackwardWorkspace w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.sched_n = static_cast<int32_t*>(take(4));
+  w.sched = static_cast<int4*>(take(size_t(expert_row_blocks_upper(c, kExpertBM)) * 16));
+  w.ones = static_cast<float*>(take(T * K * 4));
+  w.wt_down = static_cast<uint16_t*>(take(G * I * H * 2));
+  w.wt_gu = static_cast<uint16_t*>(take(G * H * 2 * I * 2));
+  w.ab = static_cast<uint16_t*>(take(rows * 2 * I * 2));
+  w.dh = static_cast<uint16_t*>(take(rows * I * 2));
+  w.dab = static_cast<uint16_t*>(take(rows * 2 * I * 2));
+  w.dx_rows = static_cast<uint16_t*>(take(rows * H * 2));
+  w.bytes = off;
+  return w;
+}
+
 static bool valid_dtype(moe_dtype d) {
   return d == MOE_F32 || d == MOE_BF16 || d == MOE_E4M3 || d == MOE_E4M3_POW2;
 }
@@ -170,6 +195,39 @@ moe_status moe_combine_backward(const moe_config* cfg, const void* dy, const voi
     return MOE_ERR_INVALID_ARGUMENT;
   return from_hip(launch_combine_backward(*cfg, dy, y_rows, pair_row, topk_gate, dgate, dy_rows,
                                           static_cast<hipStream_t>(stream)));
+}
+
+// The expert backward: bf16 activations and weights; dy_rows and the [rows, 2*inter]
+// intermediates are GEMM operands addressed through 32-bit buffer offsets.
+static moe_status validate_backward(const moe_config* c) {
+  MOE_TRY(validate(c));
+  if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const long long rows = 1LL * c->num_tokens * (c->top_k + c->num_shared);
+  const long long lim = (1LL << 31) - (1LL << 20);
+  if (2LL * rows * c->hidden > lim || 4LL * rows * c->inter > lim) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_bytes(const moe_config* cfg) {
+  if (validate_backward(cfg) != MOE_OK) return 0;
+  return backward_workspace_layout(*cfg, nullptr).bytes;
+}
+
+moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
+                                     const int32_t* expert_offsets, const int32_t* row_token,
+                                     const int32_t* pair_row, const moe_expert_weights* weights,
+                                     const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  MOE_TRY(validate_backward(cfg));
+  if (!x || !expert_offsets || !row_token || !pair_row || !dy_rows || !dx)
+    return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_weights(*cfg, weights));
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < backward_workspace_layout(*cfg, nullptr).bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const BackwardWorkspace w = backward_workspace_layout(*cfg, ws);
+  return from_hip(launch_expert_backward_input(*cfg, x, expert_offsets, row_token, pair_row,
+                                               *weights, dy_rows, dx, w,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,

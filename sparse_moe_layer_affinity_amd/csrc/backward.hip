@@ -15,7 +15,7 @@
 // over each wave by a fixed butterfly and over the four waves in order (fixed order,
 // deterministic).  gate_backward: one wave per token.  swiglu_backward: elementwise
 // over the [rows, inter] pre-activations of the SwiGLU experts.
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace moe {
 
@@ -164,23 +164,29 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_backward(
   }
 }
 
-// SwiGLU backward, elementwise over contiguous [rows, inter] arrays: for h = silu(a) b,
+// SwiGLU backward, elementwise over [rows, cols] arrays with their own row pitches:
+// for h = silu(a) b,
 //   da = dh b silu'(a),  silu'(a) = sigmoid(a) (1 + a (1 - sigmoid(a))),  db = dh silu(a)
 // in fp32, one rounding per output; 16-byte vectors, grid-stride.
+struct SwigluArgs {
+  const void *a, *b, *dh;
+  void *da, *db;
+  long long lda, ldb, ldh, ldda, lddb;   // row pitches in elements
+  int rows, cols;
+};
+
 template <typename T>
-__global__ __launch_bounds__(256) void swiglu_backward(const T* __restrict__ a,
-                                                       const T* __restrict__ b,
-                                                       const T* __restrict__ dh,
-                                                       T* __restrict__ da, T* __restrict__ db,
-                                                       size_t n_vec) {
+__global__ __launch_bounds__(256) void swiglu_backward(SwigluArgs p) {
   using V = Vec<T>;
+  const size_t per_row = size_t(p.cols) / V::N;
+  const size_t n_vec = per_row * p.rows;
   for (size_t v = size_t(blockIdx.x) * 256 + threadIdx.x; v < n_vec;
        v += size_t(gridDim.x) * 256) {
-    const size_t at = v * V::N;
+    const size_t r = v / per_row, col = (v % per_row) * V::N;
     V av, bv, hv;
-    av.load(a + at);
-    bv.load(b + at);
-    hv.load(dh + at);
+    av.load(static_cast<const T*>(p.a) + r * p.lda + col);
+    bv.load(static_cast<const T*>(p.b) + r * p.ldb + col);
+    hv.load(static_cast<const T*>(p.dh) + r * p.ldh + col);
     float fa[V::N], fb[V::N];
 #pragma unroll
     for (int i = 0; i < V::N; ++i) {
@@ -190,28 +196,141 @@ __global__ __launch_bounds__(256) void swiglu_backward(const T* __restrict__ a,
       fa[i] = hv.get(i) * bv.get(i) * dsilu;
       fb[i] = hv.get(i) * (x * sg);
     }
-    V::store_vals(da + at, fa);
-    V::store_vals(db + at, fb);
+    V::store_vals(static_cast<T*>(p.da) + r * p.ldda + col, fa);
+    V::store_vals(static_cast<T*>(p.db) + r * p.lddb + col, fb);
   }
+}
+
+static hipError_t launch_swiglu(bool f32, const SwigluArgs& p, hipStream_t st) {
+  const size_t n_vec = size_t(p.rows) * p.cols / (f32 ? 4 : 8);
+  const size_t want = (n_vec + 255) / 256;
+  const unsigned blocks = unsigned(want < 8192 ? want : 8192);
+  if (f32) hipLaunchKernelGGL(swiglu_backward<float>, dim3(blocks), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(swiglu_backward<uint16_t>, dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void* b,
                                   const void* dh, int rows, void* da, void* db, hipStream_t st) {
-  const bool f32 = c.act_dtype == MOE_F32;
-  const size_t n_vec = size_t(rows) * c.inter / (f32 ? 4 : 8);
-  const size_t want = (n_vec + 255) / 256;
-  const unsigned blocks = unsigned(want < 8192 ? want : 8192);
-  if (f32)
-    hipLaunchKernelGGL(swiglu_backward<float>, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const float*>(a), static_cast<const float*>(b),
-                       static_cast<const float*>(dh), static_cast<float*>(da),
-                       static_cast<float*>(db), n_vec);
-  else
-    hipLaunchKernelGGL(swiglu_backward<uint16_t>, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
-                       static_cast<const uint16_t*>(dh), static_cast<uint16_t*>(da),
-                       static_cast<uint16_t*>(db), n_vec);
+  const long long I = c.inter;
+  return launch_swiglu(c.act_dtype == MOE_F32,
+                       SwigluArgs{a, b, dh, da, db, I, I, I, I, I, rows, c.inter}, st);
+}
+
+// Per-expert transpose of bf16 matrices through LDS: dst[g][c][col0 + r] = src[g][r][c]
+// for src [G][R][C]; dst rows hold dst_ld elements.  64 x 64 tiles, 16-bit elements
+// read and written along rows (coalesced), the LDS tile padded against bank conflicts.
+__global__ __launch_bounds__(256) void transpose_experts(const uint16_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, int R, int C,
+                                                         long long dst_ld, int col0,
+                                                         long long dst_stride) {
+  __shared__ uint16_t tile[64][66];
+  const int g = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* s = src + size_t(g) * R * C;
+  uint16_t* d = dst + size_t(g) * dst_stride;
+  const int tc = threadIdx.x % 64, tr = threadIdx.x / 64;
+  for (int i = tr; i < 64; i += 4) {
+    const int r = r0 + i, cc = c0 + tc;
+    tile[i][tc] = (r < R && cc < C) ? s[size_t(r) * C + cc] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int i = tr; i < 64; i += 4) {
+    const int cc = c0 + i, r = r0 + tc;
+    if (cc < C && r < R) d[size_t(cc) * dst_ld + col0 + r] = tile[tc][i];
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_f32(float* __restrict__ p, int n, float v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, int R, int C,
+                                   long long dst_ld, int col0, long long dst_stride,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(transpose_experts, dim3(ceil_div(C, 64), ceil_div(R, 64), G), dim3(256), 0,
+                     st, src, dst, R, C, dst_ld, col0, dst_stride);
   return hipGetLastError();
+}
+
+// Input gradient of the grouped SwiGLU experts (bf16), on the forward's row layout:
+//   a | b   = gathered x rows times W_gate^T | W_up^T      (recomputed, plain GEMMs)
+//   dh      = dy_rows times W_down                         (B = W_down^T per expert)
+//   da | db = SwiGLU backward of (a, b, dh)
+//   dX      = [da | db] times [W_gate ; W_up]              (B = [W_gate^T | W_up^T])
+//   dx      = sum of dX over each token's rows              (the combine, unit gates)
+hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
+                                        const int32_t* offsets, const int32_t* row_token,
+                                        const int32_t* pair_row, const moe_expert_weights& wt,
+                                        const void* dy_rows, void* dx,
+                                        const BackwardWorkspace& ws, hipStream_t s) {
+  const int T = c.num_tokens, K = c.top_k, Ns = c.num_shared, E = c.num_experts;
+  const int H = c.hidden, I = c.inter, TK = T * K, rows = TK + T * Ns, G = E + Ns;
+  hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.sched, ws.sched_n, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fill_f32, dim3(ceil_div(TK, 256)), dim3(256), 0, s, ws.ones, TK, 1.0f);
+  const auto* wg = static_cast<const uint16_t*>(wt.w_gate);
+  const auto* wu = static_cast<const uint16_t*>(wt.w_up);
+  const auto* wd = static_cast<const uint16_t*>(wt.w_down);
+  // W_down [G][H][I] -> [G][I][H];  W_gate, W_up [G][I][H] -> [G][H][2I] side by side
+  if ((err = launch_transpose(wd, ws.wt_down, G, H, I, H, 0, 1LL * I * H, s)) != hipSuccess) return err;
+  if ((err = launch_transpose(wg, ws.wt_gu, G, I, H, 2LL * I, 0, 2LL * H * I, s)) != hipSuccess) return err;
+  if ((err = launch_transpose(wu, ws.wt_gu, G, I, H, 2LL * I, I, 2LL * H * I, s)) != hipSuccess) return err;
+
+  GemmArgs a{};
+  a.sched = ws.sched;
+  a.sched_n = ws.sched_n;
+  a.T = T;
+  a.TK = TK;
+  // a and b, recomputed with the row gather of the forward
+  a.A = static_cast<const uint16_t*>(x);
+  a.row_token = row_token;
+  a.gather = 1;
+  a.a_rows = T;
+  a.b_stride = 1LL * I * H;
+  a.ldc = 2 * I;
+  a.N = I;
+  a.K = H;
+  a.n_tiles = ceil_div(I, 256);
+  a.B0 = wg;
+  a.C = ws.ab;
+  if ((err = launch_grouped_plain_bf16(c, a, s)) != hipSuccess) return err;
+  a.B0 = wu;
+  a.C = ws.ab + I;
+  if ((err = launch_grouped_plain_bf16(c, a, s)) != hipSuccess) return err;
+  // dh = dy_rows W_down
+  GemmArgs d = a;
+  d.A = static_cast<const uint16_t*>(dy_rows);
+  d.row_token = nullptr;
+  d.gather = 0;
+  d.a_rows = rows;
+  d.B0 = ws.wt_down;
+  d.b_stride = 1LL * I * H;
+  d.C = ws.dh;
+  d.ldc = I;
+  d.N = I;
+  d.K = H;
+  d.n_tiles = ceil_div(I, 256);
+  if ((err = launch_grouped_plain_bf16(c, d, s)) != hipSuccess) return err;
+  // da | db
+  const long long I2 = 2LL * I;
+  err = launch_swiglu(false, SwigluArgs{ws.ab, ws.ab + I, ws.dh, ws.dab, ws.dab + I, I2, I2, I,
+                                        I2, I2, rows, I}, s);
+  if (err != hipSuccess) return err;
+  // dX = [da | db] [W_gate ; W_up]
+  GemmArgs q = d;
+  q.A = ws.dab;
+  q.B0 = ws.wt_gu;
+  q.b_stride = 2LL * H * I;
+  q.C = ws.dx_rows;
+  q.ldc = H;
+  q.N = H;
+  q.K = 2 * I;
+  q.n_tiles = ceil_div(H, 256);
+  if ((err = launch_grouped_plain_bf16(c, q, s)) != hipSuccess) return err;
+  // dx: every row of the token with weight one
+  return launch_combine(c, ws.dx_rows, pair_row, ws.ones, nullptr, dx, s);
 }
 
 hipError_t launch_combine_backward(const moe_config& c, const void* dy, const void* y_rows,

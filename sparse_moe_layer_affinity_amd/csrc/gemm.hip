@@ -818,4 +818,15 @@ hipError_t launch_grouped_ffn(const moe_config& c, const void* x, const int32_t*
   return hipGetLastError();
 }
 
+// A plain grouped GEMM C[r] = A[r] B_e^T over the row blocks of a.sched (built by
+// launch_build_schedule with kExpertBM-row blocks): the expert backward's products.
+hipError_t launch_grouped_plain_bf16(const moe_config& c, const GemmArgs& a, hipStream_t s) {
+  const int rounds = ceil_div(expert_row_blocks_upper(c, kExpertBM), kXcds);
+  const int nwg = std::min(resident_workgroups() / kXcds, rounds * a.n_tiles);
+  const dim3 grid(unsigned(nwg * kXcds));
+  if (a.K == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -26,6 +26,10 @@ struct GemmArgs {
   long long c_split_stride;  // split-K: elements between the partial outputs
 };
 
+hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int4* sched,
+                                 int32_t* sched_n, hipStream_t s);
+hipError_t launch_grouped_plain_bf16(const moe_config& c, const GemmArgs& a, hipStream_t s);
+
 // Arguments of the FP8 expert GEMMs (e4m3 operands, 128x128 / 1x128 block scales).
 struct Fp8Args {
   const uint8_t* A;          // e4m3 activations: xq [T, K] (gather) or hq [rows, K]

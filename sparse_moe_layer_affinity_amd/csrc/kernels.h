@@ -28,6 +28,22 @@ struct Workspace {
   size_t bytes;        // total bytes of the layout
 };
 
+// Scratch of the expert backward (its own workspace: the transposed weights alone are
+// as large as the weights)
+struct BackwardWorkspace {
+  int32_t* sched_n;    // [1] row blocks of the grouped GEMMs
+  int4* sched;         // row blocks {group, first row, rows}, largest first
+  float* ones;         // [T*K] unit gates for the final row sum
+  uint16_t* wt_down;   // [E+Ns, inter, hidden]  W_down^T per expert
+  uint16_t* wt_gu;     // [E+Ns, hidden, 2*inter] W_gate^T | W_up^T per expert
+  uint16_t* ab;        // [rows, 2*inter] recomputed gate | up pre-activations
+  uint16_t* dh;        // [rows, inter] gradient of h
+  uint16_t* dab;       // [rows, 2*inter] their gradients
+  uint16_t* dx_rows;   // [rows, hidden] input gradient of every grouped row
+  size_t bytes;
+};
+BackwardWorkspace backward_workspace_layout(const moe_config& c, void* base);
+
 // E4M3 expert weights, with fp32 or power-of-two block scales
 inline bool is_fp8(moe_dtype d) { return d == MOE_E4M3 || d == MOE_E4M3_POW2; }
 
@@ -85,6 +101,11 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dy, const vo
                                    void* dy_rows, hipStream_t s);
 hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void* b,
                                   const void* dh, int rows, void* da, void* db, hipStream_t s);
+hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
+                                        const int32_t* offsets, const int32_t* row_token,
+                                        const int32_t* pair_row, const moe_expert_weights& wt,
+                                        const void* dy_rows, void* dx,
+                                        const BackwardWorkspace& ws, hipStream_t s);
 hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
                                 const float* dgate, float* grad, int accumulate, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_permute", "moe_act_quant_e4m3",
                           "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
                           "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
-                          "moe_gate_backward", "moe_swiglu_backward", "moe_status_string"}
+                          "moe_gate_backward", "moe_swiglu_backward", "moe_backward_workspace_bytes",
+                          "moe_expert_backward_input", "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -182,6 +183,34 @@ def test_backward_argument_checks():
                        stream=0) == B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_swiglu_backward, c, A, A, A, 0, A, A, stream=0) == \
         B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_expert_backward_argument_checks():
+    A = ALIGNED
+    c = cfg()
+    need = moe.moe_backward_workspace_bytes(c)
+    # transposed copies of all 257 experts' weights dominate
+    assert need > 257 * 3 * 7168 * 2048 * 2 and need % 256 == 0
+    assert moe.moe_backward_workspace_bytes(cfg(w="e4m3")) == 0          # bf16 only
+    assert moe.moe_backward_workspace_bytes(cfg(act="f32", w="f32", hidden=256, inter=128,
+                                                T=64, E=16, K=4, G=4, M=2)) == 0
+    assert moe.moe_backward_workspace_bytes(cfg(T=16635)) > 0            # rows * hidden * 2 limit
+    assert moe.moe_backward_workspace_bytes(cfg(T=16636)) == 0
+    dense = dict(w_gate=A, w_up=A, w_down=A)
+
+    def call(conf=c, ws_bytes=need, ws=A, **kw):
+        args = dict(x=A, off=A, rt=A, pr=A, w=dense, dy=A, dx=A)
+        args.update(kw)
+        return code_of(B.moe_expert_backward_input, conf, args["x"], args["off"], args["rt"],
+                       args["pr"], args["w"], args["dy"], args["dx"], ws, ws_bytes, stream=0)
+
+    for k in ("x", "off", "rt", "pr", "dy", "dx"):
+        assert call(**{k: 0}) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(w=dict(dense, w_up=0)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(w=dict(dense, s_gate=A, s_up=A, s_down=A)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=A + 32) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(conf=cfg(w="e4m3")) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_weight_scale_pointer_rules():

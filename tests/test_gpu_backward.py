@@ -117,3 +117,47 @@ def test_swiglu_backward(rows, inter, act):
         excess = np.abs(got - want) - rel * np.abs(want) - 1e-5 * np.abs(want).max()
         log(f"  max rel err {np.abs(got - want).max() / np.abs(want).max():.2e}")
         assert np.all(excess <= 0)
+
+
+SMALL = dict(hidden=256, inter=256, E=16, K=4, G=4, M=2, topn=2)
+
+
+@pytest.mark.parametrize("name,over", [("decode_bf16", dict(T=37, **SMALL)),
+                                       ("decode_bf16", dict(T=64, Ns=0, **SMALL)),
+                                       ("decode_bf16", dict(T=29, Ns=2, **SMALL)),
+                                       ("decode_bf16", {})])
+def test_expert_backward_input(name, over):
+    """dx of the grouped SwiGLU experts against the oracle on up to 48 sampled tokens (the
+    oracle run on those tokens' own rows); the oracle's routing and permutation are
+    handed to the GPU.  Bound 2e-2 of the largest magnitude: the recomputed
+    pre-activations, dh, da | db and the row gradients are each held in bf16."""
+    from gpu_harness import config_of, expert_getter, inputs_on_gpu, oracle_route
+    cfg = workloads.get(name).replace(**over)
+    log(f"expert backward input {name} {over}")
+    d = inputs_on_gpu(cfg)
+    r = oracle_route(cfg, d)
+    T, K, Ns, E, H = cfg.T, cfg.K, cfg.Ns, cfg.E, cfg.hidden
+    load, off, row_token, pair_row = oracle.permute(r.idx, E)
+    dy_rows = workloads.make_dense((cfg.rows, H), "bf16", seed=T, name="dy_rows")
+    c = config_of(cfg)
+    ws = torch.empty(moe.moe_backward_workspace_bytes(c), dtype=torch.uint8, device="cuda")
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    i32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).cuda()
+    weights = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
+    moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
+                                  dy_rows.cuda(), dx, ws)
+    torch.cuda.synchronize()
+    toks = workloads.sample_rows(T, 48, seed=4).numpy()
+    n = len(toks)
+    # the chosen tokens' rows, re-indexed as a problem of n tokens (routed, then shared)
+    routed = pair_row.reshape(T, K)[toks].ravel()
+    shared = np.concatenate([T * K + s * T + toks for s in range(Ns)]) if Ns else np.zeros(0, int)
+    sub = np.concatenate([routed, shared]).astype(np.int64)
+    expert_of_row = np.concatenate([np.searchsorted(off, routed, side="right") - 1,
+                                    np.repeat(np.arange(E, E + Ns), n)])
+    _, want = oracle.expert_input_backward(d["x"][toks], np.repeat(np.arange(n), K), n, K, Ns,
+                                           dy_rows[sub], expert_getter(cfg, d), expert_of_row)
+    got = dx.cpu()[toks].double().numpy()
+    err = np.abs(got - want).max() / np.abs(want).max()
+    log(f"  dx rel err {err:.2e} on {n} tokens")
+    assert err <= 2e-2
