@@ -144,14 +144,16 @@ def balance_loss_leg(moe, cfg, c, d, idx, ws, stream, reps: int = 20):
             "loss_value": [round(float(v), 9) for v in loss.cpu()]}
 
 
-def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, reps: int = 20):
+def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows, y, ws, stream,
+                 reps: int = 20):
     """Time the combine, gate and SwiGLU backward outside the layer step: the first two
     on the step's own y_rows, routing and permutation, with the layer output standing
     in for the output gradient.  Algorithmic bytes: combine backward reads dy and the
     routed rows once and writes every row gradient once (plus dgate, pair_row and the
     gates); gate backward reads K affinities, indices and gate gradients per token and
     writes the [T, E] logit gradient; SwiGLU backward reads three [rows, inter] arrays
-    and writes two."""
+    and writes two.  The experts' input gradient (bf16) is timed on the step's own
+    inputs and the combine backward's row gradients, reported with its GEMM FLOPs."""
     import torch
     T, E, K, H = cfg.T, cfg.E, cfg.K, cfg.hidden
     eb = 4 if cfg.act == "f32" else 2
@@ -161,15 +163,15 @@ def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, rep
     grad = torch.empty((T, E), dtype=torch.float32, device="cuda")
     moe.moe_router_scores(c, d["x"], d["w_router"], scores, ws)
 
-    def timed(fn):
+    def timed(fn, n=reps):
         fn()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         ev[1].record(stream)
         torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n
 
     us_comb = timed(lambda: moe.moe_combine_backward(c, y, y_rows, pair_row, gate, dgate, dy_rows))
     us_gate = timed(lambda: moe.moe_gate_backward(c, scores, idx, dgate, grad))
@@ -186,6 +188,27 @@ def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, rep
     us_swi = timed(lambda: moe.moe_swiglu_backward(c, pre_a, pre_b, dh, cfg.rows, da, db))
     b_swi = 5 * cfg.rows * cfg.inter * eb
     gb_swi = b_swi / (us_swi * 1e-6) / 1e9
+    del pre_a, pre_b, dh, da, db
+    # input gradient of the experts (bf16 only): the step's own x, permutation and
+    # weights, the combine backward's row gradients
+    ex = None
+    need = moe.moe_backward_workspace_bytes(c)
+    if need:
+        bws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        wts = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
+        us_ex = timed(lambda: moe.moe_expert_backward_input(c, d["x"], offsets, row_token, pair_row,
+                                                            wts, dy_rows, dx, bws), n=5)
+        us_re = timed(lambda: moe.moe_expert_backward_input(c, d["x"], offsets, row_token, pair_row,
+                                                            wts, dy_rows, dx, bws,
+                                                            reuse_transposed=True), n=5)
+        flops = 8.0 * cfg.rows * H * cfg.inter        # a, b, dh: 2 r H I each; dX: 4 r H I
+        ex = {"expert_backward_input_us": round(us_ex, 1),
+              "expert_backward_input_reuse_us": round(us_re, 1),
+              "expert_backward_input_gemm_flops": flops,
+              "expert_backward_input_tflops": round(flops / (us_ex * 1e-6) / 1e12, 1),
+              "expert_backward_input_reuse_tflops": round(flops / (us_re * 1e-6) / 1e12, 1)}
+        del bws
     b_comb = T * H * eb + T * K * H * eb + cfg.rows * H * eb + T * K * (4 + 8)
     b_gate = T * K * 12 + T * E * 4
     gb_comb = b_comb / (us_comb * 1e-6) / 1e9
@@ -197,7 +220,7 @@ def backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream, rep
             "gate_backward_GBps": round(gb_gate, 1),
             "swiglu_backward_us": round(us_swi, 2), "swiglu_backward_bytes": b_swi,
             "swiglu_backward_GBps": round(gb_swi, 1),
-            "swiglu_backward_frac_hbm": round(gb_swi / HBM_PEAK, 4)}
+            "swiglu_backward_frac_hbm": round(gb_swi / HBM_PEAK, 4), **(ex or {})}
 
 
 def main():
@@ -323,7 +346,8 @@ def main():
         "roofline": roof,
     }
     result["balance_loss"] = balance_loss_leg(moe, cfg, c, d, idx, ws, stream)
-    result["backward"] = backward_leg(moe, cfg, c, d, idx, gate, pair_row, y_rows, y, ws, stream)
+    result["backward"] = backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row,
+                                      y_rows, y, ws, stream)
     if args.cpu_tokens > 0:
         log(f"[bench] oracle baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_tokens)

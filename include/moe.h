@@ -255,12 +255,16 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  * hidden] (e.g. from moe_combine_backward), dx [T, hidden] out, all BF16;
  * expert_offsets, row_token, pair_row as written by moe_permute; weights as for
  * moe_grouped_ffn (BF16, no scales).  Workspace: moe_backward_workspace_bytes(cfg),
- * 256-byte aligned.  The weight gradients are not computed here. */
+ * 256-byte aligned; it receives transposed copies of the weights (about half the
+ * call's time at the prefill shape).  reuse_transposed != 0 skips making them: the
+ * caller asserts that this workspace already holds them from an earlier call with the
+ * same weight contents and config (e.g. further micro-batches before the weights
+ * change); otherwise pass 0.  The weight gradients are not computed here. */
 moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* expert_offsets, const int32_t* row_token,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
-                                     const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
-                                     void* stream);
+                                     const void* dy_rows, void* dx, int32_t reuse_transposed,
+                                     void* ws, size_t ws_bytes, void* stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.

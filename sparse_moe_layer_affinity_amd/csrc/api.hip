@@ -216,8 +216,8 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg) {
 moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* expert_offsets, const int32_t* row_token,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
-                                     const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     const void* dy_rows, void* dx, int32_t reuse_transposed,
+                                     void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate_backward(cfg));
   if (!x || !expert_offsets || !row_token || !pair_row || !dy_rows || !dx)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -226,7 +226,7 @@ moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
   if (ws_bytes < backward_workspace_layout(*cfg, nullptr).bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const BackwardWorkspace w = backward_workspace_layout(*cfg, ws);
   return from_hip(launch_expert_backward_input(*cfg, x, expert_offsets, row_token, pair_row,
-                                               *weights, dy_rows, dx, w,
+                                               *weights, dy_rows, dx, reuse_transposed != 0, w,
                                                static_cast<hipStream_t>(stream)));
 }
 

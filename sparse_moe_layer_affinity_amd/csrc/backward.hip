@@ -218,26 +218,39 @@ hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void
 }
 
 // Per-expert transpose of bf16 matrices through LDS: dst[g][c][col0 + r] = src[g][r][c]
-// for src [G][R][C]; dst rows hold dst_ld elements.  64 x 64 tiles, 16-bit elements
-// read and written along rows (coalesced), the LDS tile padded against bank conflicts.
+// for src [G][R][C] (R, C multiples of 8); dst rows hold dst_ld elements.  64 x 64
+// tiles: 16-byte vector reads along source rows, 16-byte vector writes along
+// destination rows (each gathered from 8 LDS rows); the LDS pitch of 72 elements keeps
+// rows 16-byte aligned.
 __global__ __launch_bounds__(256) void transpose_experts(const uint16_t* __restrict__ src,
                                                          uint16_t* __restrict__ dst, int R, int C,
                                                          long long dst_ld, int col0,
                                                          long long dst_stride) {
-  __shared__ uint16_t tile[64][66];
+  constexpr int kPitch = 72;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
   const int g = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const uint16_t* s = src + size_t(g) * R * C;
   uint16_t* d = dst + size_t(g) * dst_stride;
-  const int tc = threadIdx.x % 64, tr = threadIdx.x / 64;
-  for (int i = tr; i < 64; i += 4) {
-    const int r = r0 + i, cc = c0 + tc;
-    tile[i][tc] = (r < R && cc < C) ? s[size_t(r) * C + cc] : uint16_t(0);
+  const int lane8 = (threadIdx.x % 8) * 8, row = threadIdx.x / 8;     // row 0..31
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = row + 32 * pass, r = r0 + i, cc = c0 + lane8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R && cc < C) v = *reinterpret_cast<const uint4*>(s + size_t(r) * C + cc);
+    *reinterpret_cast<uint4*>(&tile[i * kPitch + lane8]) = v;
   }
   __syncthreads();
-  for (int i = tr; i < 64; i += 4) {
-    const int cc = c0 + i, r = r0 + tc;
-    if (cc < C && r < R) d[size_t(cc) * dst_ld + col0 + r] = tile[tc][i];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int j = row + 32 * pass, cc = c0 + j, r = r0 + lane8;    // source column j
+    uint16_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = tile[(lane8 + q) * kPitch + j];
+    if (cc < C && r < R)
+      *reinterpret_cast<uint4*>(d + size_t(cc) * dst_ld + col0 + r) =
+          make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
   }
 }
 
@@ -263,7 +276,7 @@ static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, in
 hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
                                         const int32_t* offsets, const int32_t* row_token,
                                         const int32_t* pair_row, const moe_expert_weights& wt,
-                                        const void* dy_rows, void* dx,
+                                        const void* dy_rows, void* dx, bool reuse_transposed,
                                         const BackwardWorkspace& ws, hipStream_t s) {
   const int T = c.num_tokens, K = c.top_k, Ns = c.num_shared, E = c.num_experts;
   const int H = c.hidden, I = c.inter, TK = T * K, rows = TK + T * Ns, G = E + Ns;
@@ -274,9 +287,15 @@ hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
   const auto* wu = static_cast<const uint16_t*>(wt.w_up);
   const auto* wd = static_cast<const uint16_t*>(wt.w_down);
   // W_down [G][H][I] -> [G][I][H];  W_gate, W_up [G][I][H] -> [G][H][2I] side by side
-  if ((err = launch_transpose(wd, ws.wt_down, G, H, I, H, 0, 1LL * I * H, s)) != hipSuccess) return err;
-  if ((err = launch_transpose(wg, ws.wt_gu, G, I, H, 2LL * I, 0, 2LL * H * I, s)) != hipSuccess) return err;
-  if ((err = launch_transpose(wu, ws.wt_gu, G, I, H, 2LL * I, I, 2LL * H * I, s)) != hipSuccess) return err;
+  // (skipped when the workspace already holds them for these weights)
+  if (!reuse_transposed) {
+    if ((err = launch_transpose(wd, ws.wt_down, G, H, I, H, 0, 1LL * I * H, s)) != hipSuccess)
+      return err;
+    if ((err = launch_transpose(wg, ws.wt_gu, G, I, H, 2LL * I, 0, 2LL * H * I, s)) != hipSuccess)
+      return err;
+    if ((err = launch_transpose(wu, ws.wt_gu, G, I, H, 2LL * I, I, 2LL * H * I, s)) != hipSuccess)
+      return err;
+  }
 
   GemmArgs a{};
   a.sched = ws.sched;

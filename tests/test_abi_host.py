@@ -202,7 +202,8 @@ def test_expert_backward_argument_checks():
         args = dict(x=A, off=A, rt=A, pr=A, w=dense, dy=A, dx=A)
         args.update(kw)
         return code_of(B.moe_expert_backward_input, conf, args["x"], args["off"], args["rt"],
-                       args["pr"], args["w"], args["dy"], args["dx"], ws, ws_bytes, stream=0)
+                       args["pr"], args["w"], args["dy"], args["dx"], ws, ws_bytes, stream=0,
+                       reuse_transposed=False)
 
     for k in ("x", "off", "rt", "pr", "dy", "dx"):
         assert call(**{k: 0}) == B.MOE_ERR_INVALID_ARGUMENT

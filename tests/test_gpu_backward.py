@@ -146,7 +146,16 @@ def test_expert_backward_input(name, over):
     weights = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
     moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
                                   dy_rows.cuda(), dx, ws)
+    # a second micro-batch on the same weights reuses the transposed copies
+    dy2 = workloads.make_dense((cfg.rows, H), "bf16", seed=T + 1, name="dy_rows")
+    dx2 = torch.empty_like(dx)
+    moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
+                                  dy2.cuda(), dx2, ws, reuse_transposed=True)
+    dx3 = torch.empty_like(dx)
+    moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
+                                  dy2.cuda(), dx3, torch.empty_like(ws))
     torch.cuda.synchronize()
+    assert torch.equal(dx2, dx3), "reusing the transposed weights changed the result"
     toks = workloads.sample_rows(T, 48, seed=4).numpy()
     n = len(toks)
     # the chosen tokens' rows, re-indexed as a problem of n tokens (routed, then shared)
