@@ -125,6 +125,11 @@ SMALL = dict(hidden=256, inter=256, E=16, K=4, G=4, M=2, topn=2)
 @pytest.mark.parametrize("name,over", [("decode_bf16", dict(T=37, **SMALL)),
                                        ("decode_bf16", dict(T=64, Ns=0, **SMALL)),
                                        ("decode_bf16", dict(T=29, Ns=2, **SMALL)),
+                                       ("decode_bf16", dict(T=1, **SMALL)),
+                                       ("decode_bf16", dict(T=5, **{**SMALL, "K": 1, "M": 1})),
+                                       ("decode_bf16", dict(T=400, **{**SMALL, "inter": 128})),
+                                       ("decode_bf16", dict(T=50, **{**SMALL, "hidden": 128,
+                                                                     "inter": 128})),
                                        ("decode_bf16", {})])
 def test_expert_backward_input(name, over):
     """dx of the grouped SwiGLU experts against the oracle on up to 48 sampled tokens (the
