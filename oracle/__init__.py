@@ -44,10 +44,13 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   swiglu_backward  pinned: central finite differences, the closed forms at a = 0
   expert_input_    pinned: central finite differences of sum_r <dy_r, FFN(x_t)> in x,
   backward         linearity in dy
+  expert_weight_   pinned: central finite differences of the same sum in the weights
+  backward
 """
 from .moe_layer import (RouteResult, affinities, route, permute, expert_ffn, layer_output,
                         bias_update, silu)
-from .backward import combine_backward, expert_input_backward, gate_backward, swiglu_backward
+from .backward import (combine_backward, expert_input_backward, expert_weight_backward,
+                       gate_backward, swiglu_backward)
 from .balance import balance_loss, balance_loss_grad_logits
 from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128,
                    dequantize_blocks_128, expert_ffn_fp8_emulated, pow2_scale,
@@ -57,4 +60,4 @@ __all__ = ["RouteResult", "affinities", "route", "permute", "expert_ffn", "layer
            "bias_update", "silu", "e4m3_table", "e4m3_encode_rne", "quantize_1x128",
            "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated",
            "balance_loss", "balance_loss_grad_logits", "combine_backward", "gate_backward",
-           "swiglu_backward", "expert_input_backward"]
+           "swiglu_backward", "expert_input_backward", "expert_weight_backward"]

@@ -28,7 +28,8 @@ gates, a hand-computed case, and a closed form (a dg equal over k gives no gradi
 because the gates sum to one); the SwiGLU backward by central finite differences of
 sum(dh * h) and the closed forms at a = 0 (silu' = 1/2, silu = 0); the expert input
 gradient by central finite differences of sum_r <dy_r, FFN_e(x_t)> with respect to x
-and by linearity in dy.
+and by linearity in dy; the expert weight gradients by central finite differences of
+the same sum with respect to weight entries.
 """
 from __future__ import annotations
 
@@ -125,4 +126,31 @@ def expert_input_backward(x, row_token, num_tokens: int, top_k: int, num_shared:
     for r in range(rows):
         dx[tok[r]] += dX[r]
     return dX, dx
+
+
+def expert_weight_backward(x, row_token, num_tokens: int, top_k: int, dy_rows, get_expert,
+                           expert_of_row, experts):
+    """Weight gradients of the grouped SwiGLU experts: for each expert e in `experts`,
+    over its rows r (u = x[token of r], a = W_gate u, b = W_up u, h = silu(a) b),
+      dW_down[e] = sum_r dy_r h_r^T,   dW_gate[e] = sum_r da_r u_r^T,
+      dW_up[e]   = sum_r db_r u_r^T,   (da, db) = swiglu_backward(a, b, W_down^T dy_r).
+    Returns {e: (dW_gate [I, H], dW_up [I, H], dW_down [H, I])} in float64."""
+    x = _f64(x)
+    dY = _f64(dy_rows)
+    T, K = num_tokens, top_k
+    TK = T * K
+    expert_of_row = np.asarray(expert_of_row)
+    out = {}
+    for e in experts:
+        rs = np.nonzero(expert_of_row == e)[0]
+        wg, wu, wd = (_f64(m) for m in get_expert(int(e)))
+        tok = np.array([row_token[r] if r < TK else (r - TK) % T for r in rs], dtype=np.int64)
+        u = x[tok] if len(rs) else np.zeros((0, x.shape[1]))
+        a = u @ wg.T
+        b = u @ wu.T
+        h = a / (1.0 + np.exp(-a)) * b
+        dh = dY[rs] @ wd
+        da, db = swiglu_backward(a, b, dh)
+        out[int(e)] = (da.T @ u, db.T @ u, dY[rs].T @ h)
+    return out
 

@@ -167,3 +167,29 @@ def test_expert_input_backward_matches_central_differences():
     np.testing.assert_allclose(dX2[3], 2 * dX[3], rtol=1e-12)
     np.testing.assert_allclose(np.delete(dX2, 3, 0), np.delete(dX, 3, 0), rtol=0, atol=0)
 
+
+def test_expert_weight_backward_matches_central_differences():
+    T, K, Ns = 4, 2, 1
+    x, row_token, experts, eor, dY = _ffn_case(13, T=T, K=K, Ns=Ns)
+    tok = [row_token[r] if r < T * K else (r - T * K) % T for r in range(len(eor))]
+
+    def loss(ex):
+        return sum(np.dot(dY[r], oracle.expert_ffn(x[tok[r]][None, :], *ex[e])[0])
+                   for r, e in enumerate(eor))
+
+    grads = oracle.expert_weight_backward(x, row_token, T, K, dY, lambda e: experts[e], eor,
+                                          range(len(experts)))
+    h = 1e-6
+    for e in range(len(experts)):
+        for m in range(3):                   # gate, up, down
+            W = experts[e][m]
+            for idx in [(0, 0), (1, 2), (W.shape[0] - 1, W.shape[1] - 1)]:
+                plus = [list(t) for t in experts]
+                minus = [list(t) for t in experts]
+                Wp, Wm = W.copy(), W.copy()
+                Wp[idx] += h
+                Wm[idx] -= h
+                plus[e][m], minus[e][m] = Wp, Wm
+                fd = (loss(plus) - loss(minus)) / (2 * h)
+                np.testing.assert_allclose(grads[e][m][idx], fd, rtol=1e-6, atol=1e-8)
+
