@@ -2,7 +2,7 @@
  * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward, with the
  * training-side pieces next to it: router affinities, the sequence-wise balance loss
  * and its gradient, the backward of the combine, of the gates and of the SwiGLU
- * activation, and the input gradient of the experts.
+ * activation, and the input and weight gradients of the experts.
  *
  * The layer (DeepSeek-V3 technical report summary "深度解读报告", section 2.2):
  *
@@ -259,12 +259,31 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  * call's time at the prefill shape).  reuse_transposed != 0 skips making them: the
  * caller asserts that this workspace already holds them from an earlier call with the
  * same weight contents and config (e.g. further micro-batches before the weights
- * change); otherwise pass 0.  The weight gradients are not computed here. */
+ * change); otherwise pass 0.  The weight gradients: moe_expert_backward. */
 moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* expert_offsets, const int32_t* row_token,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
                                      const void* dy_rows, void* dx, int32_t reuse_transposed,
                                      void* ws, size_t ws_bytes, void* stream);
+
+/* Input and weight gradients of the grouped SwiGLU experts together
+ * ("深度解读报告" section 2.2, differentiated): dx as in moe_expert_backward_input
+ * (nullable here), and, when dw_gate, dw_up and dw_down are all given (all or none),
+ * for every expert e over its rows r (u = x[token of r], h = silu(a) * b)
+ *   dw_down[e] = sum_r dy_rows[r]^T h_r       [E+Ns, hidden, inter] fp32 out
+ *   dw_gate[e] = sum_r da_r^T u_r             [E+Ns, inter, hidden] fp32 out
+ *   dw_up[e]   = sum_r db_r^T u_r             [E+Ns, inter, hidden] fp32 out
+ * with a, b recomputed and (da, db) as in moe_swiglu_backward, summed in fp32 in row
+ * order (deterministic); experts without rows get zeros.  At least one of dx and the
+ * weight gradients must be requested.  Other arguments, the workspace and
+ * reuse_transposed as for moe_expert_backward_input (the transposed W_down is used
+ * either way). */
+moe_status moe_expert_backward(const moe_config* cfg, const void* x,
+                               const int32_t* expert_offsets, const int32_t* row_token,
+                               const int32_t* pair_row, const moe_expert_weights* weights,
+                               const void* dy_rows, void* dx, float* dw_gate, float* dw_up,
+                               float* dw_down, int32_t reuse_transposed, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.

@@ -62,6 +62,9 @@ _SIGS = {
     "moe_gate_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "moe_swiglu_backward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_backward_workspace_bytes": (ctypes.c_size_t, [_CFG]),
+    "moe_expert_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.POINTER(MoeExpertWeights),
+                                           _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                           ctypes.c_size_t, _P]),
     "moe_expert_backward_input": (ctypes.c_int, [_CFG, _P, _P, _P, _P,
                                                  ctypes.POINTER(MoeExpertWeights), _P, _P,
                                                  ctypes.c_int32, _P, ctypes.c_size_t, _P]),
@@ -243,6 +246,19 @@ def moe_expert_backward_input(cfg, x, expert_offsets, row_token, pair_row, weigh
         _dev(row_token, "row_token"), _dev(pair_row, "pair_row"), ctypes.byref(w),
         _dev(dy_rows, "dy_rows"), _dev(dx, "dx"), int(bool(reuse_transposed)), _dev(ws, "ws"),
         ws_bytes, _stream(stream)))
+
+
+def moe_expert_backward(cfg, x, expert_offsets, row_token, pair_row, weights: dict, dy_rows, dx,
+                        dw_gate, dw_up, dw_down, ws, ws_bytes=None, stream=None,
+                        reuse_transposed=False):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    w = _weights(weights)
+    _check("moe_expert_backward", lib().moe_expert_backward(
+        ctypes.byref(cfg), _dev(x, "x"), _dev(expert_offsets, "expert_offsets"),
+        _dev(row_token, "row_token"), _dev(pair_row, "pair_row"), ctypes.byref(w),
+        _dev(dy_rows, "dy_rows"), _dev(dx, "dx", True), _dev(dw_gate, "dw_gate", True),
+        _dev(dw_up, "dw_up", True), _dev(dw_down, "dw_down", True), int(bool(reuse_transposed)),
+        _dev(ws, "ws"), ws_bytes, _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

@@ -213,21 +213,35 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg) {
   return backward_workspace_layout(*cfg, nullptr).bytes;
 }
 
+moe_status moe_expert_backward(const moe_config* cfg, const void* x,
+                               const int32_t* expert_offsets, const int32_t* row_token,
+                               const int32_t* pair_row, const moe_expert_weights* weights,
+                               const void* dy_rows, void* dx, float* dw_gate, float* dw_up,
+                               float* dw_down, int32_t reuse_transposed, void* ws,
+                               size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_backward(cfg));
+  if (!x || !expert_offsets || !row_token || !pair_row || !dy_rows)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool dw_all = dw_gate && dw_up && dw_down, dw_none = !dw_gate && !dw_up && !dw_down;
+  if (!(dw_all || dw_none) || (!dx && dw_none)) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_weights(*cfg, weights));
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < backward_workspace_layout(*cfg, nullptr).bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const BackwardWorkspace w = backward_workspace_layout(*cfg, ws);
+  return from_hip(launch_expert_backward(*cfg, x, expert_offsets, row_token, pair_row, *weights,
+                                         dy_rows, dx, dw_gate, dw_up, dw_down,
+                                         reuse_transposed != 0, w,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* expert_offsets, const int32_t* row_token,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
                                      const void* dy_rows, void* dx, int32_t reuse_transposed,
                                      void* ws, size_t ws_bytes, void* stream) {
-  MOE_TRY(validate_backward(cfg));
-  if (!x || !expert_offsets || !row_token || !pair_row || !dy_rows || !dx)
-    return MOE_ERR_INVALID_ARGUMENT;
-  MOE_TRY(check_weights(*cfg, weights));
-  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return MOE_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < backward_workspace_layout(*cfg, nullptr).bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const BackwardWorkspace w = backward_workspace_layout(*cfg, ws);
-  return from_hip(launch_expert_backward_input(*cfg, x, expert_offsets, row_token, pair_row,
-                                               *weights, dy_rows, dx, reuse_transposed != 0, w,
-                                               static_cast<hipStream_t>(stream)));
+  if (!dx) return MOE_ERR_INVALID_ARGUMENT;
+  return moe_expert_backward(cfg, x, expert_offsets, row_token, pair_row, weights, dy_rows, dx,
+                             nullptr, nullptr, nullptr, reuse_transposed, ws, ws_bytes, stream);
 }
 
 moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,

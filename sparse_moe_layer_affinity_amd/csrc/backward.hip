@@ -267,17 +267,119 @@ static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, in
   return hipGetLastError();
 }
 
+// Weight gradients of the grouped SwiGLU experts, one 64 x 64 fp32 output tile of one
+// expert per workgroup, summed over that expert's rows in row order (fp32 FMAs):
+//   C[g][m][n] = sum_r A[r][m] * Bv(r, n)
+// A rows at A + r * lda; Bv(r, n) = B[r][n] (plain), x[token of r][n] (gather), or
+// silu(a) * b with a = B[r][n] and b = B[r][boff + n] (the forward's h, from the
+// pre-activations).  Each expert's row range comes from the device offsets, so the
+// host needs no row counts; experts without rows get zeros.  The shared experts'
+// tiles (T rows each) are dispatched first.
+enum { kWgPlainB = 0, kWgGatherB = 1, kWgSwigluB = 2 };
+struct WgradArgs {
+  const uint16_t* A;
+  long long lda;
+  const uint16_t* B;
+  long long ldb;
+  int boff;
+  const int32_t* offsets;
+  const int32_t* row_token;
+  int T, TK, E, Ns, M, N;
+  float* C;                                 // [E+Ns][M][N]
+};
+
+__device__ __forceinline__ void bf16x4_to_f32(uint2 raw, float f[4]) {
+  f[0] = bf16_bits_to_f32(raw.x & 0xffffu);
+  f[1] = bf16_bits_to_f32(raw.x >> 16);
+  f[2] = bf16_bits_to_f32(raw.y & 0xffffu);
+  f[3] = bf16_bits_to_f32(raw.y >> 16);
+}
+
+template <int BMODE>
+__global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
+  __shared__ __attribute__((aligned(16))) float As[16][68];
+  __shared__ __attribute__((aligned(16))) float Bs[16][68];
+  const int G = p.E + p.Ns;
+  const int g = (int(blockIdx.z) + p.E) % G;          // shared experts first
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  int r0, r1;
+  if (g < p.E) {
+    r0 = p.offsets[g];
+    r1 = p.offsets[g + 1];
+  } else {
+    r0 = p.TK + (g - p.E) * p.T;
+    r1 = r0 + p.T;
+  }
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const int lr = tid / 16, lc = (tid % 16) * 4;      // loader: row lr, columns lc..lc+3
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int rb = r0; rb < r1; rb += 16) {
+    const int r = rb + lr;
+    float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < r1) {
+      bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.A + size_t(r) * p.lda + m0 + lc), av);
+      if (BMODE == kWgGatherB) {
+        const int t = r < p.TK ? p.row_token[r] : (r - p.TK) % p.T;
+        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.B + size_t(t) * p.ldb + n0 + lc), bv);
+      } else if (BMODE == kWgSwigluB) {
+        const uint16_t* pa = p.B + size_t(r) * p.ldb + n0 + lc;
+        float a4[4], b4[4];
+        bf16x4_to_f32(*reinterpret_cast<const uint2*>(pa), a4);
+        bf16x4_to_f32(*reinterpret_cast<const uint2*>(pa + p.boff), b4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[i] = a4[i] * (1.0f / (1.0f + expf(-a4[i]))) * b4[i];
+      } else {
+        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.B + size_t(r) * p.ldb + n0 + lc), bv);
+      }
+    }
+    __syncthreads();                        // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      As[lr][lc + i] = av[i];
+      Bs[lr][lc + i] = bv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&As[k][ty * 4]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
+      const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+  }
+  float* c = p.C + size_t(g) * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<float4*>(c + size_t(m0 + ty * 4 + i) * p.N + n0 + tx * 4) =
+        make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+}
+
+template <int BMODE>
+static hipError_t launch_wgrad(const WgradArgs& p, hipStream_t st) {
+  hipLaunchKernelGGL(expert_wgrad<BMODE>, dim3(p.N / 64, p.M / 64, p.E + p.Ns), dim3(256), 0, st,
+                     p);
+  return hipGetLastError();
+}
+
 // Input gradient of the grouped SwiGLU experts (bf16), on the forward's row layout:
 //   a | b   = gathered x rows times W_gate^T | W_up^T      (recomputed, plain GEMMs)
 //   dh      = dy_rows times W_down                         (B = W_down^T per expert)
 //   da | db = SwiGLU backward of (a, b, dh)
 //   dX      = [da | db] times [W_gate ; W_up]              (B = [W_gate^T | W_up^T])
 //   dx      = sum of dX over each token's rows              (the combine, unit gates)
-hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
-                                        const int32_t* offsets, const int32_t* row_token,
-                                        const int32_t* pair_row, const moe_expert_weights& wt,
-                                        const void* dy_rows, void* dx, bool reuse_transposed,
-                                        const BackwardWorkspace& ws, hipStream_t s) {
+hipError_t launch_expert_backward(const moe_config& c, const void* x, const int32_t* offsets,
+                                  const int32_t* row_token, const int32_t* pair_row,
+                                  const moe_expert_weights& wt, const void* dy_rows, void* dx,
+                                  float* dw_gate, float* dw_up, float* dw_down,
+                                  bool reuse_transposed, const BackwardWorkspace& ws,
+                                  hipStream_t s) {
   const int T = c.num_tokens, K = c.top_k, Ns = c.num_shared, E = c.num_experts;
   const int H = c.hidden, I = c.inter, TK = T * K, rows = TK + T * Ns, G = E + Ns;
   hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.sched, ws.sched_n, s);
@@ -337,6 +439,38 @@ hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
   err = launch_swiglu(false, SwigluArgs{ws.ab, ws.ab + I, ws.dh, ws.dab, ws.dab + I, I2, I2, I,
                                         I2, I2, rows, I}, s);
   if (err != hipSuccess) return err;
+  if (dw_down) {
+    // dW_down = dy^T h, dW_gate = da^T u, dW_up = db^T u over each expert's rows
+    WgradArgs w{};
+    w.offsets = offsets;
+    w.row_token = row_token;
+    w.T = T;
+    w.TK = TK;
+    w.E = E;
+    w.Ns = Ns;
+    w.A = static_cast<const uint16_t*>(dy_rows);
+    w.lda = H;
+    w.B = ws.ab;
+    w.ldb = 2LL * I;
+    w.boff = I;
+    w.M = H;
+    w.N = I;
+    w.C = dw_down;
+    if ((err = launch_wgrad<kWgSwigluB>(w, s)) != hipSuccess) return err;
+    w.A = ws.dab;
+    w.lda = 2LL * I;
+    w.B = static_cast<const uint16_t*>(x);
+    w.ldb = H;
+    w.boff = 0;
+    w.M = I;
+    w.N = H;
+    w.C = dw_gate;
+    if ((err = launch_wgrad<kWgGatherB>(w, s)) != hipSuccess) return err;
+    w.A = ws.dab + I;
+    w.C = dw_up;
+    if ((err = launch_wgrad<kWgGatherB>(w, s)) != hipSuccess) return err;
+  }
+  if (!dx) return hipSuccess;
   // dX = [da | db] [W_gate ; W_up]
   GemmArgs q = d;
   q.A = ws.dab;

@@ -101,11 +101,12 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dy, const vo
                                    void* dy_rows, hipStream_t s);
 hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void* b,
                                   const void* dh, int rows, void* da, void* db, hipStream_t s);
-hipError_t launch_expert_backward_input(const moe_config& c, const void* x,
-                                        const int32_t* offsets, const int32_t* row_token,
-                                        const int32_t* pair_row, const moe_expert_weights& wt,
-                                        const void* dy_rows, void* dx, bool reuse_transposed,
-                                        const BackwardWorkspace& ws, hipStream_t s);
+hipError_t launch_expert_backward(const moe_config& c, const void* x, const int32_t* offsets,
+                                  const int32_t* row_token, const int32_t* pair_row,
+                                  const moe_expert_weights& wt, const void* dy_rows, void* dx,
+                                  float* dw_gate, float* dw_up, float* dw_down,
+                                  bool reuse_transposed, const BackwardWorkspace& ws,
+                                  hipStream_t s);
 hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
                                 const float* dgate, float* grad, int accumulate, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                           "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
                           "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
                           "moe_gate_backward", "moe_swiglu_backward", "moe_backward_workspace_bytes",
-                          "moe_expert_backward_input", "moe_status_string"}
+                          "moe_expert_backward_input", "moe_expert_backward", "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -212,6 +212,14 @@ def test_expert_backward_argument_checks():
     assert call(ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
     assert call(ws=A + 32) == B.MOE_ERR_INVALID_ARGUMENT
     assert call(conf=cfg(w="e4m3")) == B.MOE_ERR_UNSUPPORTED
+
+    def full(dx=A, dw=(A, A, A)):
+        return code_of(B.moe_expert_backward, c, A, A, A, A, dense, A, dx, *dw, A, need,
+                       stream=0)
+
+    assert full(dx=0, dw=(0, 0, 0)) == B.MOE_ERR_INVALID_ARGUMENT       # nothing requested
+    assert full(dw=(A, 0, A)) == B.MOE_ERR_INVALID_ARGUMENT             # all or none
+    assert full(dw=(0, 0, A)) == B.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_weight_scale_pointer_rules():

@@ -175,3 +175,58 @@ def test_expert_backward_input(name, over):
     err = np.abs(got - want).max() / np.abs(want).max()
     log(f"  dx rel err {err:.2e} on {n} tokens")
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("name,over,n_check", [("decode_bf16", dict(T=37, **SMALL), None),
+                                               ("decode_bf16", dict(T=29, Ns=2, **SMALL), None),
+                                               ("decode_bf16", dict(T=3, **SMALL), None),
+                                               ("decode_bf16", {}, 4)])
+def test_expert_backward_weights(name, over, n_check):
+    """Weight gradients of every expert (small shapes) or of the shared expert and a few
+    routed ones (full decode shape, among them one with no rows when there is one), and
+    dx from the same call equal to moe_expert_backward_input's.  Bound 2e-2 of each
+    matrix's largest magnitude (bf16 pre-activations and gradients, fp32 sums)."""
+    from gpu_harness import config_of, expert_getter, inputs_on_gpu, oracle_route
+    cfg = workloads.get(name).replace(**over)
+    log(f"expert backward weights {name} {over}")
+    d = inputs_on_gpu(cfg)
+    r = oracle_route(cfg, d)
+    T, K, Ns, E, H, I = cfg.T, cfg.K, cfg.Ns, cfg.E, cfg.hidden, cfg.inter
+    load, off, row_token, pair_row = oracle.permute(r.idx, E)
+    dy_rows = workloads.make_dense((cfg.rows, H), "bf16", seed=T + 7, name="dy_rows")
+    c = config_of(cfg)
+    ws = torch.empty(moe.moe_backward_workspace_bytes(c), dtype=torch.uint8, device="cuda")
+    i32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).cuda()
+    weights = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
+    G = E + Ns
+    dwg = torch.full((G, I, H), 7.0, device="cuda")
+    dwu = torch.full((G, I, H), 7.0, device="cuda")
+    dwd = torch.full((G, H, I), 7.0, device="cuda")
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    dx_only = torch.empty_like(dx)
+    args = (c, d["x"], i32(off), i32(row_token), i32(pair_row), weights, dy_rows.cuda())
+    moe.moe_expert_backward(*args, dx, dwg, dwu, dwd, ws)
+    moe.moe_expert_backward_input(*args, dx_only, ws, reuse_transposed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_only)
+    expert_of_row = np.concatenate([np.repeat(np.arange(E), np.diff(off)),
+                                    np.repeat(np.arange(E, G), T)])
+    if n_check is None:
+        check = list(range(G))
+    else:
+        empty = [e for e in range(E) if load[e] == 0][:1]
+        busy = list(np.argsort(-load)[:n_check - len(empty)])
+        check = sorted(set(empty + busy + list(range(E, G))))
+    want = oracle.expert_weight_backward(d["x"], row_token, T, K, dy_rows, expert_getter(cfg, d),
+                                         expert_of_row, check)
+    worst = 0.0
+    for e in check:
+        for got, ref in zip((dwg[e], dwu[e], dwd[e]), want[e]):
+            got = got.cpu().double().numpy()
+            scale = np.abs(ref).max()
+            if scale == 0.0:
+                assert np.all(got == 0.0)
+                continue
+            worst = max(worst, np.abs(got - ref).max() / scale)
+    log(f"  {len(check)} experts checked, worst rel err {worst:.2e}")
+    assert worst <= 2e-2
