@@ -46,11 +46,12 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   backward         linearity in dy
   expert_weight_   pinned: central finite differences of the same sum in the weights
   backward
+  router_backward  pinned: the adjoint identities of z = x W_r^T in x and in W_r
 """
 from .moe_layer import (RouteResult, affinities, route, permute, expert_ffn, layer_output,
                         bias_update, silu)
 from .backward import (combine_backward, expert_input_backward, expert_weight_backward,
-                       gate_backward, swiglu_backward)
+                       gate_backward, router_backward, swiglu_backward)
 from .balance import balance_loss, balance_loss_grad_logits
 from .e4m3 import (e4m3_table, e4m3_encode_rne, quantize_1x128, dequantize_1x128,
                    dequantize_blocks_128, expert_ffn_fp8_emulated, pow2_scale,
@@ -60,4 +61,5 @@ __all__ = ["RouteResult", "affinities", "route", "permute", "expert_ffn", "layer
            "bias_update", "silu", "e4m3_table", "e4m3_encode_rne", "quantize_1x128",
            "dequantize_1x128", "dequantize_blocks_128", "expert_ffn_fp8_emulated", "pow2_scale", "quantize_1x128_pow2", "expert_ffn_fp8_pow2_emulated",
            "balance_loss", "balance_loss_grad_logits", "combine_backward", "gate_backward",
-           "swiglu_backward", "expert_input_backward", "expert_weight_backward"]
+           "swiglu_backward", "expert_input_backward", "expert_weight_backward",
+           "router_backward"]

@@ -29,7 +29,8 @@ because the gates sum to one); the SwiGLU backward by central finite differences
 sum(dh * h) and the closed forms at a = 0 (silu' = 1/2, silu = 0); the expert input
 gradient by central finite differences of sum_r <dy_r, FFN_e(x_t)> with respect to x
 and by linearity in dy; the expert weight gradients by central finite differences of
-the same sum with respect to weight entries.
+the same sum with respect to weight entries; the router backward by the adjoint
+identity <dz, x' W_r^T> = <dx, x'> and <dz, x W'^T> = <dW_r, W'>.
 """
 from __future__ import annotations
 
@@ -153,4 +154,13 @@ def expert_weight_backward(x, row_token, num_tokens: int, top_k: int, dy_rows, g
         da, db = swiglu_backward(a, b, dh)
         out[int(e)] = (da.T @ u, db.T @ u, dY[rs].T @ h)
     return out
+
+
+def router_backward(x, w_router, grad_logits):
+    """Backward of the router logits z = x W_r^T for a logit gradient dz [T, E]:
+    dx = dz W_r [T, H] and dW_r = dz^T x [E, H], float64."""
+    x = _f64(x)
+    w = _f64(w_router)
+    dz = _f64(grad_logits)
+    return dz @ w, dz.T @ x
 

@@ -193,3 +193,17 @@ def test_expert_weight_backward_matches_central_differences():
                 fd = (loss(plus) - loss(minus)) / (2 * h)
                 np.testing.assert_allclose(grads[e][m][idx], fd, rtol=1e-6, atol=1e-8)
 
+
+def test_router_backward_adjoint_identities():
+    rng = np.random.default_rng(14)
+    x, w, dz = rng.normal(size=(6, 5)), rng.normal(size=(4, 5)), rng.normal(size=(6, 4))
+    dx, dw = oracle.router_backward(x, w, dz)
+    x2, w2 = rng.normal(size=x.shape), rng.normal(size=w.shape)
+    np.testing.assert_allclose(np.sum(dz * (x2 @ w.T)), np.sum(dx * x2), rtol=1e-12)
+    np.testing.assert_allclose(np.sum(dz * (x @ w2.T)), np.sum(dw * w2), rtol=1e-12)
+    # hand case: one token, one expert: z = <x, w>, dz = 2 -> dx = 2 w, dW = 2 x
+    dx1, dw1 = oracle.router_backward(np.array([[1.0, -2.0]]), np.array([[3.0, 0.5]]),
+                                      np.array([[2.0]]))
+    np.testing.assert_array_equal(dx1, [[6.0, 1.0]])
+    np.testing.assert_array_equal(dw1, [[2.0, -4.0]])
+
