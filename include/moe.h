@@ -2,7 +2,8 @@
  * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward, with the
  * training-side pieces next to it: router affinities, the sequence-wise balance loss
  * and its gradient, the backward of the combine, of the gates and of the SwiGLU
- * activation, and the input and weight gradients of the experts.
+ * activation, the input and weight gradients of the experts, and the backward of the
+ * router logits.
  *
  * The layer (DeepSeek-V3 technical report summary "深度解读报告", section 2.2):
  *
@@ -265,6 +266,17 @@ moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
                                      const void* dy_rows, void* dx, int32_t reuse_transposed,
                                      void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the router logits z = x w_router^T ("深度解读报告" section 2.2, the
+ * affinity logits, differentiated) for a logit gradient grad_logits [T, E] fp32 (the
+ * sum of moe_gate_backward's and moe_balance_loss's):
+ *   dx[t, c]        = sum_e grad_logits[t, e] * w_router[e, c]     [T, hidden] fp32 out
+ *   dw_router[e, c] = sum_t grad_logits[t, e] * x[t, c]            [E, hidden] fp32 out
+ * fp32 sums in a fixed order; either output may be NULL, not both.  x [T, hidden] and
+ * w_router [E, hidden] BF16 (act_dtype BF16 only; E a multiple of 4). */
+moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* grad_logits, float* dx, float* dw_router,
+                               void* stream);
 
 /* Input and weight gradients of the grouped SwiGLU experts together
  * ("深度解读报告" section 2.2, differentiated): dx as in moe_expert_backward_input

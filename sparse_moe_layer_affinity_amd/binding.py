@@ -62,6 +62,7 @@ _SIGS = {
     "moe_gate_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "moe_swiglu_backward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_backward_workspace_bytes": (ctypes.c_size_t, [_CFG]),
+    "moe_router_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
     "moe_expert_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.POINTER(MoeExpertWeights),
                                            _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                            ctypes.c_size_t, _P]),
@@ -259,6 +260,13 @@ def moe_expert_backward(cfg, x, expert_offsets, row_token, pair_row, weights: di
         _dev(dy_rows, "dy_rows"), _dev(dx, "dx", True), _dev(dw_gate, "dw_gate", True),
         _dev(dw_up, "dw_up", True), _dev(dw_down, "dw_down", True), int(bool(reuse_transposed)),
         _dev(ws, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_router_backward(cfg, x, w_router, grad_logits, dx, dw_router, stream=None):
+    _check("moe_router_backward", lib().moe_router_backward(
+        ctypes.byref(cfg), _dev(x, "x"), _dev(w_router, "w_router"),
+        _dev(grad_logits, "grad_logits"), _dev(dx, "dx", True), _dev(dw_router, "dw_router", True),
+        _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

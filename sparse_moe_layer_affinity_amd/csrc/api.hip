@@ -244,6 +244,16 @@ moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                              nullptr, nullptr, nullptr, reuse_transposed, ws, ws_bytes, stream);
 }
 
+moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* grad_logits, float* dx, float* dw_router,
+                               void* stream) {
+  MOE_TRY(validate(cfg));
+  if (!x || !w_router || !grad_logits || (!dx && !dw_router)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->act_dtype != MOE_BF16 || cfg->num_experts % 4) return MOE_ERR_UNSUPPORTED;
+  return from_hip(launch_router_backward(*cfg, x, w_router, grad_logits, dx, dw_router,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,
                                const void* dh, int32_t rows, void* da, void* db, void* stream) {
   MOE_TRY(validate(cfg));

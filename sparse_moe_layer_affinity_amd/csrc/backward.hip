@@ -276,8 +276,11 @@ static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, in
 // host needs no row counts; experts without rows get zeros.  The shared experts'
 // tiles (T rows each) are dispatched first.
 enum { kWgPlainB = 0, kWgGatherB = 1, kWgSwigluB = 2 };
+// A operand: bf16 rows [r][m], fp32 rows [r][m], or fp32 stored [m][r]
+enum { kWgAbf16 = 0, kWgAf32 = 1, kWgAf32T = 2 };
 struct WgradArgs {
   const uint16_t* A;
+  const float* Af;
   long long lda;
   const uint16_t* B;
   long long ldb;
@@ -295,7 +298,7 @@ __device__ __forceinline__ void bf16x4_to_f32(uint2 raw, float f[4]) {
   f[3] = bf16_bits_to_f32(raw.y >> 16);
 }
 
-template <int BMODE>
+template <int BMODE, int AMODE>
 __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
   __shared__ __attribute__((aligned(16))) float As[16][68];
   __shared__ __attribute__((aligned(16))) float Bs[16][68];
@@ -320,8 +323,21 @@ __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
   for (int rb = r0; rb < r1; rb += 16) {
     const int r = rb + lr;
     float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (r < r1) {
-      bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.A + size_t(r) * p.lda + m0 + lc), av);
+    // N, and M for the row-major A forms, are multiples of 4: a 4-element group is
+    // wholly inside or outside; the transposed fp32 A (M = tokens) is guarded per row
+    if (r < r1 && m0 + lc < p.M) {
+      if (AMODE == kWgAbf16) {
+        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.A + size_t(r) * p.lda + m0 + lc), av);
+      } else if (AMODE == kWgAf32) {
+        const float4 f = *reinterpret_cast<const float4*>(p.Af + size_t(r) * p.lda + m0 + lc);
+        av[0] = f.x; av[1] = f.y; av[2] = f.z; av[3] = f.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          av[i] = m0 + lc + i < p.M ? p.Af[size_t(m0 + lc + i) * p.lda + r] : 0.0f;
+      }
+    }
+    if (r < r1 && n0 + lc < p.N) {
       if (BMODE == kWgGatherB) {
         const int t = r < p.TK ? p.row_token[r] : (r - p.TK) % p.T;
         bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.B + size_t(t) * p.ldb + n0 + lc), bv);
@@ -355,17 +371,52 @@ __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
     }
   }
   float* c = p.C + size_t(g) * p.M * p.N;
+  if (n0 + tx * 4 >= p.N) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<float4*>(c + size_t(m0 + ty * 4 + i) * p.N + n0 + tx * 4) =
-        make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    if (m0 + ty * 4 + i < p.M)
+      *reinterpret_cast<float4*>(c + size_t(m0 + ty * 4 + i) * p.N + n0 + tx * 4) =
+          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
 }
 
-template <int BMODE>
+template <int BMODE, int AMODE = kWgAbf16>
 static hipError_t launch_wgrad(const WgradArgs& p, hipStream_t st) {
-  hipLaunchKernelGGL(expert_wgrad<BMODE>, dim3(p.N / 64, p.M / 64, p.E + p.Ns), dim3(256), 0, st,
-                     p);
+  hipLaunchKernelGGL((expert_wgrad<BMODE, AMODE>),
+                     dim3(ceil_div(p.N, 64), ceil_div(p.M, 64), p.E + p.Ns), dim3(256), 0, st, p);
   return hipGetLastError();
+}
+
+// Backward of the router logits z = x W_r^T for a logit gradient dz [T, E] (fp32):
+//   dx = dz W_r  [T, H]   (rows r = experts, A = dz read transposed)
+//   dW = dz^T x  [E, H]   (rows r = tokens)
+// each as one row group through the weight-gradient kernel, fp32 sums in row order.
+hipError_t launch_router_backward(const moe_config& c, const void* x, const void* w_router,
+                                  const float* dz, float* dx, float* dw, hipStream_t st) {
+  const int T = c.num_tokens, E = c.num_experts, H = c.hidden;
+  WgradArgs w{};
+  w.E = 0;                                  // one group: "shared" rows [0, rows)
+  w.Ns = 1;
+  w.TK = 0;
+  w.Af = dz;
+  w.lda = E;
+  w.ldb = H;
+  w.N = H;
+  hipError_t err = hipSuccess;
+  if (dx) {
+    w.T = E;
+    w.M = T;
+    w.B = static_cast<const uint16_t*>(w_router);
+    w.C = dx;
+    if ((err = launch_wgrad<kWgPlainB, kWgAf32T>(w, st)) != hipSuccess) return err;
+  }
+  if (dw) {
+    w.T = T;
+    w.M = E;
+    w.B = static_cast<const uint16_t*>(x);
+    w.C = dw;
+    if ((err = launch_wgrad<kWgPlainB, kWgAf32>(w, st)) != hipSuccess) return err;
+  }
+  return err;
 }
 
 // Input gradient of the grouped SwiGLU experts (bf16), on the forward's row layout:

@@ -107,6 +107,8 @@ hipError_t launch_expert_backward(const moe_config& c, const void* x, const int3
                                   float* dw_gate, float* dw_up, float* dw_down,
                                   bool reuse_transposed, const BackwardWorkspace& ws,
                                   hipStream_t s);
+hipError_t launch_router_backward(const moe_config& c, const void* x, const void* w_router,
+                                  const float* dz, float* dx, float* dw, hipStream_t s);
 hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
                                 const float* dgate, float* grad, int accumulate, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,

@@ -34,7 +34,8 @@ def test_library_exports_every_declared_symbol():
                           "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
                           "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
                           "moe_gate_backward", "moe_swiglu_backward", "moe_backward_workspace_bytes",
-                          "moe_expert_backward_input", "moe_expert_backward", "moe_status_string"}
+                          "moe_expert_backward_input", "moe_expert_backward", "moe_router_backward",
+                          "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -220,6 +221,13 @@ def test_expert_backward_argument_checks():
     assert full(dx=0, dw=(0, 0, 0)) == B.MOE_ERR_INVALID_ARGUMENT       # nothing requested
     assert full(dw=(A, 0, A)) == B.MOE_ERR_INVALID_ARGUMENT             # all or none
     assert full(dw=(0, 0, A)) == B.MOE_ERR_INVALID_ARGUMENT
+    rb = B.moe_router_backward
+    assert code_of(rb, c, A, A, A, 0, 0, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(rb, c, 0, A, A, A, A, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(rb, c, A, A, 0, A, None, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(rb, cfg(act="f32", w="f32", hidden=256, inter=128, T=64, E=16, K=4, G=4, M=2),
+                   A, A, A, A, A, stream=0) == B.MOE_ERR_UNSUPPORTED
+    assert code_of(rb, cfg(E=250, G=10, M=4), A, A, A, A, A, stream=0) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_weight_scale_pointer_rules():

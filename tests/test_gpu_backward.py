@@ -230,3 +230,36 @@ def test_expert_backward_weights(name, over, n_check):
             worst = max(worst, np.abs(got - ref).max() / scale)
     log(f"  {len(check)} experts checked, worst rel err {worst:.2e}")
     assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("name,over", [("decode_bf16", dict(T=37, **SMALL)),
+                                       ("decode_bf16", dict(T=3, **SMALL)),
+                                       ("decode_bf16", {}),
+                                       ("prefill_bf16", {})])
+def test_router_backward(name, over):
+    """dx = dz W_r (sampled tokens) and dW_r = dz^T x (all experts) against the oracle on
+    a seeded logit gradient; bound 5e-5 of the largest magnitude (fp32 products of the
+    fp32 gradient and bf16 operands, sequential fp32 sums over up to T = 8192 terms:
+    about eps * sqrt(T) relative to the result, with headroom)."""
+    cfg = workloads.get(name).replace(**over)
+    log(f"router backward {name} {over}")
+    T, E, H = cfg.T, cfg.E, cfg.hidden
+    x = workloads.make_tokens(cfg)
+    w_r = workloads.make_router(cfg)
+    dz = workloads.make_dense((T, E), "f32", std=1e-3, seed=T, name="grad_logits")
+    from gpu_harness import config_of
+    c = config_of(cfg)
+    dx = torch.full((T, H), 7.0, device="cuda")
+    dw = torch.full((E, H), 7.0, device="cuda")
+    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), dx, dw)
+    dx_only = torch.empty_like(dx)
+    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), dx_only, None)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_only)
+    toks = workloads.sample_rows(T, 256, seed=6).numpy()
+    want_dx, _ = oracle.router_backward(x[toks], w_r, dz[toks])
+    _, want_dw = oracle.router_backward(x, w_r, dz)
+    e_dx = np.abs(dx.cpu().double().numpy()[toks] - want_dx).max() / np.abs(want_dx).max()
+    e_dw = np.abs(dw.cpu().double().numpy() - want_dw).max() / np.abs(want_dw).max()
+    log(f"  dx rel err {e_dx:.2e}, dW_r rel err {e_dw:.2e}")
+    assert e_dx <= 5e-5 and e_dw <= 5e-5
