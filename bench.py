@@ -154,7 +154,8 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
     writes the [T, E] logit gradient; SwiGLU backward reads three [rows, inter] arrays
     and writes two.  The experts' input gradient (bf16) is timed on the step's own
     inputs and the combine backward's row gradients, reported with its GEMM FLOPs, and
-    their weight gradients with the a, b and dh GEMMs they need (transposes reused)."""
+    their weight gradients with the a, b and dh GEMMs they need (transposes reused), and
+    the router logits' backward (dx and dW_r, 4 T E H flops)."""
     import torch
     T, E, K, H = cfg.T, cfg.E, cfg.K, cfg.hidden
     eb = 4 if cfg.act == "f32" else 2
@@ -176,6 +177,12 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
 
     us_comb = timed(lambda: moe.moe_combine_backward(c, y, y_rows, pair_row, gate, dgate, dy_rows))
     us_gate = timed(lambda: moe.moe_gate_backward(c, scores, idx, dgate, grad))
+    us_rb = None
+    if cfg.act != "f32":
+        dxr = torch.empty((T, H), device="cuda")
+        dwr = torch.empty((E, H), device="cuda")
+        us_rb = timed(lambda: moe.moe_router_backward(c, d["x"], d["w_router"], grad, dxr, dwr))
+        del dxr, dwr
     # SwiGLU backward over every grouped row: seeded stand-ins for the pre-activations
     # and the gradient of h (the forward does not keep the pre-activations)
     g = torch.Generator(device="cuda")
@@ -232,6 +239,9 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
             "combine_backward_frac_hbm": round(gb_comb / HBM_PEAK, 4),
             "gate_backward_us": round(us_gate, 2), "gate_backward_bytes": b_gate,
             "gate_backward_GBps": round(gb_gate, 1),
+            "router_backward_us": None if us_rb is None else round(us_rb, 1),
+            "router_backward_tflops": None if us_rb is None else
+            round(4.0 * T * E * H / (us_rb * 1e-6) / 1e12, 1),
             "swiglu_backward_us": round(us_swi, 2), "swiglu_backward_bytes": b_swi,
             "swiglu_backward_GBps": round(gb_swi, 1),
             "swiglu_backward_frac_hbm": round(gb_swi / HBM_PEAK, 4), **(ex or {})}
