@@ -273,7 +273,7 @@ moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
  *   dx[t, c]        = sum_e grad_logits[t, e] * w_router[e, c]     [T, hidden] fp32 out
  *   dw_router[e, c] = sum_t grad_logits[t, e] * x[t, c]            [E, hidden] fp32 out
  * fp32 sums in a fixed order; either output may be NULL, not both.  x [T, hidden] and
- * w_router [E, hidden] BF16 (act_dtype BF16 only; E a multiple of 4). */
+ * w_router [E, hidden] BF16 (act_dtype BF16 only; E a multiple of 8). */
 moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
                                const float* grad_logits, float* dx, float* dw_router,
                                void* stream);

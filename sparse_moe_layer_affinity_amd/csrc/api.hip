@@ -249,7 +249,7 @@ moe_status moe_router_backward(const moe_config* cfg, const void* x, const void*
                                void* stream) {
   MOE_TRY(validate(cfg));
   if (!x || !w_router || !grad_logits || (!dx && !dw_router)) return MOE_ERR_INVALID_ARGUMENT;
-  if (cfg->act_dtype != MOE_BF16 || cfg->num_experts % 4) return MOE_ERR_UNSUPPORTED;
+  if (cfg->act_dtype != MOE_BF16 || cfg->num_experts % 8) return MOE_ERR_UNSUPPORTED;
   return from_hip(launch_router_backward(*cfg, x, w_router, grad_logits, dx, dw_router,
                                          static_cast<hipStream_t>(stream)));
 }

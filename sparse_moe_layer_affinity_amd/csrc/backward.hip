@@ -267,8 +267,9 @@ static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, in
   return hipGetLastError();
 }
 
-// Weight gradients of the grouped SwiGLU experts, one 64 x 64 fp32 output tile of one
-// expert per workgroup, summed over that expert's rows in row order (fp32 FMAs):
+// Weight gradients of the grouped SwiGLU experts, one fp32 output tile (128 x 128, 8 x 8
+// per thread; 64 x 64 for small outputs) of one expert per workgroup, summed over that
+// expert's rows in row order (fp32 FMAs):
 //   C[g][m][n] = sum_r A[r][m] * Bv(r, n)
 // A rows at A + r * lda; Bv(r, n) = B[r][n] (plain), x[token of r][n] (gather), or
 // silu(a) * b with a = B[r][n] and b = B[r][boff + n] (the forward's h, from the
@@ -298,13 +299,14 @@ __device__ __forceinline__ void bf16x4_to_f32(uint2 raw, float f[4]) {
   f[3] = bf16_bits_to_f32(raw.y >> 16);
 }
 
-template <int BMODE, int AMODE>
+template <int BMODE, int AMODE, int kT>
 __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
-  __shared__ __attribute__((aligned(16))) float As[16][68];
-  __shared__ __attribute__((aligned(16))) float Bs[16][68];
+  constexpr int kU = kT / 16, kPitch = kT + 4;        // kU x kU outputs per thread
+  __shared__ __attribute__((aligned(16))) float As[16][kPitch];
+  __shared__ __attribute__((aligned(16))) float Bs[16][kPitch];
   const int G = p.E + p.Ns;
   const int g = (int(blockIdx.z) + p.E) % G;          // shared experts first
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   int r0, r1;
   if (g < p.E) {
     r0 = p.offsets[g];
@@ -314,75 +316,100 @@ __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
     r1 = r0 + p.T;
   }
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  const int lr = tid / 16, lc = (tid % 16) * 4;      // loader: row lr, columns lc..lc+3
-  float acc[4][4];
+  const int lr = tid / 16, lc = (tid % 16) * kU;     // loader: row lr, kU columns from lc
+  float acc[kU][kU];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kU; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int j = 0; j < kU; ++j) acc[i][j] = 0.0f;
   for (int rb = r0; rb < r1; rb += 16) {
     const int r = rb + lr;
-    float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
-    // N, and M for the row-major A forms, are multiples of 4: a 4-element group is
+    float av[kU], bv[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) av[i] = bv[i] = 0.0f;
+    // N, and M for the row-major A forms, are multiples of 8: a group of kU elements is
     // wholly inside or outside; the transposed fp32 A (M = tokens) is guarded per row
     if (r < r1 && m0 + lc < p.M) {
       if (AMODE == kWgAbf16) {
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.A + size_t(r) * p.lda + m0 + lc), av);
+#pragma unroll
+        for (int q = 0; q < kU / 4; ++q)
+          bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.A + size_t(r) * p.lda + m0 + lc + 4 * q),
+                        av + 4 * q);
       } else if (AMODE == kWgAf32) {
-        const float4 f = *reinterpret_cast<const float4*>(p.Af + size_t(r) * p.lda + m0 + lc);
-        av[0] = f.x; av[1] = f.y; av[2] = f.z; av[3] = f.w;
+#pragma unroll
+        for (int q = 0; q < kU / 4; ++q) {
+          const float4 f =
+              *reinterpret_cast<const float4*>(p.Af + size_t(r) * p.lda + m0 + lc + 4 * q);
+          av[4 * q] = f.x; av[4 * q + 1] = f.y; av[4 * q + 2] = f.z; av[4 * q + 3] = f.w;
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kU; ++i)
           av[i] = m0 + lc + i < p.M ? p.Af[size_t(m0 + lc + i) * p.lda + r] : 0.0f;
       }
     }
     if (r < r1 && n0 + lc < p.N) {
+      const uint16_t* pb;
       if (BMODE == kWgGatherB) {
         const int t = r < p.TK ? p.row_token[r] : (r - p.TK) % p.T;
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.B + size_t(t) * p.ldb + n0 + lc), bv);
-      } else if (BMODE == kWgSwigluB) {
-        const uint16_t* pa = p.B + size_t(r) * p.ldb + n0 + lc;
-        float a4[4], b4[4];
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(pa), a4);
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(pa + p.boff), b4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = a4[i] * (1.0f / (1.0f + expf(-a4[i]))) * b4[i];
+        pb = p.B + size_t(t) * p.ldb + n0 + lc;
       } else {
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.B + size_t(r) * p.ldb + n0 + lc), bv);
+        pb = p.B + size_t(r) * p.ldb + n0 + lc;
+      }
+#pragma unroll
+      for (int q = 0; q < kU / 4; ++q)
+        bf16x4_to_f32(*reinterpret_cast<const uint2*>(pb + 4 * q), bv + 4 * q);
+      if (BMODE == kWgSwigluB) {
+        float bu[kU];
+#pragma unroll
+        for (int q = 0; q < kU / 4; ++q)
+          bf16x4_to_f32(*reinterpret_cast<const uint2*>(pb + p.boff + 4 * q), bu + 4 * q);
+#pragma unroll
+        for (int i = 0; i < kU; ++i) bv[i] = bv[i] * (1.0f / (1.0f + expf(-bv[i]))) * bu[i];
       }
     }
     __syncthreads();                        // the previous chunk's reads are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      As[lr][lc + i] = av[i];
-      Bs[lr][lc + i] = bv[i];
+    for (int q = 0; q < kU / 4; ++q) {
+      *reinterpret_cast<float4*>(&As[lr][lc + 4 * q]) =
+          make_float4(av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]);
+      *reinterpret_cast<float4*>(&Bs[lr][lc + 4 * q]) =
+          make_float4(bv[4 * q], bv[4 * q + 1], bv[4 * q + 2], bv[4 * q + 3]);
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&As[k][ty * 4]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
-      const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+      float a[kU], b[kU];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < kU / 4; ++q) {
+        const float4 fa = *reinterpret_cast<const float4*>(&As[k][ty * kU + 4 * q]);
+        const float4 fb = *reinterpret_cast<const float4*>(&Bs[k][tx * kU + 4 * q]);
+        a[4 * q] = fa.x; a[4 * q + 1] = fa.y; a[4 * q + 2] = fa.z; a[4 * q + 3] = fa.w;
+        b[4 * q] = fb.x; b[4 * q + 1] = fb.y; b[4 * q + 2] = fb.z; b[4 * q + 3] = fb.w;
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < kU; ++i)
+#pragma unroll
+        for (int j = 0; j < kU; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
   }
   float* c = p.C + size_t(g) * p.M * p.N;
-  if (n0 + tx * 4 >= p.N) return;
+  if (n0 + tx * kU >= p.N) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (m0 + ty * 4 + i < p.M)
-      *reinterpret_cast<float4*>(c + size_t(m0 + ty * 4 + i) * p.N + n0 + tx * 4) =
-          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  for (int i = 0; i < kU; ++i)
+    if (m0 + ty * kU + i < p.M) {
+      float4* q = reinterpret_cast<float4*>(c + size_t(m0 + ty * kU + i) * p.N + n0 + tx * kU);
+#pragma unroll
+      for (int u = 0; u < kU / 4; ++u)
+        q[u] = make_float4(acc[i][4 * u], acc[i][4 * u + 1], acc[i][4 * u + 2], acc[i][4 * u + 3]);
+    }
 }
 
-template <int BMODE, int AMODE = kWgAbf16>
+template <int BMODE, int AMODE = kWgAbf16, int TILE = 128>
 static hipError_t launch_wgrad(const WgradArgs& p, hipStream_t st) {
-  hipLaunchKernelGGL((expert_wgrad<BMODE, AMODE>),
-                     dim3(ceil_div(p.N, 64), ceil_div(p.M, 64), p.E + p.Ns), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((expert_wgrad<BMODE, AMODE, TILE>),
+                     dim3(ceil_div(p.N, TILE), ceil_div(p.M, TILE), p.E + p.Ns), dim3(256), 0, st,
+                     p);
   return hipGetLastError();
 }
 
@@ -414,7 +441,8 @@ hipError_t launch_router_backward(const moe_config& c, const void* x, const void
     w.M = E;
     w.B = static_cast<const uint16_t*>(x);
     w.C = dw;
-    if ((err = launch_wgrad<kWgPlainB, kWgAf32>(w, st)) != hipSuccess) return err;
+    // few output tiles (E x H): 64 x 64 tiles keep more workgroups in flight
+    if ((err = launch_wgrad<kWgPlainB, kWgAf32, 64>(w, st)) != hipSuccess) return err;
   }
   return err;
 }
