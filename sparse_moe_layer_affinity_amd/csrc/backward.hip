@@ -1,4 +1,5 @@
-// Backward of the combine, of the gates and of the SwiGLU activation.
+// Backward of the layer: the combine, the gates, the SwiGLU activation, the experts'
+// input and weight gradients, and the router logits.
 //
 // "DeepSeek-V3 Technical Report 深度解读报告", section 2.2: the layer output adds the
 // shared experts' outputs and the routed experts' outputs weighted by the gates
@@ -14,7 +15,10 @@
 // loaded together; the K dot products are summed per thread in column order, then
 // over each wave by a fixed butterfly and over the four waves in order (fixed order,
 // deterministic).  gate_backward: one wave per token.  swiglu_backward: elementwise
-// over the [rows, inter] pre-activations of the SwiGLU experts.
+// over the [rows, inter] pre-activations of the SwiGLU experts.  The experts' input
+// gradient reuses the forward's expert GEMM (plain mode) on per-expert transposed
+// weight copies (transpose_experts); their weight gradients and the router logits'
+// backward run in expert_wgrad, which reads each expert's row range on the device.
 #include "gemm_common.h"
 
 namespace moe {
