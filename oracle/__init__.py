@@ -31,6 +31,11 @@ Parity status per function (what pins it; the tests under ``tests/`` hold the pi
   quantize_1x128_pow2      float32 sweep against an integer-exponent search), hand
                    values (448 -> 1, 449 -> 2, 1 -> 2^-8), blocks of e4m3 values times
                    a power of two quantise exactly, the half-step bound
+  expert_ffn_fp8_  pinned: a hand-worked one-token expert over two 1x128 tiles in each
+  emulated (and    GEMM, every e4m3 code and scale derived by hand (both scale rules);
+  _pow2_emulated)  planted mistakes (h or x left unquantised, no bf16 rounding of h,
+                   power-of-two scales on the amax/448 path, one scale per row, gate
+                   and up swapped) each move a hand-derived output
   balance_loss /   formula is a reading (the pages name the sequence-wise loss but
   balance_loss_    print no formula): pinned by hand-computed cases, the closed
   grad_logits      forms of perfect balance, uniform affinities and full

@@ -238,3 +238,101 @@ def test_fp8_pow2_emulated_close_to_exact():
     rel = np.abs(emu - exact).max() / np.abs(exact).max()
     assert 1e-4 < rel < 0.1
     assert not np.array_equal(emu, oracle.expert_ffn_fp8_emulated(u, wg, wu, wd))
+
+
+# ---- hand-worked FP8 expert (devpress page, section 2: 1x128 activation tiles) ------
+# One token, hidden = inter = 256: two 128-wide K blocks in each GEMM, so each tile's
+# own scale matters.  Every value below is derived by hand (the derivation is in the
+# comments); the oracle must reproduce them exactly.
+#
+# x, block 0: x0 = 14 is the block maximum, so s = 14 / 448 = 2^-5 (exact) and the
+#   quotients are x / 2^-5: 14 -> 448 (exact), 0.08 -> 2.56 -> e4m3 2.5 (grid 0.25 on
+#   [2, 4)), 0.3 -> 9.6 -> 10 (grid 1 on [8, 16)).  Dequantised: 14, 0.078125, 0.3125.
+# x, block 1: x128 = 0.875 is the maximum, s = 0.875 / 448 = 2^-9 (exact):
+#   0.0107 -> 5.4784 -> 5.5 (grid 0.5 on [4, 8)) -> 0.0107421875;
+#   0.00035 -> 0.1792 -> 0.171875 (grid 2^-6 on [1/8, 1/4)) -> 11 / 32768.
+#   With one scale per row (2^-5) instead, 0.00035 -> 0.0112, subnormal (grid 2^-9):
+#   -> 6 * 2^-9 -> 12 / 32768: a per-row scale changes the result.
+# Gate rows read x0 with weight 4: a = 56 and silu(56) = 56 in float64
+#   (56 / (1 + e^-56), e^-56 ~ 5e-25 is below half an ulp).
+# Up rows: b0 = xq1 = 0.078125, b1 = xq2 = 0.3125, b2 = 0.0301 * xq0 = 0.4214,
+#   b128 = 2^16 * xq130 = 22, b129 = 2^10 * xq129 = 11.
+# h = 56 b: 4.375, 17.5, 23.5984 (float64), 1232, 616; in bf16 (7 stored bits)
+#   23.5984 -> 23.625 (grid 0.125 on [16, 32)); the others are exact.
+# h, block 0: s = 23.625 / 448 = 27 / 512 (exact); quotients 4.375 * 512/27 = 82.96 -> 80
+#   (grid 8 on [64, 128)), 17.5 * 512/27 = 331.85 -> 320 (grid 32 on [256, 512)), 448.
+#   Dequantised: 80 * 27/512 = 4.21875, 320 * 27/512 = 16.875, 23.625.
+# h, block 1: s = 1232 / 448 = 2.75, quotients 448 and 616 / 2.75 = 224 (exact).
+# W_down copies h columns 0, 1, 2, 128, 129 to outputs 0..4 and sends
+#   h0 + 2 h128 to output 5 (a sum over both K blocks of GEMM2).
+_HAND_Y = [4.21875, 16.875, 23.625, 1232.0, 616.0, 4.21875 + 2 * 1232.0]
+# power-of-two scales (the smallest 2^k with amax <= 448 * 2^k): x keeps 2^-5 and 2^-9
+# (its maxima are 448 times a power of two), so xq is unchanged; h block 0: 23.625 <=
+# 448 * 2^-4, s = 1/16: 4.375 -> 70 -> 72 (grid 8) -> 4.5; 17.5 -> 280 -> 288 (grid
+# 32) -> 18; 23.625 -> 378 -> 384 -> 24.  h block 1: 1232 <= 448 * 4, s = 4: 1232 ->
+# 308 -> 320 -> 1280; 616 -> 154 -> 160 (grid 16 on [128, 256)) -> 640.
+_HAND_Y_POW2 = [4.5, 18.0, 24.0, 1280.0, 640.0, 4.5 + 2 * 1280.0]
+
+
+def _hand_expert():
+    x = np.zeros((1, 256), np.float32)
+    x[0, [0, 1, 2, 128, 129, 130]] = [14.0, 0.08, 0.3, 0.875, 0.0107, 0.00035]
+    wg = np.zeros((256, 256))
+    wu = np.zeros((256, 256))
+    wd = np.zeros((256, 256))
+    wg[[0, 1, 2, 128, 129], 0] = 4.0
+    wu[0, 1] = 1.0
+    wu[1, 2] = 1.0
+    wu[2, 0] = 0.0301
+    wu[128, 130] = 2.0 ** 16
+    wu[129, 129] = 2.0 ** 10
+    for c, i in enumerate([0, 1, 2, 128, 129]):
+        wd[c, i] = 1.0
+    wd[5, 0] = 1.0
+    wd[5, 128] = 2.0
+    return x, wg, wu, wd
+
+
+def _quant_per_row(v):
+    """A planted mistake: one scale per row instead of one per 1x128 tile."""
+    v = np.asarray(v, np.float32)
+    s = (np.abs(v).max(1, keepdims=True) / np.float32(448)).astype(np.float32)
+    return oracle.e4m3_table()[oracle.e4m3_encode_rne((v / s).astype(np.float32))] * s.astype(np.float64)
+
+
+def _variant(x, wg, wu, wd, quant_x=True, quant_h=True, bf16_h=True, pow2=False, row_x=False,
+             row_h=False, swap=False):
+    """The FP8-emulating expert with one step switched (a planted mistake each)."""
+    quant = oracle.quantize_1x128_pow2 if pow2 else oracle.quantize_1x128
+    tile = lambda v: oracle.dequantize_1x128(*quant(v))
+    xq = (_quant_per_row(x) if row_x else tile(x)) if quant_x else np.asarray(x, np.float64)
+    a, b = xq @ wg.T, xq @ wu.T
+    h = oracle.silu(b) * a if swap else oracle.silu(a) * b
+    hb = torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).float().numpy() if bf16_h \
+        else h.astype(np.float32)
+    hq = (_quant_per_row(hb) if row_h else tile(hb)) if quant_h else h
+    return hq @ wd.T
+
+
+def test_fp8_emulated_hand_case():
+    x, wg, wu, wd = _hand_expert()
+    y = oracle.expert_ffn_fp8_emulated(x, wg, wu, wd)
+    assert y[0, :6].tolist() == _HAND_Y and np.all(y[0, 6:] == 0)
+    # the unswitched variant is the same computation
+    assert np.array_equal(_variant(x, wg, wu, wd), y)
+    # each planted mistake moves at least one hand-derived output
+    for mistake in (dict(quant_h=False), dict(quant_x=False), dict(bf16_h=False), dict(pow2=True),
+                    dict(row_x=True), dict(row_h=True), dict(swap=True)):
+        got = _variant(x, wg, wu, wd, **mistake)[0, :6]
+        assert np.abs(got - np.array(_HAND_Y)).max() > 1e-3, mistake
+
+
+def test_fp8_pow2_emulated_hand_case():
+    x, wg, wu, wd = _hand_expert()
+    y = oracle.expert_ffn_fp8_pow2_emulated(x, wg, wu, wd)
+    assert y[0, :6].tolist() == _HAND_Y_POW2 and np.all(y[0, 6:] == 0)
+    assert np.array_equal(_variant(x, wg, wu, wd, pow2=True), y)
+    for mistake in (dict(quant_h=False), dict(quant_x=False), dict(pow2=False),
+                    dict(swap=True)):
+        got = _variant(x, wg, wu, wd, **{"pow2": True, **mistake})[0, :6]
+        assert np.abs(got - np.array(_HAND_Y_POW2)).max() > 1e-3, mistake
