@@ -103,7 +103,13 @@ def route(x, w_router, bias, num_groups: int, top_groups: int, group_topn: int,
     stable sorts of the negated keys, so equal keys keep the lower index first.
     All tokens are processed at once; rows are independent.
     """
-    z, s = affinities(x, w_router)
+    return select(affinities(x, w_router)[1], bias, num_groups, top_groups, group_topn, top_k)
+
+
+def select(s: np.ndarray, bias, num_groups: int, top_groups: int, group_topn: int,
+           top_k: int) -> RouteResult:
+    """The selection steps of ``route`` on given float64 affinities s [T, E] (so that
+    several biases can be tried on one batch without recomputing the logits)."""
     T, E = s.shape
     G, M, K = num_groups, top_groups, top_k
     n = E // G
@@ -214,3 +220,47 @@ def bias_update(load, bias, gamma: float, num_tokens: int, top_k: int) -> np.nda
         elif load[e] * E < total:
             b[e] = np.float32(b[e] + g)
     return b
+
+
+def valid_selections(sb_t: np.ndarray, num_groups: int, top_groups: int, group_topn: int,
+                     top_k: int, tol: float = NEAR_TIE) -> set:
+    """Every expert set one token may legitimately select when gaps below ``tol`` are
+    treated as ties ([R] 2.3-2.4 with the near-tie reading): a K-set X is valid iff
+    some set S of M groups has
+      min_{g in S} score_g >= max_{g not in S} score_g - tol   (S is a top-M group set)
+      X within the experts of S, and
+      min_{e in X} sb_e >= max_{e in S, not in X} sb_e - tol    (X is a top-K of S),
+    score_g being the sum of the group_topn largest float64 sb of group g.
+    sb_t [E] float64 biased affinities of the token.  Returns a set of frozensets.
+
+    Within a top-M (top-K) set every member must be at least the (M+1)-th (K+1)-th
+    value minus tol, and everything above the M-th (K-th) value plus tol is forced
+    in, so only the values within tol of the boundary are enumerated."""
+    import itertools
+    sb_t = np.asarray(sb_t, np.float64)
+    E = sb_t.shape[0]
+    G, M, K = num_groups, top_groups, top_k
+    n = E // G
+    score = (-np.sort(-sb_t.reshape(G, n), axis=1))[:, :group_topn].sum(1)
+
+    def top_sets(vals, keys, k):
+        """All k-subsets of keys whose values form a top-k within tol."""
+        order = sorted(keys, key=lambda i: -vals[i])
+        if k >= len(order):
+            return [frozenset(order)]
+        vk = vals[order[k - 1]]
+        forced = [i for i in order if vals[i] > vk + tol]
+        window = [i for i in order if vk - tol <= vals[i] <= vk + tol]
+        out = []
+        for extra in itertools.combinations(window, k - len(forced)):
+            xs = frozenset(forced) | frozenset(extra)
+            rest = [vals[i] for i in keys if i not in xs]
+            if not rest or min(vals[i] for i in xs) >= max(rest) - tol:
+                out.append(xs)
+        return out
+
+    result = set()
+    for gs in top_sets(score, list(range(G)), M):
+        cand = [e for g in sorted(gs) for e in range(g * n, (g + 1) * n)]
+        result.update(top_sets(sb_t, cand, K))
+    return result

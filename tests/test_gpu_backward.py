@@ -263,3 +263,53 @@ def test_router_backward(name, over):
     e_dw = np.abs(dw.cpu().double().numpy() - want_dw).max() / np.abs(want_dw).max()
     log(f"  dx rel err {e_dx:.2e}, dW_r rel err {e_dw:.2e}")
     assert e_dx <= 5e-5 and e_dw <= 5e-5
+
+
+@pytest.mark.slow
+def test_expert_backward_weights_prefill_rows():
+    """Weight gradients at the prefill shape (T = 8192: the shared expert over 8192 rows,
+    routed experts over about 256), in the launch the bench times, on 64 sampled
+    intermediate channels i of the shared expert, the three busiest routed experts and
+    the least busy one: rows i of dW_gate and dW_up, column i of dW_down.  The oracle
+    runs each expert restricted to those channels (the SwiGLU is elementwise in i and
+    dh_i needs only column i of W_down, so the restriction is the same computation)."""
+    from gpu_harness import config_of, expert_getter, inputs_on_gpu, oracle_route
+    cfg = workloads.get("prefill_bf16")
+    log("expert backward weights at prefill rows (T=8192)")
+    d = inputs_on_gpu(cfg)
+    r = oracle_route(cfg, d)
+    T, K, Ns, E, H, I = cfg.T, cfg.K, cfg.Ns, cfg.E, cfg.hidden, cfg.inter
+    load, off, row_token, pair_row = oracle.permute(r.idx, E)
+    dy_rows = workloads.make_dense((cfg.rows, H), "bf16", seed=11, name="dy_rows")
+    c = config_of(cfg)
+    ws = torch.empty(moe.moe_backward_workspace_bytes(c), dtype=torch.uint8, device="cuda")
+    i32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).cuda()
+    weights = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
+    G = E + Ns
+    dwg = torch.empty((G, I, H), device="cuda")
+    dwu = torch.empty((G, I, H), device="cuda")
+    dwd = torch.empty((G, H, I), device="cuda")
+    moe.moe_expert_backward(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
+                            dy_rows.cuda(), None, dwg, dwu, dwd, ws)
+    torch.cuda.synchronize()
+    chan = np.sort(workloads.sample_rows(I, 64, seed=12).numpy())
+    order = np.argsort(-load, kind="stable")
+    check = [E] + [int(e) for e in order[:3]] + [int(order[-1])]
+    log(f"  experts {check} with rows {[T] + [int(load[e]) for e in check[1:]]}")
+    expert_of_row = np.concatenate([np.repeat(np.arange(E), np.diff(off)),
+                                    np.repeat(np.arange(E, G), T)])
+    full = expert_getter(cfg, d)
+    get = lambda e: (lambda g, u, w: (g[chan], u[chan], w[:, chan]))(*full(e))
+    worst = 0.0
+    for e in check:
+        want = oracle.expert_weight_backward(d["x"], row_token, T, K, dy_rows, get,
+                                             expert_of_row, [e])[e]
+        got = (dwg[e][chan], dwu[e][chan], dwd[e][:, chan])
+        for gm, ref in zip(got, want):
+            gm = gm.cpu().double().numpy()
+            if np.abs(ref).max() == 0.0:               # an expert without rows
+                assert np.all(gm == 0.0)
+                continue
+            worst = max(worst, np.abs(gm - ref).max() / np.abs(ref).max())
+    log(f"  worst rel err {worst:.2e}")
+    assert worst <= 2e-2

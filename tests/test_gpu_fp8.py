@@ -13,44 +13,48 @@ import torch
 import oracle
 import sparse_moe_layer_affinity_amd as moe
 import workloads
-from gpu_harness import (TOL, compare_routing, config_of, expert_getter, inputs_on_gpu,
+from gpu_harness import (TOL, check_layer_stages, config_of, expert_getter, inputs_on_gpu,
                          layer_forward, log, oracle_route, rel_err, weights_of, workspace)
 
 pytestmark = pytest.mark.gpu
 
 SMALL = dict(hidden=256, inter=256, E=16, K=4, G=4, M=2, topn=2)
-# Against the fp32 oracle the FP8 method itself (exact quantisation, float64 sums)
-# is off by ~4.4e-2 in the global norm at >= 64 rows and up to the per-row figure
-# (~6e-2, more for a single row) when only a few rows are compared; the 6e-2 bar
-# applies from 64 rows, 0.1 below.  Against the FP8-emulating oracle the remaining
+# Against the fp32 oracle the FP8 method itself (the oracle's exact emulation of the
+# quantisation, float64 sums) is off by 4.1e-2 .. 5.6e-2 on these shapes (global norm;
+# most of it from quantising x).  Against the FP8-emulating oracle the remaining
 # difference is the few e4m3 codes of h that flip because the kernel's h carries
-# fp32-accumulation rounding before its bf16 rounding: one code step is 1/16 of
-# the value, a handful per row out of `inter` terms gives a few 1e-3 (measured
+# fp32-accumulation rounding before its bf16 rounding: one code step is 1/16 of the
+# value, a handful per row out of `inter` terms gives a few 1e-3 (measured
 # 3e-3..9e-3 on MI355X); bound 2e-2.
 EMU_TOL = 2e-2
+# the kernel's own share beyond the method's error when judged against the fp32 oracle
+KERNEL_SHARE = 1e-2
 
 
-def fp32_tol(n_rows):
-    return TOL["e4m3"] if n_rows >= 64 else 0.1
+def fp32_bound(method_err):
+    """The workload's 6e-2 bar wherever the FP8 method itself leaves the kernel its
+    1e-2 share (method error <= 5e-2); where the method alone takes more, the bar is
+    the method's error plus that share (logged by the callers)."""
+    return max(TOL["e4m3"], method_err + KERNEL_SHARE)
 
 
 def _check(cfg, d, out, rows=None):
     r = oracle_route(cfg, d)
-    ties = compare_routing(r, out["idx"], out["gate"], where=cfg.name)
-    same = np.all(out["idx"].cpu().numpy() == r.idx, axis=1)
+    idx_ref, gate_ref, _, flipped = check_layer_stages(cfg, r, out, where=cfg.name)
     rows = np.arange(cfg.T) if rows is None else np.asarray(rows)
-    rows = rows[same[rows]]
     get = expert_getter(cfg, d)
     got = out["y"].float().cpu().numpy()[rows]
-    ref = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows)
+    ref = oracle.layer_output(d["x"], idx_ref, gate_ref, get, cfg.E, cfg.Ns, rows=rows)
     err = rel_err(got, ref)
     emu_ffn = (oracle.expert_ffn_fp8_pow2_emulated if cfg.w == "e4m3_pow2"
                else oracle.expert_ffn_fp8_emulated)
-    emu = oracle.layer_output(d["x"], r.idx, r.gate, get, cfg.E, cfg.Ns, rows=rows, ffn=emu_ffn)
+    emu = oracle.layer_output(d["x"], idx_ref, gate_ref, get, cfg.E, cfg.Ns, rows=rows, ffn=emu_ffn)
     err_emu = rel_err(got, emu)
-    log(f"  {cfg.name} ({cfg.w}): rows {len(rows)}, near-ties {ties}, rel err vs fp32 {err:.3e}, "
-        f"vs fp8-emulating {err_emu:.3e}")
-    assert err <= fp32_tol(len(rows)), err
+    method = rel_err(emu, ref)
+    log(f"  {cfg.name} ({cfg.w}): rows {len(rows)}, near-ties {int(r.near_tie.sum())}, flipped "
+        f"{flipped}, rel err vs fp32 {err:.3e} (the FP8 method itself {method:.3e}, bar "
+        f"{fp32_bound(method):.3e}), vs fp8-emulating {err_emu:.3e}")
+    assert err <= fp32_bound(method), err
     assert err_emu <= EMU_TOL, err_emu
 
 

@@ -97,12 +97,12 @@ def test_row_block_edges_fp8(dims, w):
     errs_emu = _per_expert_errors(cfg, off, got, emu)
     log("  vs fp32: " + ", ".join(f"{k}:{v:.1e}" for k, v in errs.items()))
     log("  vs fp8-emulating: " + ", ".join(f"{k}:{v:.1e}" for k, v in errs_emu.items()))
-    # the workload's 6e-2 bound (from 64 rows, 0.1 below, as the layer tests) holds for
-    # the FP8 method itself once both GEMMs sum at least 256 products per output; with
-    # 128 the quantisation errors average less (measured up to 6.1e-2), and only the
-    # emulating oracle's bound applies
-    if min(hidden, inter) >= 256:
-        for k, v in errs.items():
-            n = cfg.T if k == "shared" else LOADS[k]
-            assert v <= (TOL["e4m3"] if n >= 64 else 0.1), (k, v)
+    # against the fp32 oracle: the workload's 6e-2 bar for every expert whose FP8
+    # method error (the emulating oracle against the fp32 one) leaves the kernel a 1e-2
+    # share, else the method's own error plus that share (few rows and short K sums
+    # average the quantisation errors less)
+    method = _per_expert_errors(cfg, off, emu, ref32)
+    log("  the FP8 method itself: " + ", ".join(f"{k}:{v:.1e}" for k, v in method.items()))
+    for k, v in errs.items():
+        assert v <= max(TOL["e4m3"], method[k] + 1e-2), (k, v, method[k])
     assert max(errs_emu.values()) <= _emu_tol(inter), errs_emu

@@ -175,3 +175,49 @@ def test_near_tie_flag_on_planted_gap():
     r = oracle.route(x, w, b, 1, 1, 1, 2)
     assert r.idx[0].tolist() == [0, 2]
     assert r.near_tie_expert[0]
+
+
+def _valid_brute(sb_row, G, M, topn, K, tol=1e-6):
+    """Every K-set that is a top-K (within tol) of some top-M group set (within tol), by
+    enumerating all group subsets and all expert subsets."""
+    E = sb_row.shape[0]
+    n = E // G
+    gscore = [sum(sorted(sb_row[j * n:(j + 1) * n], reverse=True)[:topn]) for j in range(G)]
+    out = set()
+    for S in itertools.combinations(range(G), M):
+        rest_g = [gscore[j] for j in range(G) if j not in S]
+        if rest_g and min(gscore[j] for j in S) < max(rest_g) - tol:
+            continue
+        cand = [e for j in S for e in range(j * n, (j + 1) * n)]
+        for X in itertools.combinations(cand, K):
+            rest = [sb_row[e] for e in cand if e not in X]
+            if not rest or min(sb_row[e] for e in X) >= max(rest) - tol:
+                out.add(frozenset(X))
+    return out
+
+
+@pytest.mark.parametrize("E,G,M,topn,K", [(16, 4, 2, 2, 4), (12, 3, 2, 2, 3), (8, 4, 4, 1, 3),
+                                          (8, 1, 1, 1, 2), (16, 8, 3, 2, 5)])
+def test_valid_selections_brute_force(E, G, M, topn, K):
+    """Affinities on a coarse grid (steps of 4e-7 around three levels) so that many
+    tokens have several valid selections; the enumeration equals brute force, always
+    holds the canonical selection, and is that selection alone without near-ties."""
+    rng = np.random.default_rng(E * 100 + K)
+    multi = 0
+    for t in range(60):
+        sb = 0.5 + 0.1 * rng.integers(0, 3, E) + 4e-7 * rng.integers(0, 4, E)
+        want = _valid_brute(sb, G, M, topn, K)
+        got = oracle.valid_selections(sb, G, M, topn, K)
+        assert got == want, t
+        r = oracle.select(sb[None, :] - 0.0, np.zeros(E, np.float32), G, M, topn, K)
+        assert frozenset(r.idx[0].tolist()) in got
+        if not r.near_tie[0]:
+            assert got == {frozenset(r.idx[0].tolist())}
+        multi += len(got) > 1
+    assert multi >= 5
+    # a planted flip: two experts 5e-7 apart straddle the K-th place
+    sb = np.linspace(0.9, 0.1, E)
+    sb[K] = sb[K - 1] - 5e-7
+    got = oracle.valid_selections(sb, 1, 1, 1, K)
+    top = list(range(K))
+    assert got == {frozenset(top), frozenset(top[:-1] + [K])}
