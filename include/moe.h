@@ -25,14 +25,16 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *    call only enqueues work on `stream`; none synchronises, allocates device
  *    memory, or keeps a pointer after it returns.  Scratch memory comes from the
- *    caller's workspace `ws` of `ws_bytes` bytes (see moe_workspace_bytes).
+ *    caller's workspace `ws` of `ws_bytes` bytes (see moe_workspace_bytes), except
+ *    for moe_layer_forward_noalloc (a library-held array, see there).
  *  - The caller owns every buffer.  Outputs are fully overwritten.
  *  - Arguments are validated on the host before anything is launched; on any
  *    error nothing is enqueued.  Return codes only (no global error state);
  *    moe_status_string() names a code.  MOE_ERR_HIP reports a failed launch;
  *    faults inside kernels surface at the caller's next synchronisation.
  *  - Calls are thread-safe (the only global state is a per-device cache of the
- *    CU count, stored atomically).  Results are deterministic: no floating-point
+ *    CU count and of the no-alloc array's address, stored atomically, and that
+ *    array itself).  Results are deterministic: no floating-point
  *    atomics; the router's split-K partials are summed in a fixed order.
  *  - Row-major layouts throughout.  Experts are stacked routed-first: experts
  *    0..E-1 are routed, E..E+Ns-1 are the shared experts.
@@ -307,6 +309,24 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                              const void* residual, void* y, int32_t* topk_idx,
                              float* topk_gate, int32_t* expert_load,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels, with the workspace taken from a 64 MiB array that the library holds on
+ * each device it runs on, from its load until the process ends.  Accepts exactly the
+ * configurations with moe_workspace_bytes(cfg) <= 64 MiB (at hidden 7168, inter
+ * 2048, E 256, K 8, one shared expert: up to 365 tokens in BF16, 316 with E4M3
+ * weights) and returns MOE_ERR_UNSUPPORTED for larger ones, before anything is
+ * enqueued.  Allocates nothing: no hipMalloc, hipFree or allocating library call;
+ * the first call on a device looks the array's address up (hipGetSymbolAddress) and
+ * caches it.  Every call on a device shares that device's array (its contents on
+ * entry are irrelevant: nothing in it needs clearing), so calls that overlap on one
+ * device -- concurrent streams or threads -- race and must be serialised by the
+ * caller.  Arguments and outputs as for moe_layer_forward. */
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                                     const float* bias, const moe_expert_weights* weights,
+                                     const void* residual, void* y, int32_t* topk_idx,
+                                     float* topk_gate, int32_t* expert_load, void* stream);
 
 /* Static string naming a status code ("unknown status" for other values). */
 const char* moe_status_string(moe_status status);

@@ -55,6 +55,8 @@ _SIGS = {
     "moe_bias_update": (ctypes.c_int, [_CFG, _P, ctypes.c_float, _P, _P]),
     "moe_layer_forward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.POINTER(MoeExpertWeights), _P,
                                          _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.POINTER(MoeExpertWeights),
+                                                 _P, _P, _P, _P, _P, _P]),
     "moe_router_scores": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_balance_loss": (ctypes.c_int, [_CFG, _P, _P, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
                                         _P, _P, ctypes.c_size_t, _P]),
@@ -195,6 +197,16 @@ def moe_layer_forward(cfg, x, w_router, bias, weights: dict, residual, y, topk_i
         ctypes.byref(w), _dev(residual, "residual", True), _dev(y, "y"),
         _dev(topk_idx, "topk_idx"), _dev(topk_gate, "topk_gate"),
         _dev(expert_load, "expert_load"), _dev(ws, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward_noalloc(cfg, x, w_router, bias, weights: dict, residual, y, topk_idx,
+                              topk_gate, expert_load, stream=None):
+    w = _weights(weights)
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        ctypes.byref(cfg), _dev(x, "x"), _dev(w_router, "w_router"), _dev(bias, "bias"),
+        ctypes.byref(w), _dev(residual, "residual", True), _dev(y, "y"),
+        _dev(topk_idx, "topk_idx"), _dev(topk_gate, "topk_gate"),
+        _dev(expert_load, "expert_load"), _stream(stream)))
 
 
 def moe_router_scores(cfg, x, w_router, scores, ws, ws_bytes=None, stream=None):

@@ -2,6 +2,8 @@
 // launch sequences.  Every check runs before anything is enqueued.
 #include <math.h>
 
+#include <atomic>
+
 #include "kernels.h"
 
 namespace moe {
@@ -130,6 +132,25 @@ static moe_status from_hip(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
   return MOE_ERR_HIP;
+}
+
+// Workspace of moe_layer_forward_noalloc: one array per device, resident from the
+// library's load until the process ends, shared by every such call on that device.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+// Device address of this device's `scratch`, looked up once per device (with that
+// device current) and cached; the array's name in host code is only a stand-in for
+// the symbol.  nullptr if the lookup fails.
+static void* noalloc_scratch() {
+  static std::atomic<void*> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+  cached[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 #define MOE_TRY(expr)                      \
@@ -322,14 +343,21 @@ moe_status moe_bias_update(const moe_config* cfg, const int32_t* expert_load, fl
                                      static_cast<hipStream_t>(stream)));
 }
 
+static moe_status check_layer_args(const moe_config* cfg, const void* x, const void* w_router,
+                                   const float* bias, const moe_expert_weights* weights,
+                                   const void* y, const int32_t* topk_idx,
+                                   const float* topk_gate, const int32_t* expert_load) {
+  MOE_TRY(validate(cfg));
+  if (!x || !w_router || !bias || !y || !topk_idx || !topk_gate || !expert_load)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return check_weights(*cfg, weights);
+}
+
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                              const float* bias, const moe_expert_weights* weights,
                              const void* residual, void* y, int32_t* topk_idx, float* topk_gate,
                              int32_t* expert_load, void* ws, size_t ws_bytes, void* stream) {
-  MOE_TRY(validate(cfg));
-  if (!x || !w_router || !bias || !y || !topk_idx || !topk_gate || !expert_load)
-    return MOE_ERR_INVALID_ARGUMENT;
-  MOE_TRY(check_weights(*cfg, weights));
+  MOE_TRY(check_layer_args(cfg, x, w_router, bias, weights, y, topk_idx, topk_gate, expert_load));
   MOE_TRY(check_ws(*cfg, ws, ws_bytes));
   const Workspace w = workspace_layout(*cfg, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -339,6 +367,18 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                                   w.pair_row, w, s)));
   MOE_TRY(from_hip(launch_grouped_ffn(*cfg, x, w.offsets, w.row_token, *weights, w.y_rows, w, s)));
   return from_hip(launch_combine(*cfg, w.y_rows, w.pair_row, topk_gate, residual, y, s));
+}
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                                     const float* bias, const moe_expert_weights* weights,
+                                     const void* residual, void* y, int32_t* topk_idx,
+                                     float* topk_gate, int32_t* expert_load, void* stream) {
+  MOE_TRY(check_layer_args(cfg, x, w_router, bias, weights, y, topk_idx, topk_gate, expert_load));
+  if (workspace_layout(*cfg, nullptr).bytes > kNoallocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  void* ws = noalloc_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_layer_forward(cfg, x, w_router, bias, weights, residual, y, topk_idx, topk_gate,
+                           expert_load, ws, kNoallocScratchBytes, stream);
 }
 
 const char* moe_status_string(moe_status status) {

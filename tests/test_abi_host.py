@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
                           "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
                           "moe_gate_backward", "moe_swiglu_backward", "moe_backward_workspace_bytes",
                           "moe_expert_backward_input", "moe_expert_backward", "moe_router_backward",
-                          "moe_status_string"}
+                          "moe_layer_forward_noalloc", "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -248,6 +248,26 @@ def test_weight_scale_pointer_rules():
                    stream=0) == B.MOE_ERR_INVALID_ARGUMENT
     assert code_of(B.moe_layer_forward, cfg(), A, A, A, dense, None, A, A, A, 0, A, need8,
                    stream=0) == B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_argument_checks():
+    """moe_layer_forward_noalloc rejects null pointers and batches whose workspace is
+    beyond its 64 MiB array on the host, before it touches a device."""
+    A = ALIGNED
+    dense = dict(w_gate=A, w_up=A, w_down=A)
+    fn = B.moe_layer_forward_noalloc
+    assert moe.moe_workspace_bytes(cfg(T=365)) <= 64 << 20 < moe.moe_workspace_bytes(cfg(T=366))
+    assert code_of(fn, cfg(T=366), A, A, A, dense, None, A, A, A, A, stream=0) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert code_of(fn, cfg(), A, A, A, dense, None, A, A, A, A, stream=0) == B.MOE_ERR_UNSUPPORTED
+    assert code_of(fn, cfg(T=128), 0, A, A, dense, None, A, A, A, A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(fn, cfg(T=128), A, A, A, dense, None, A, A, A, 0, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert code_of(fn, cfg(T=128, w="e4m3"), A, A, A, dense, None, A, A, A, A, stream=0) == \
+        B.MOE_ERR_INVALID_ARGUMENT                             # scales missing
+    assert code_of(fn, cfg(T=128, K=9), A, A, A, dense, None, A, A, A, A, stream=0) == \
+        B.MOE_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_host_tensors():
