@@ -69,6 +69,12 @@ BackwardWorkspace backward_workspace_layout(const moe_config& c, void* base) {
   w.dh = static_cast<uint16_t*>(take(rows * I * 2));
   w.dab = static_cast<uint16_t*>(take(rows * 2 * I * 2));
   w.dx_rows = static_cast<uint16_t*>(take(rows * H * 2));
+  const size_t packed = size_t(wgrad_packed_rows(c));
+  w.pack.poff = static_cast<int32_t*>(take((G + 1) * 4));
+  w.pack.xt = static_cast<uint16_t*>(take(H * packed * 2));
+  w.pack.dyt = static_cast<uint16_t*>(take(H * packed * 2));
+  w.pack.dabt = static_cast<uint16_t*>(take(2 * I * packed * 2));
+  w.pack.ht = static_cast<uint16_t*>(take(I * packed * 2));
   w.bytes = off;
   return w;
 }

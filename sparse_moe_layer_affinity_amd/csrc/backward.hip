@@ -17,8 +17,9 @@
 // deterministic).  gate_backward: one wave per token.  swiglu_backward: elementwise
 // over the [rows, inter] pre-activations of the SwiGLU experts.  The experts' input
 // gradient reuses the forward's expert GEMM (plain mode) on per-expert transposed
-// weight copies (transpose_experts); their weight gradients and the router logits'
-// backward run in expert_wgrad, which reads each expert's row range on the device.
+// weight copies (transpose_experts); their weight gradients run on the matrix cores
+// (wgrad.hip, each expert's row range read on the device); the router logits' backward
+// runs in router_wgrad (fp32 logit gradient, VALU).
 #include "gemm_common.h"
 
 namespace moe {
@@ -271,29 +272,19 @@ static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, in
   return hipGetLastError();
 }
 
-// Weight gradients of the grouped SwiGLU experts, one fp32 output tile (128 x 128, 8 x 8
-// per thread; 64 x 64 for small outputs) of one expert per workgroup, summed over that
-// expert's rows in row order (fp32 FMAs):
-//   C[g][m][n] = sum_r A[r][m] * Bv(r, n)
-// A rows at A + r * lda; Bv(r, n) = B[r][n] (plain), x[token of r][n] (gather), or
-// silu(a) * b with a = B[r][n] and b = B[r][boff + n] (the forward's h, from the
-// pre-activations).  Each expert's row range comes from the device offsets, so the
-// host needs no row counts; experts without rows get zeros.  The shared experts'
-// tiles (T rows each) are dispatched first.
-enum { kWgPlainB = 0, kWgGatherB = 1, kWgSwigluB = 2 };
-// A operand: bf16 rows [r][m], fp32 rows [r][m], or fp32 stored [m][r]
-enum { kWgAbf16 = 0, kWgAf32 = 1, kWgAf32T = 2 };
+// The router logits' backward on the VALU: one fp32 output tile (128 x 128, 8 x 8 per
+// thread; 64 x 64 for small outputs) per workgroup, summed over the rows r of one row
+// group in row order (fp32 FMAs):
+//   C[m][n] = sum_r A(r, m) * B[r][n]
+// A(r, m) = Af[r][m] (row-major fp32) or Af[m][r] (stored transposed); B bf16 rows.
+enum { kWgAf32 = 1, kWgAf32T = 2 };
 struct WgradArgs {
-  const uint16_t* A;
   const float* Af;
   long long lda;
   const uint16_t* B;
   long long ldb;
-  int boff;
-  const int32_t* offsets;
-  const int32_t* row_token;
-  int T, TK, E, Ns, M, N;
-  float* C;                                 // [E+Ns][M][N]
+  int rows, M, N;
+  float* C;                                 // [M][N]
 };
 
 __device__ __forceinline__ void bf16x4_to_f32(uint2 raw, float f[4]) {
@@ -303,22 +294,12 @@ __device__ __forceinline__ void bf16x4_to_f32(uint2 raw, float f[4]) {
   f[3] = bf16_bits_to_f32(raw.y >> 16);
 }
 
-template <int BMODE, int AMODE, int kT>
-__global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
+template <int AMODE, int kT>
+__global__ __launch_bounds__(256) void router_wgrad(WgradArgs p) {
   constexpr int kU = kT / 16, kPitch = kT + 4;        // kU x kU outputs per thread
   __shared__ __attribute__((aligned(16))) float As[16][kPitch];
   __shared__ __attribute__((aligned(16))) float Bs[16][kPitch];
-  const int G = p.E + p.Ns;
-  const int g = (int(blockIdx.z) + p.E) % G;          // shared experts first
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
-  int r0, r1;
-  if (g < p.E) {
-    r0 = p.offsets[g];
-    r1 = p.offsets[g + 1];
-  } else {
-    r0 = p.TK + (g - p.E) * p.T;
-    r1 = r0 + p.T;
-  }
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const int lr = tid / 16, lc = (tid % 16) * kU;     // loader: row lr, kU columns from lc
   float acc[kU][kU];
@@ -326,20 +307,15 @@ __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
   for (int i = 0; i < kU; ++i)
 #pragma unroll
     for (int j = 0; j < kU; ++j) acc[i][j] = 0.0f;
-  for (int rb = r0; rb < r1; rb += 16) {
+  for (int rb = 0; rb < p.rows; rb += 16) {
     const int r = rb + lr;
     float av[kU], bv[kU];
 #pragma unroll
     for (int i = 0; i < kU; ++i) av[i] = bv[i] = 0.0f;
-    // N, and M for the row-major A forms, are multiples of 8: a group of kU elements is
-    // wholly inside or outside; the transposed fp32 A (M = tokens) is guarded per row
-    if (r < r1 && m0 + lc < p.M) {
-      if (AMODE == kWgAbf16) {
-#pragma unroll
-        for (int q = 0; q < kU / 4; ++q)
-          bf16x4_to_f32(*reinterpret_cast<const uint2*>(p.A + size_t(r) * p.lda + m0 + lc + 4 * q),
-                        av + 4 * q);
-      } else if (AMODE == kWgAf32) {
+    // N, and M for the row-major A, are multiples of 8: a group of kU elements is wholly
+    // inside or outside; the transposed A (M = tokens) is guarded per row
+    if (r < p.rows && m0 + lc < p.M) {
+      if (AMODE == kWgAf32) {
 #pragma unroll
         for (int q = 0; q < kU / 4; ++q) {
           const float4 f =
@@ -352,25 +328,11 @@ __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
           av[i] = m0 + lc + i < p.M ? p.Af[size_t(m0 + lc + i) * p.lda + r] : 0.0f;
       }
     }
-    if (r < r1 && n0 + lc < p.N) {
-      const uint16_t* pb;
-      if (BMODE == kWgGatherB) {
-        const int t = r < p.TK ? p.row_token[r] : (r - p.TK) % p.T;
-        pb = p.B + size_t(t) * p.ldb + n0 + lc;
-      } else {
-        pb = p.B + size_t(r) * p.ldb + n0 + lc;
-      }
+    if (r < p.rows && n0 + lc < p.N) {
+      const uint16_t* pb = p.B + size_t(r) * p.ldb + n0 + lc;
 #pragma unroll
       for (int q = 0; q < kU / 4; ++q)
         bf16x4_to_f32(*reinterpret_cast<const uint2*>(pb + 4 * q), bv + 4 * q);
-      if (BMODE == kWgSwigluB) {
-        float bu[kU];
-#pragma unroll
-        for (int q = 0; q < kU / 4; ++q)
-          bf16x4_to_f32(*reinterpret_cast<const uint2*>(pb + p.boff + 4 * q), bu + 4 * q);
-#pragma unroll
-        for (int i = 0; i < kU; ++i) bv[i] = bv[i] * (1.0f / (1.0f + expf(-bv[i]))) * bu[i];
-      }
     }
     __syncthreads();                        // the previous chunk's reads are done
 #pragma unroll
@@ -397,23 +359,21 @@ __global__ __launch_bounds__(256) void expert_wgrad(WgradArgs p) {
         for (int j = 0; j < kU; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
   }
-  float* c = p.C + size_t(g) * p.M * p.N;
   if (n0 + tx * kU >= p.N) return;
 #pragma unroll
   for (int i = 0; i < kU; ++i)
     if (m0 + ty * kU + i < p.M) {
-      float4* q = reinterpret_cast<float4*>(c + size_t(m0 + ty * kU + i) * p.N + n0 + tx * kU);
+      float4* q = reinterpret_cast<float4*>(p.C + size_t(m0 + ty * kU + i) * p.N + n0 + tx * kU);
 #pragma unroll
       for (int u = 0; u < kU / 4; ++u)
         q[u] = make_float4(acc[i][4 * u], acc[i][4 * u + 1], acc[i][4 * u + 2], acc[i][4 * u + 3]);
     }
 }
 
-template <int BMODE, int AMODE = kWgAbf16, int TILE = 128>
-static hipError_t launch_wgrad(const WgradArgs& p, hipStream_t st) {
-  hipLaunchKernelGGL((expert_wgrad<BMODE, AMODE, TILE>),
-                     dim3(ceil_div(p.N, TILE), ceil_div(p.M, TILE), p.E + p.Ns), dim3(256), 0, st,
-                     p);
+template <int AMODE, int TILE = 128>
+static hipError_t launch_router_wgrad(const WgradArgs& p, hipStream_t st) {
+  hipLaunchKernelGGL((router_wgrad<AMODE, TILE>), dim3(ceil_div(p.N, TILE), ceil_div(p.M, TILE)),
+                     dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -425,28 +385,25 @@ hipError_t launch_router_backward(const moe_config& c, const void* x, const void
                                   const float* dz, float* dx, float* dw, hipStream_t st) {
   const int T = c.num_tokens, E = c.num_experts, H = c.hidden;
   WgradArgs w{};
-  w.E = 0;                                  // one group: "shared" rows [0, rows)
-  w.Ns = 1;
-  w.TK = 0;
   w.Af = dz;
   w.lda = E;
   w.ldb = H;
   w.N = H;
   hipError_t err = hipSuccess;
   if (dx) {
-    w.T = E;
+    w.rows = E;
     w.M = T;
     w.B = static_cast<const uint16_t*>(w_router);
     w.C = dx;
-    if ((err = launch_wgrad<kWgPlainB, kWgAf32T>(w, st)) != hipSuccess) return err;
+    if ((err = launch_router_wgrad<kWgAf32T>(w, st)) != hipSuccess) return err;
   }
   if (dw) {
-    w.T = T;
+    w.rows = T;
     w.M = E;
     w.B = static_cast<const uint16_t*>(x);
     w.C = dw;
     // few output tiles (E x H): 64 x 64 tiles keep more workgroups in flight
-    if ((err = launch_wgrad<kWgPlainB, kWgAf32, 64>(w, st)) != hipSuccess) return err;
+    if ((err = launch_router_wgrad<kWgAf32, 64>(w, st)) != hipSuccess) return err;
   }
   return err;
 }
@@ -523,35 +480,11 @@ hipError_t launch_expert_backward(const moe_config& c, const void* x, const int3
                                         I2, I2, rows, I}, s);
   if (err != hipSuccess) return err;
   if (dw_down) {
-    // dW_down = dy^T h, dW_gate = da^T u, dW_up = db^T u over each expert's rows
-    WgradArgs w{};
-    w.offsets = offsets;
-    w.row_token = row_token;
-    w.T = T;
-    w.TK = TK;
-    w.E = E;
-    w.Ns = Ns;
-    w.A = static_cast<const uint16_t*>(dy_rows);
-    w.lda = H;
-    w.B = ws.ab;
-    w.ldb = 2LL * I;
-    w.boff = I;
-    w.M = H;
-    w.N = I;
-    w.C = dw_down;
-    if ((err = launch_wgrad<kWgSwigluB>(w, s)) != hipSuccess) return err;
-    w.A = ws.dab;
-    w.lda = 2LL * I;
-    w.B = static_cast<const uint16_t*>(x);
-    w.ldb = H;
-    w.boff = 0;
-    w.M = I;
-    w.N = H;
-    w.C = dw_gate;
-    if ((err = launch_wgrad<kWgGatherB>(w, s)) != hipSuccess) return err;
-    w.A = ws.dab + I;
-    w.C = dw_up;
-    if ((err = launch_wgrad<kWgGatherB>(w, s)) != hipSuccess) return err;
+    // dW_down = dy^T h, dW_gate = da^T u, dW_up = db^T u over each expert's rows, on the
+    // matrix cores (wgrad.hip)
+    err = launch_expert_wgrad_mfma(c, x, offsets, row_token, dy_rows, ws.ab, ws.dab, dw_gate,
+                                   dw_up, dw_down, ws.pack, s);
+    if (err != hipSuccess) return err;
   }
   if (!dx) return hipSuccess;
   // dX = [da | db] [W_gate ; W_up]

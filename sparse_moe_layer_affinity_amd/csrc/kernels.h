@@ -28,6 +28,17 @@ struct Workspace {
   size_t bytes;        // total bytes of the layout
 };
 
+// Transposed, padded operands of the MFMA weight gradients (see wgrad.hip):
+// [features][packed rows], every expert's rows padded to a multiple of 64
+struct WgradPackWorkspace {
+  int32_t* poff;       // [E+Ns+1] padded row offsets
+  uint16_t* xt;        // [hidden][packed rows]  u^T (x gathered by row)
+  uint16_t* dyt;       // [hidden][packed rows]  dy^T
+  uint16_t* dabt;      // [2*inter][packed rows] [da | db]^T
+  uint16_t* ht;        // [inter][packed rows]   h^T
+};
+long long wgrad_packed_rows(const moe_config& c);
+
 // Scratch of the expert backward (its own workspace: the transposed weights alone are
 // as large as the weights)
 struct BackwardWorkspace {
@@ -40,6 +51,7 @@ struct BackwardWorkspace {
   uint16_t* dh;        // [rows, inter] gradient of h
   uint16_t* dab;       // [rows, 2*inter] their gradients
   uint16_t* dx_rows;   // [rows, hidden] input gradient of every grouped row
+  WgradPackWorkspace pack;  // operands of the weight gradients
   size_t bytes;
 };
 BackwardWorkspace backward_workspace_layout(const moe_config& c, void* base);
@@ -107,6 +119,11 @@ hipError_t launch_expert_backward(const moe_config& c, const void* x, const int3
                                   float* dw_gate, float* dw_up, float* dw_down,
                                   bool reuse_transposed, const BackwardWorkspace& ws,
                                   hipStream_t s);
+hipError_t launch_expert_wgrad_mfma(const moe_config& c, const void* x, const int32_t* offsets,
+                                    const int32_t* row_token, const void* dy_rows,
+                                    const uint16_t* ab, const uint16_t* dab, float* dw_gate,
+                                    float* dw_up, float* dw_down, const WgradPackWorkspace& ws,
+                                    hipStream_t s);
 hipError_t launch_router_backward(const moe_config& c, const void* x, const void* w_router,
                                   const float* dz, float* dx, float* dw, hipStream_t s);
 hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
