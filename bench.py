@@ -60,6 +60,20 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def stored_counters(workload: str):
+    """MFMA-busy fraction, sustained shader clock and fetched/written bytes per expert-GEMM
+    kernel from the committed counter runs (rocprofv3 --pmc), or None when the kernels
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("kernels")
+
+
 def stored_traffic(workload: str):
     """HBM bytes per moe_grouped_ffn call from the committed counter runs, or None
     when the kernels changed since the counters were taken."""
@@ -73,38 +87,105 @@ def stored_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, d, n_tokens: int):
-    """The oracle as it stands, on n_tokens seeded tokens of the batch: routing and
-    the full layer output (shared + routed SwiGLU experts, float64)."""
+def cpu_baseline(cfg, d, n_tokens: int, n_tokens_1t: int = 8):
+    """The oracle as it stands (float64 numpy), on the host cores of this machine:
+      * routing of all T tokens of the batch (affinities, bias, group limit, top-K,
+        gates), tokens/s;
+      * the full layer on n_tokens seeded tokens of the batch (their routing, then the
+        shared and the K routed SwiGLU experts and the weighted sum), tokens/s; the
+        device-to-host copies of each expert's weights and their widening to float64
+        are timed apart and excluded;
+      * the same layer leg with BLAS limited to one thread on n_tokens_1t tokens.
+    ``value`` is the layer rate (the metric's unit)."""
     import numpy as np
     import oracle
     import workloads
-    rows = workloads.sample_rows(cfg.T, n_tokens, seed=1).numpy()
-    x = d["x"][rows.tolist()].cpu()
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     bias = d["bias"].cpu().numpy()
     w_r = d["w_router"].cpu()
+    x_all = d["x"].cpu()
 
-    def get(e):
-        if workloads.is_fp8(cfg.w):
-            return tuple(oracle.dequantize_blocks_128(d[n][e], d["s" + n[1:]][e])
-                         for n in ("w_gate", "w_up", "w_down"))
-        return tuple(d[n][e].to("cpu").double().numpy() for n in ("w_gate", "w_up", "w_down"))
+    def get_expert(fetch):
+        def get(e):
+            t = time.perf_counter()
+            if workloads.is_fp8(cfg.w):
+                w = tuple(oracle.dequantize_blocks_128(d[n][e], d["s" + n[1:]][e])
+                          for n in ("w_gate", "w_up", "w_down"))
+            else:
+                w = tuple(d[n][e].to("cpu").double().numpy() for n in ("w_gate", "w_up", "w_down"))
+            fetch[0] += time.perf_counter() - t
+            return w
+        return get
+
+    def layer_leg(n):
+        rows = workloads.sample_rows(cfg.T, n, seed=1).numpy()
+        x = x_all[rows.tolist()]
+        fetch = [0.0]
+        t0 = time.perf_counter()
+        r = oracle.route(x, w_r, bias, cfg.G, cfg.M, cfg.topn, cfg.K)
+        oracle.layer_output(x, r.idx, r.gate, get_expert(fetch), cfg.E, cfg.Ns)
+        return n / (time.perf_counter() - t0 - fetch[0]), fetch[0]
 
     t0 = time.perf_counter()
-    r = oracle.route(x, w_r, bias, cfg.G, cfg.M, cfg.topn, cfg.K)
-    oracle.layer_output(x, r.idx, r.gate, get, cfg.E, cfg.Ns)
-    dt = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        blas = 1
+    oracle.route(x_all, w_r, bias, cfg.G, cfg.M, cfg.topn, cfg.K)
+    route_rate = cfg.T / (time.perf_counter() - t0)
+    layer_rate, fetch_s = layer_leg(n_tokens)
+    with threadpool_limits(limits=1):
+        layer_rate_1t, _ = layer_leg(n_tokens_1t)
+    blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     cores = min(len(os.sched_getaffinity(0)), max(blas, 1))
-    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+    return {"value": round(layer_rate, 3), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{n_tokens} seeded tokens of the {cfg.T}-token batch: float64 routing and "
-                      f"the full layer output (shared + {cfg.K} routed SwiGLU experts, weights "
-                      f"streamed from HBM and widened to float64); {dt:.1f} s"}
+            "routing_all_tokens_per_s": round(route_rate, 1),
+            "layer_tokens_per_s_1_thread": round(layer_rate_1t, 3),
+            "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(blas),
+            "sample": f"layer: {n_tokens} seeded tokens of the {cfg.T}-token batch (float64 "
+                      f"routing, shared + {cfg.K} routed SwiGLU experts, weighted sum; the "
+                      f"{fetch_s:.1f} s of weight copies to the host and widening to float64 "
+                      f"excluded); routing: all {cfg.T} tokens; 1 thread: {n_tokens_1t} tokens"}
+
+
+def calibration_leg(stream):
+    """Measured ceilings of this device (calibration kernels of libmoe_calib.so, timed
+    between HIP events on the bench stream after the layer steps): a plain read stream
+    over 4 GiB (16-byte vectors, eight in flight per lane) and back-to-back MFMAs
+    (eight accumulator chains per wave, four waves per CU, sustained about 20 ms) in
+    bf16 (32x32x16) and e4m3 (32x32x64).  Each is run twice; the second run counts."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_layer_affinity_amd", "libmoe_calib.so"))
+    lib.moe_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    s = stream.cuda_stream
+
+    def timed(fn):
+        ms = None
+        for _ in range(2):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            assert fn() == 0
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1])
+        return ms
+
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    blocks = 2048
+    out = torch.empty(blocks * 256 * 4, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: lib.moe_calib_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, s))
+    read_gbps = nbytes / (ms * 1e-3) / 1e9
+    del buf
+    res = {"hbm_read_GBps": round(read_gbps, 1)}
+    iters = 20000
+    outf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    for name, fp8, flop in (("mfma_bf16_TFLOPs", 0, 32768), ("mfma_e4m3_TFLOPs", 1, 131072)):
+        ms = timed(lambda: lib.moe_calib_mfma(fp8, iters, outf.data_ptr(), blocks, s))
+        res[name] = round(blocks * 4 * iters * 8 * flop / (ms * 1e-3) / 1e12, 1)
+    return res
 
 
 def balance_loss_leg(moe, cfg, c, d, idx, ws, stream, reps: int = 20):
@@ -300,33 +381,46 @@ def main():
     bias = d["bias"].clone()
     weights = {k: d[k] for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down") if k in d}
     stages = ["route", "permute", "grouped_ffn", "combine", "bias_update"]
+    n_all = args.warmup + args.steps
+    # every step writes its loads to a buffer of its own (read after the timed region);
+    # the skewed workload draws a fresh seeded batch per step (the balancing loop of its
+    # configuration), generated before the timed region and resident in HBM
+    loads = torch.empty((n_all, E), dtype=torch.int32, device="cuda")
+    fresh = cfg.steps > 1
+    batches = [d["x"]] + ([workloads.make_tokens(cfg, step=s, device="cuda")
+                           for s in range(1, n_all)] if fresh else [])
 
-    def step(ev=None):
-        def mark(i):
+    def step(i, ev=None):
+        def mark(j):
             if ev is not None:
-                ev[i].record(stream)
+                ev[j].record(stream)
+        x = batches[i] if fresh else d["x"]
+        load = loads[i]
         mark(0)
-        moe.moe_route(c, d["x"], d["w_router"], bias, idx, gate, ws)
+        moe.moe_route(c, x, d["w_router"], bias, idx, gate, ws)
         mark(1)
         moe.moe_permute(c, idx, load, offsets, row_token, pair_row, ws)
         mark(2)
-        moe.moe_grouped_ffn(c, d["x"], offsets, row_token, weights, y_rows, ws)
+        moe.moe_grouped_ffn(c, x, offsets, row_token, weights, y_rows, ws)
         mark(3)
         moe.moe_combine(c, y_rows, pair_row, gate, None, y)
         mark(4)
         moe.moe_bias_update(c, load, cfg.gamma, bias)
         mark(5)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(events[s])
+        step(args.warmup + s, events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    timed_loads = loads[args.warmup:].cpu().numpy()
+    load = loads[n_all - 1]
+    d["x"] = batches[n_all - 1] if fresh else d["x"]       # the last step's batch, for the extras
 
     stage_ms = {st: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                                    for s in range(args.steps)])) for i, st in enumerate(stages)}
@@ -336,23 +430,35 @@ def main():
     ffn_flops = 6.0 * cfg.hidden * cfg.inter * T * (K + cfg.Ns)      # real rows only
     ffn_ms = stage_ms["grouped_ffn"]
     gemm_tflops = ffn_flops / (ffn_ms * 1e-3) / 1e12
-    touched = int((load > 0).sum().item()) + cfg.Ns
+    # algorithmic bytes of each timed step: the weights of the experts that step touched
+    # (the bias moves every step, so the set does) + x read + the rows written once
+    touched = (timed_loads > 0).sum(1) + cfg.Ns                          # [steps]
     wbytes_per_elem = 1 if workloads.is_fp8(cfg.w) else (4 if cfg.w == "f32" else 2)
-    weight_bytes = touched * 3 * cfg.hidden * cfg.inter * wbytes_per_elem
+    per_expert = 3 * cfg.hidden * cfg.inter * wbytes_per_elem
     if workloads.is_fp8(cfg.w):
-        weight_bytes += touched * 3 * (cfg.hidden // 128) * (cfg.inter // 128) * 4
-    ffn_bytes = weight_bytes + 2 * T * cfg.hidden * (4 if cfg.act == "f32" else 2)
+        per_expert += 3 * (cfg.hidden // 128) * (cfg.inter // 128) * 4
+    ab = 4 if cfg.act == "f32" else 2
+    ffn_bytes = float(np.mean(touched)) * per_expert + 2 * T * cfg.hidden * ab
+    # the layer's: + the router weight, the bias, indices, gates and loads
+    layer_bytes = ffn_bytes + E * cfg.hidden * ab + E * 8 + T * K * 8
     decode = cfg.T <= 512
     if decode:
         achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK, 4)}
+        lay = layer_bytes / (ms_per_step * 1e-3) / 1e9
+        roof["layer"] = {"achieved": round(lay, 1), "frac": round(lay / HBM_PEAK, 4),
+                         "bytes": layer_bytes, "ms": round(ms_per_step, 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK[cfg.w],
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK[cfg.w], 4)}
     roof["traffic"] = stored_traffic(cfg.name)
     roof["kernel"] = "moe_grouped_ffn (grouped_gemm gated GEMM1 + GEMM2)"
-    roof["algorithmic"] = {"flops": ffn_flops, "bytes": ffn_bytes}
+    roof["algorithmic"] = {"flops": ffn_flops, "bytes": ffn_bytes,
+                           "touched_experts_per_step": [int(v) for v in touched]}
+    counters = stored_counters(cfg.name)
+    if counters:
+        roof["counters"] = counters
 
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -369,6 +475,20 @@ def main():
         "max_over_mean_load": round(float(load.max().item()) / (T * K / E), 3),
         "roofline": roof,
     }
+    if fresh:
+        # the balancing loop: max/mean load of every step, warm-up steps first
+        mean_load = T * K / E
+        result["balancing"] = {
+            "steps": n_all, "gamma": cfg.gamma, "fresh_batch_per_step": True,
+            "max_over_mean_load_per_step": [round(float(v) / mean_load, 3)
+                                            for v in loads.max(1).values.cpu().numpy()]}
+
+    cal = calibration_leg(stream)
+    result["calibration"] = cal
+    measured = cal["hbm_read_GBps"] if decode else cal["mfma_e4m3_TFLOPs" if workloads.is_fp8(cfg.w)
+                                                       else "mfma_bf16_TFLOPs"]
+    roof["measured_peak"] = measured
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / measured, 4)
     result["balance_loss"] = balance_loss_leg(moe, cfg, c, d, idx, ws, stream)
     result["backward"] = backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row,
                                       y_rows, y, ws, stream)
