@@ -30,26 +30,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
 }
 
 // fp32 -> OCP e4m3fn code: round to nearest even, saturate to +-448, keep the sign
-// of values that round to zero, NaN -> 0x7F.
+// of values that round to zero, NaN -> 0x7F.  Branch-free (every lane takes the same
+// path): below 2^-6 the code is the value on the subnormal grid of 2^-9, RNE; above,
+// the code is the fp32 bit pattern's exponent and top three mantissa bits, rounded to
+// nearest even by adding 0x7FFFF plus the kept lsb before the shift (a carry moves
+// into the exponent), rebiased by (127 - 7) << 3 = 960; magnitudes at or above 448
+// give 0x7E.
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7Fu;
-  if (a >= 0x43e00000u) return sign | 0x7Eu;              // |v| >= 448
-  if (a < 0x3c800000u) {                                  // |v| < 2^-6: subnormal grid of 2^-9
-    float q = rintf(__uint_as_float(a) * 512.0f);         // exact scaling, RNE to 0..8
-    return sign | uint32_t(q);                            // 8 is the smallest normal, code 0x08
-  }
-  int e = int(a >> 23) - 127;                             // -6 .. 8
-  uint32_t mant = a & 0x7fffffu;
-  uint32_t m = mant >> 20;
-  uint32_t rem = mant & 0xfffffu;
-  if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
-    if (++m == 8u) { m = 0u; ++e; }
-  }
-  uint32_t code = (uint32_t(e + 7) << 3) | m;
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  const uint32_t sub = uint32_t(rintf(__uint_as_float(a) * 512.0f));   // used if a < 2^-6
+  const uint32_t an = a < 0x43e00000u ? a : 0x43e00000u;
+  const uint32_t nrm = ((an + 0x7ffffu + ((an >> 20) & 1u)) >> 20) - 960u;
+  // both candidates exist before the selection (otherwise the compiler turns it back
+  // into a divergent branch around each computation)
+  asm volatile("" :: "v"(sub), "v"(nrm));
+  const uint32_t code = sign | (a < 0x3c800000u ? sub : (nrm > 0x7Eu ? 0x7Eu : nrm));
+  return a > 0x7f800000u ? 0x7Fu : code;
 }
 
 // Value of an e4m3fn code (codes 0x7F / 0xFF never reach the kernels: the

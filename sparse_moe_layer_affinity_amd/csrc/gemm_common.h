@@ -43,7 +43,9 @@ struct Fp8Args {
   const float* S1;           // GEMM1: up
   long long b_stride;        // bytes per expert (N*K)
   long long s_stride;        // floats per expert
-  uint16_t* C;               // bf16 output [rows, ldc]
+  uint16_t* C;               // bf16 output [rows, ldc] (plain mode; gated without Q)
+  uint8_t* Q;                // gated: e4m3 codes of h [rows, ldc], quantised in the epilogue
+  float* QS;                 // gated: their 1x128 scales [ldc/128, scale_rows]
   int ldc, N, K;
   int T, TK;
   int n_tiles;
@@ -97,6 +99,85 @@ __device__ __forceinline__ void stage_barrier() {
 __device__ __forceinline__ float silu_fast(float a) {
   const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);
   return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// GEMM1 epilogue of the FP8 expert GEMMs with 256 weight rows per tile (128 gate rows
+// over the matching 128 up rows) and 16x16x128 MFMA blocks (lane l holds weight rows
+// 4 (l >> 4) + q of each 16-row block, token l & 15): h = silu(gate) * up, rounded once
+// to bf16, then quantised per token over the tile's 128 h columns -- one 1x128 block
+// ("DeepSeek-V3 ... 技术解析" (devpress), section 2) -- with the arithmetic of
+// act_quant_e4m3: scale amax / 448 (pow2: the smallest power of two s >= 2^-126 with
+// amax <= 448 s), code = RNE-saturate(h / scale).  Each wave holds 64 of the 128
+// columns (wn = w & 1 picks the half).  Pass 1 reads each accumulator once, writes the
+// bf16 h to the wave's LDS staging area (stage: 8 waves x 80 tokens x 64 columns,
+// 80 KB; the caller's operand buffers, free once every wave has passed the barrier at
+// the start) and its per-token amax to amax_lds (8 x 80 floats); after a second
+// workgroup barrier pass 2 combines the two halves' amax and quantises from LDS.
+// Every wave of the workgroup calls this (two barriers).  Codes go to hq [rows][ldq]
+// (4 bytes per lane and block), scales to hs [ldq / 128][scale_rows] at block n0 / 128.
+template <int NJB, class Acc>
+__device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l, int m0,
+                                                    int mvalid, int n0, uint8_t* hq, int ldq,
+                                                    float* hs, int scale_rows, float* amax_lds,
+                                                    uint32_t* stage, bool pow2) {
+  const int wn = w & 1, wt = w >> 1;
+  // staging: wave w, token block jb, block ib: 64 lanes x 2 dwords (lane l's four bf16)
+  uint2* st = reinterpret_cast<uint2*>(stage) + size_t(w) * (5 * 4 * 64);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // operand buffers free
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {
+    float a = 0.f;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      float hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q];
+      const uint32_t lo = pack_bf16x2(hv[0], hv[1]), hi = pack_bf16x2(hv[2], hv[3]);
+      st[(jb * 4 + ib) * 64 + l] = make_uint2(lo, hi);
+      a = fmaxf(a, fmaxf(fmaxf(fabsf(bf16_bits_to_f32(lo & 0xffffu)), fabsf(bf16_bits_to_f32(lo >> 16))),
+                         fmaxf(fabsf(bf16_bits_to_f32(hi & 0xffffu)), fabsf(bf16_bits_to_f32(hi >> 16)))));
+    }
+    a = fmaxf(a, __shfl_xor(a, 16));
+    a = fmaxf(a, __shfl_xor(a, 32));
+    if ((l >> 4) == 0) amax_lds[w * 80 + jb * 16 + (l & 15)] = a;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {
+    const int tk = jb * 16 + (l & 15);
+    const float a = fmaxf(amax_lds[w * 80 + tk], amax_lds[(w ^ 1) * 80 + tk]);
+    float s = 1.0f;
+    if (a > 0.f) {
+      if (pow2) {
+        int e;
+        const float m = frexpf(a, &e);
+        s = ldexpf(1.0f, max(m <= 0.875f ? e - 9 : e - 8, -126));
+      } else {
+        s = __fdiv_rn(a, 448.0f);
+      }
+    }
+    const int rl = wt * 80 + tk;
+    if (rl >= mvalid) continue;
+    uint8_t* qrow = hq + size_t(m0 + rl) * ldq;
+    const float rs = 1.0f / s;                           // exact for a power of two
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const uint2 hb = st[(jb * 4 + ib) * 64 + l];
+      const float v[4] = {bf16_bits_to_f32(hb.x & 0xffffu), bf16_bits_to_f32(hb.x >> 16),
+                          bf16_bits_to_f32(hb.y & 0xffffu), bf16_bits_to_f32(hb.y >> 16)};
+      const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        c |= f32_to_e4m3_rne_sat(pow2 ? v[q] * rs : __fdiv_rn(v[q], s)) << (8 * q);
+      *reinterpret_cast<uint32_t*>(qrow + col) = c;
+    }
+    if (wn == 0 && (l >> 4) == 0) hs[size_t(n0 / 128) * scale_rows + m0 + rl] = s;
+  }
 }
 
 }  // namespace moe

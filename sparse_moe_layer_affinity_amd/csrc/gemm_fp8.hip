@@ -304,6 +304,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   err = launch_build_schedule(c, offsets, kFp8BT, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
   const int rounds = ceil_div(expert_row_blocks_upper(c, kFp8BT), kXcds);
+  // GEMM1: gated; the power-of-two kernel's tiles hold 128 h columns, a whole 1x128
+  // block, and quantise h to e4m3 (codes + scales) in their epilogue
   Fp8Args a{};
   a.A = ws.xq;
   a.a_scales = ws.xg_scales;
@@ -316,26 +318,32 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   a.S1 = w.s_up;
   a.b_stride = 1LL * I * H;
   a.s_stride = 1LL * (I / 128) * (H / 128);
-  a.C = static_cast<uint16_t*>(ws.h);
+  a.Q = ws.hq;
+  a.QS = ws.h_scales;
   a.ldc = I;
   a.N = I;
   a.K = H;
   a.T = T;
   a.TK = TK;
-  a.n_tiles = ceil_div(I, 64);
+  a.n_tiles = ceil_div(I, 128);
   a.gather = 1;
   a.a_rows = T;
   a.scale_rows = rows;
   if (pow2) {
-    Fp8Args p = a;
-    p.n_tiles = ceil_div(I, 128);
-    err = launch_gemm_fp8p2(p, true, rounds * kXcds * p.n_tiles, s);
+    err = launch_gemm_fp8p2(a, true, rounds * kXcds * a.n_tiles, s);
     if (err != hipSuccess) return err;
   } else {
-    hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles), dim3(512), 0, s, a);
+    // 128-row tiles (64 h columns): h goes out in bf16 and is quantised by its own pass
+    Fp8Args f = a;
+    f.Q = nullptr;
+    f.QS = nullptr;
+    f.C = static_cast<uint16_t*>(ws.h);
+    f.n_tiles = ceil_div(I, 64);
+    hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * f.n_tiles), dim3(512), 0, s, f);
+    err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true, false);
+    if (err != hipSuccess) return err;
   }
-  err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true, pow2);
-  if (err != hipSuccess) return err;
+  // GEMM2: plain, on the e4m3 h
   Fp8Args d = a;
   d.A = ws.hq;
   d.a_scales = ws.h_scales;
@@ -350,15 +358,16 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   d.b_stride = 1LL * H * I;
   d.s_stride = 1LL * (H / 128) * (I / 128);
   d.C = static_cast<uint16_t*>(y_rows);
+  d.Q = nullptr;
+  d.QS = nullptr;
   d.ldc = H;
   d.N = H;
   d.K = I;
-  d.n_tiles = ceil_div(H, 128);
   if (pow2) {
-    Fp8Args p = d;
-    p.n_tiles = ceil_div(H, 256);
-    return launch_gemm_fp8p2(p, false, rounds * kXcds * p.n_tiles, s);
+    d.n_tiles = ceil_div(H, 256);
+    return launch_gemm_fp8p2(d, false, rounds * kXcds * d.n_tiles, s);
   }
+  d.n_tiles = ceil_div(H, 128);
   hipLaunchKernelGGL(grouped_gemm_fp8<kPlainBf16>, dim3(rounds * kXcds * d.n_tiles), dim3(512), 0, s, d);
   return hipGetLastError();
 }

@@ -63,8 +63,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
   constexpr uint32_t kSaStage = 4 * BT;                   // 1280 B
   constexpr uint32_t kSwOff = kSaOff + 2 * kSaStage;
   constexpr uint32_t kSwStage = 768;
+  constexpr uint32_t kAmOff = kSwOff + 2 * kSwStage;      // the epilogue's amax exchange
   constexpr int BN_OUT = MODE == kGatedBf16 ? BW / 2 : BW;
-  __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2 * kSwStage) / 16];
+  __shared__ __attribute__((aligned(1024))) uint4 lds[(kAmOff + 8 * 80 * 4) / 16];
 
   // ---- tile decode (as the fp32-scale FP8 kernel) -------------------------------------
   const int b = blockIdx.x;
@@ -252,6 +253,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
     }
 
     // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
+    if constexpr (MODE == kGatedBf16) {
+      if (a.Q) {
+        // staging in the token buffer and the weight ring (80 KB of their 136 KB)
+        fp8_epilogue_hquant<NJB>(acc, w, l, m0, mvalid, n0, a.Q, a.ldc, a.QS, a.scale_rows,
+                                 reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kAmOff),
+                                 reinterpret_cast<uint32_t*>(lds), true);
+        return;
+      }
+    }
   #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
       const int rl = wt * 80 + jb * 16 + (l & 15);

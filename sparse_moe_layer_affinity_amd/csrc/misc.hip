@@ -157,55 +157,82 @@ hipError_t launch_bias_update(const moe_config& c, const int32_t* load, float ga
 // at least 2^-126 (a normal float32, whose exponent field is its 8-bit exponent code):
 // with amax = m 2^e, m in [0.5, 1), and 448 = 0.875 2^9, s = 2^(e-9) if m <= 0.875,
 // else 2^(e-8); the quotient x / s is then exact.
+// A grid of a few workgroups per CU walks the blocks with a stride, each wave taking
+// kQuantUnroll groups of four blocks per step with all their loads issued first.
+constexpr int kQuantUnroll = 4;
+
 __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x, int rows,
                                                       int cols, uint8_t* __restrict__ q,
                                                       float* __restrict__ scales, int transposed,
                                                       int pow2) {
-  const int bpr = cols / 128;                                   // blocks per row
-  const long long blk = (1LL * blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + ((threadIdx.x >> 4) & 3);
-  const bool valid = blk < 1LL * rows * bpr;
+  // block counts stay below 2^31 (checked by the launcher): 32-bit index arithmetic
+  const uint32_t bpr = uint32_t(cols) / 128u;                   // blocks per row
+  const uint32_t nblk = uint32_t(rows) * bpr;
   const int l16 = threadIdx.x & 15;
-  const long long r = valid ? blk / bpr : 0;
-  const int j = valid ? int(blk % bpr) : 0;
-  const size_t off = size_t(r) * cols + size_t(j) * 128 + size_t(l16) * 8;
-  uint4 p = make_uint4(0, 0, 0, 0);
-  if (valid) p = *reinterpret_cast<const uint4*>(x + off);
-  const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
-  float v[8];
+  // block of group u of this lane in step it: ((it * grid + wg) * 4 + wave) * U + u, then
+  // * 4 + the lane's quarter
+  const uint32_t wave_id = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t waves = gridDim.x * 4u;
+  for (uint32_t base = wave_id * kQuantUnroll; base < (nblk + 3u) / 4u; base += waves * kQuantUnroll) {
+    uint4 p[kQuantUnroll];
+    uint32_t blk[kQuantUnroll];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_bits_to_f32(wd[i] & 0xffffu);
-    v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
-  }
-  float amax = 0.f;
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      blk[u] = (base + u) * 4u + ((threadIdx.x >> 4) & 3u);
+      p[u] = make_uint4(0, 0, 0, 0);
+      if (blk[u] < nblk) {
+        const uint32_t r = blk[u] / bpr, j = blk[u] - r * bpr;
+        p[u] = *reinterpret_cast<const uint4*>(x + size_t(r) * cols + size_t(j) * 128 + size_t(l16) * 8);
+      }
+    }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const uint32_t wd[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
+      float v[8];
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  if (!valid) return;
-  float s = 1.0f;
-  if (amax > 0.f) {
-    if (pow2) {
-      int e;
-      const float m = frexpf(amax, &e);
-      s = ldexpf(1.0f, max(m <= 0.875f ? e - 9 : e - 8, -126));
-    } else {
-      s = __fdiv_rn(amax, 448.0f);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(wd[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      if (blk[u] >= nblk) continue;
+      float s = 1.0f;
+      if (amax > 0.f) {
+        if (pow2) {
+          int e;
+          const float m = frexpf(amax, &e);
+          s = ldexpf(1.0f, max(m <= 0.875f ? e - 9 : e - 8, -126));
+        } else {
+          s = __fdiv_rn(amax, 448.0f);
+        }
+      }
+      // x / s: an IEEE division (pow2: the product with 1/s, exact for a power of two)
+      uint32_t c[8];
+      const float rs = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = f32_to_e4m3_rne_sat(pow2 ? v[i] * rs : __fdiv_rn(v[i], s));
+      const uint32_t r = blk[u] / bpr, j = blk[u] - r * bpr;
+      const size_t off = size_t(r) * cols + size_t(j) * 128 + size_t(l16) * 8;
+      *reinterpret_cast<uint2*>(q + off) =
+          make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+      if (l16 == 0) scales[transposed ? size_t(j) * rows + r : size_t(r) * bpr + j] = s;
     }
   }
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = f32_to_e4m3_rne_sat(__fdiv_rn(v[i], s));
-  *reinterpret_cast<uint2*>(q + off) =
-      make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                 c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-  if (l16 == 0) scales[transposed ? size_t(j) * rows + r : size_t(r) * bpr + j] = s;
 }
 
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,
                             hipStream_t s, bool transposed, bool pow2) {
   const long long blocks = 1LL * rows * (cols / 128);
-  hipLaunchKernelGGL(act_quant_e4m3, dim3(unsigned((blocks + 15) / 16)), dim3(256), 0, s,
+  if (blocks >= (1LL << 31)) return hipErrorNotSupported;
+  // 16 blocks per workgroup and step; at most 8 workgroups per CU (2048 on MI355X)
+  const long long need = (blocks + 16 * kQuantUnroll - 1) / (16 * kQuantUnroll);
+  const unsigned grid = unsigned(need < 2048 ? need : 2048);
+  hipLaunchKernelGGL(act_quant_e4m3, dim3(grid), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), rows, cols, q, scales, transposed ? 1 : 0,
                      pow2 ? 1 : 0);
   return hipGetLastError();
