@@ -16,7 +16,8 @@
 //
 // GEMM tile 256 x 256, four waves of 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16
 // accumulators in AGPRs, the MFMA computing the transposed tile so that a lane holds
-// four adjacent output columns of one row: 16-byte fp32 stores).  K advances 64 rows
+// four adjacent output columns of one row; the tile leaves through LDS as whole
+// 512-byte row segments).  K advances 64 rows
 // per stage through two 64 KB LDS buffers filled by buffer loads in LDS mode; rows
 // are 128 bytes, chunk c of row r in slot c ^ (r & 7) ^ ((r >> 3) & 1) (conflict-free
 // fragment reads).  One workgroup per (expert, tile); the shared experts' tiles
@@ -215,24 +216,35 @@ __global__ __launch_bounds__(256) void wgrad_mfma(WgMfmaArgs p) {
     }
   }
 
-  // value r of lane l of block (i, j): output row wm*128 + 32 i + (l & 31), column
-  // wn*128 + 32 j + 8 (r >> 2) + 4 (l >> 5) + (r & 3)
+  // Epilogue.  Value r of lane l of block (i, j) is output row wm*128 + 32 i + (l & 31),
+  // column wn*128 + 32 j + 8 (r >> 2) + 4 (l >> 5) + (r & 3).  Each wave stages one
+  // 32 x 128 fp32 strip at a time (its rows 32 i ..) in its own 16.5 KB of LDS (row
+  // pitch 132 floats), then stores it as whole 512-byte row segments: each store
+  // instruction writes two rows.
+  stage_barrier();                           // every wave is done with the operand buffers
+  constexpr int kPitch = 132;
+  float* stg = reinterpret_cast<float*>(lds) + w * (32 * kPitch);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + 32 * i + (l & 31);
-    if (m >= p.M) continue;
-    float* crow = m < p.M0 ? p.C0 + size_t(g) * p.cstride + size_t(m) * p.N
-                           : p.C1 + size_t(g) * p.cstride + size_t(m - p.M0) * p.N;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * (l >> 5);
-        if (n < p.N)
-          *reinterpret_cast<float4*>(crow + n) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(stg + (l & 31) * kPitch + 32 * j + 8 * q + 4 * (l >> 5)) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+    const int n = n0 + wn * 128 + 4 * (l & 31);
+#pragma unroll
+    for (int rr = 0; rr < 32; rr += 2) {
+      const int row = rr + (l >> 5);
+      const int m = m0 + wm * 128 + 32 * i + row;
+      const float4 v = *reinterpret_cast<const float4*>(stg + row * kPitch + 4 * (l & 31));
+      if (m < p.M && n < p.N) {
+        float* crow = m < p.M0 ? p.C0 + size_t(g) * p.cstride + size_t(m) * p.N
+                               : p.C1 + size_t(g) * p.cstride + size_t(m - p.M0) * p.N;
+        *reinterpret_cast<float4*>(crow + n) = v;
       }
+    }
   }
 }
 
