@@ -235,7 +235,7 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
     writes the [T, E] logit gradient; SwiGLU backward reads three [rows, inter] arrays
     and writes two.  The experts' input gradient (bf16) is timed on the step's own
     inputs and the combine backward's row gradients, reported with its GEMM FLOPs, and
-    their weight gradients with the a, b and dh GEMMs they need (transposes reused), and
+    their weight gradients with the a, b and dh GEMMs they need, and
     the router logits' backward (dx and dW_r, 4 T E H flops)."""
     import torch
     T, E, K, H = cfg.T, cfg.E, cfg.K, cfg.hidden
@@ -288,24 +288,18 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
         wts = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
         us_ex = timed(lambda: moe.moe_expert_backward_input(c, d["x"], offsets, row_token, pair_row,
                                                             wts, dy_rows, dx, bws), n=5)
-        us_re = timed(lambda: moe.moe_expert_backward_input(c, d["x"], offsets, row_token, pair_row,
-                                                            wts, dy_rows, dx, bws,
-                                                            reuse_transposed=True), n=5)
         G = cfg.E + cfg.Ns
         dwg = torch.empty((G, cfg.inter, H), device="cuda")
         dwu = torch.empty_like(dwg)
         dwd = torch.empty((G, H, cfg.inter), device="cuda")
         us_w = timed(lambda: moe.moe_expert_backward(c, d["x"], offsets, row_token, pair_row, wts,
-                                                     dy_rows, None, dwg, dwu, dwd, bws,
-                                                     reuse_transposed=True), n=2)
+                                                     dy_rows, None, dwg, dwu, dwd, bws), n=2)
         del dwg, dwu, dwd
         flops_w = 6.0 * cfg.rows * H * cfg.inter      # three weight gradients: 2 r H I each
         flops = 8.0 * cfg.rows * H * cfg.inter        # a, b, dh: 2 r H I each; dX: 4 r H I
         ex = {"expert_backward_input_us": round(us_ex, 1),
-              "expert_backward_input_reuse_us": round(us_re, 1),
               "expert_backward_input_gemm_flops": flops,
               "expert_backward_input_tflops": round(flops / (us_ex * 1e-6) / 1e12, 1),
-              "expert_backward_input_reuse_tflops": round(flops / (us_re * 1e-6) / 1e12, 1),
               "expert_backward_weights_us": round(us_w, 1),
               "expert_backward_weights_flops": flops_w + 6.0 * cfg.rows * H * cfg.inter,
               "expert_backward_weights_tflops": round(

@@ -241,8 +241,8 @@ moe_status moe_gate_backward(const moe_config* cfg, const float* scores, const i
 moe_status moe_swiglu_backward(const moe_config* cfg, const void* a, const void* b,
                                const void* dh, int32_t rows, void* da, void* db, void* stream);
 
-/* Bytes of device workspace moe_expert_backward_input needs for `cfg` (its own: it
- * holds transposed copies of all expert weights, as large as the weights).  Host-only;
+/* Bytes of device workspace moe_expert_backward_input and moe_expert_backward need for
+ * `cfg` (row-sized buffers and the weight gradients' packed operands).  Host-only;
  * 0 when cfg is invalid or not supported by the backward (BF16 activations and weights
  * only, and T*(K+Ns)*hidden*2 and T*(K+Ns)*inter*4 bytes each below 2^31 - 2^20). */
 size_t moe_backward_workspace_bytes(const moe_config* cfg);
@@ -257,17 +257,14 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  * in bf16; fp32 accumulation; dx rounded once.  x [T, hidden], dy_rows [T*K + T*Ns,
  * hidden] (e.g. from moe_combine_backward), dx [T, hidden] out, all BF16;
  * expert_offsets, row_token, pair_row as written by moe_permute; weights as for
- * moe_grouped_ffn (BF16, no scales).  Workspace: moe_backward_workspace_bytes(cfg),
- * 256-byte aligned; it receives transposed copies of the weights (about half the
- * call's time at the prefill shape).  reuse_transposed != 0 skips making them: the
- * caller asserts that this workspace already holds them from an earlier call with the
- * same weight contents and config (e.g. further micro-batches before the weights
- * change); otherwise pass 0.  The weight gradients: moe_expert_backward. */
+ * moe_grouped_ffn (BF16, no scales), read as stored (no transposed copies).
+ * Workspace: moe_backward_workspace_bytes(cfg), 256-byte aligned.  The weight
+ * gradients: moe_expert_backward. */
 moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* expert_offsets, const int32_t* row_token,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
-                                     const void* dy_rows, void* dx, int32_t reuse_transposed,
-                                     void* ws, size_t ws_bytes, void* stream);
+                                     const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* Backward of the router logits z = x w_router^T ("深度解读报告" section 2.2, the
  * affinity logits, differentiated) for a logit gradient grad_logits [T, E] fp32 (the
@@ -289,15 +286,13 @@ moe_status moe_router_backward(const moe_config* cfg, const void* x, const void*
  *   dw_up[e]   = sum_r db_r^T u_r             [E+Ns, inter, hidden] fp32 out
  * with a, b recomputed and (da, db) as in moe_swiglu_backward, summed in fp32 in row
  * order (deterministic); experts without rows get zeros.  At least one of dx and the
- * weight gradients must be requested.  Other arguments, the workspace and
- * reuse_transposed as for moe_expert_backward_input (the transposed W_down is used
- * either way). */
+ * weight gradients must be requested.  Other arguments and the workspace as for
+ * moe_expert_backward_input. */
 moe_status moe_expert_backward(const moe_config* cfg, const void* x,
                                const int32_t* expert_offsets, const int32_t* row_token,
                                const int32_t* pair_row, const moe_expert_weights* weights,
                                const void* dy_rows, void* dx, float* dw_gate, float* dw_up,
-                               float* dw_down, int32_t reuse_transposed, void* ws,
-                               size_t ws_bytes, void* stream);
+                               float* dw_down, void* ws, size_t ws_bytes, void* stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and moe_combine
  * enqueued back to back on `stream` with no host synchronisation in between.

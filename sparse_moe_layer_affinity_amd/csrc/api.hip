@@ -63,8 +63,6 @@ BackwardWorkspace backward_workspace_layout(const moe_config& c, void* base) {
   w.sched_n = static_cast<int32_t*>(take(4));
   w.sched = static_cast<int4*>(take(size_t(expert_row_blocks_upper(c, kExpertBM)) * 16));
   w.ones = static_cast<float*>(take(T * K * 4));
-  w.wt_down = static_cast<uint16_t*>(take(G * I * H * 2));
-  w.wt_gu = static_cast<uint16_t*>(take(G * H * 2 * I * 2));
   w.ab = static_cast<uint16_t*>(take(rows * 2 * I * 2));
   w.dh = static_cast<uint16_t*>(take(rows * I * 2));
   w.dab = static_cast<uint16_t*>(take(rows * 2 * I * 2));
@@ -244,8 +242,7 @@ moe_status moe_expert_backward(const moe_config* cfg, const void* x,
                                const int32_t* expert_offsets, const int32_t* row_token,
                                const int32_t* pair_row, const moe_expert_weights* weights,
                                const void* dy_rows, void* dx, float* dw_gate, float* dw_up,
-                               float* dw_down, int32_t reuse_transposed, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               float* dw_down, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate_backward(cfg));
   if (!x || !expert_offsets || !row_token || !pair_row || !dy_rows)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -256,19 +253,18 @@ moe_status moe_expert_backward(const moe_config* cfg, const void* x,
   if (ws_bytes < backward_workspace_layout(*cfg, nullptr).bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const BackwardWorkspace w = backward_workspace_layout(*cfg, ws);
   return from_hip(launch_expert_backward(*cfg, x, expert_offsets, row_token, pair_row, *weights,
-                                         dy_rows, dx, dw_gate, dw_up, dw_down,
-                                         reuse_transposed != 0, w,
+                                         dy_rows, dx, dw_gate, dw_up, dw_down, w,
                                          static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const int32_t* expert_offsets, const int32_t* row_token,
                                      const int32_t* pair_row, const moe_expert_weights* weights,
-                                     const void* dy_rows, void* dx, int32_t reuse_transposed,
-                                     void* ws, size_t ws_bytes, void* stream) {
+                                     const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
+                                     void* stream) {
   if (!dx) return MOE_ERR_INVALID_ARGUMENT;
   return moe_expert_backward(cfg, x, expert_offsets, row_token, pair_row, weights, dy_rows, dx,
-                             nullptr, nullptr, nullptr, reuse_transposed, ws, ws_bytes, stream);
+                             nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,

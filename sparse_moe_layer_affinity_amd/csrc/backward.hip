@@ -16,10 +16,10 @@
 // over each wave by a fixed butterfly and over the four waves in order (fixed order,
 // deterministic).  gate_backward: one wave per token.  swiglu_backward: elementwise
 // over the [rows, inter] pre-activations of the SwiGLU experts.  The experts' input
-// gradient reuses the forward's expert GEMM (plain mode) on per-expert transposed
-// weight copies (transpose_experts); their weight gradients run on the matrix cores
-// (wgrad.hip, each expert's row range read on the device); the router logits' backward
-// runs in router_wgrad (fp32 logit gradient, VALU).
+// gradient runs the forward's expert GEMM in its [K][N] weight mode (the weights read
+// as they are stored, fragments transposed on their way out of LDS); their weight
+// gradients run on the matrix cores (wgrad.hip, each expert's row range read on the
+// device); the router logits' backward runs in router_wgrad (fp32 logit gradient, VALU).
 #include "gemm_common.h"
 
 namespace moe {
@@ -222,54 +222,9 @@ hipError_t launch_swiglu_backward(const moe_config& c, const void* a, const void
                        SwigluArgs{a, b, dh, da, db, I, I, I, I, I, rows, c.inter}, st);
 }
 
-// Per-expert transpose of bf16 matrices through LDS: dst[g][c][col0 + r] = src[g][r][c]
-// for src [G][R][C] (R, C multiples of 8); dst rows hold dst_ld elements.  64 x 64
-// tiles: 16-byte vector reads along source rows, 16-byte vector writes along
-// destination rows (each gathered from 8 LDS rows); the LDS pitch of 72 elements keeps
-// rows 16-byte aligned.
-__global__ __launch_bounds__(256) void transpose_experts(const uint16_t* __restrict__ src,
-                                                         uint16_t* __restrict__ dst, int R, int C,
-                                                         long long dst_ld, int col0,
-                                                         long long dst_stride) {
-  constexpr int kPitch = 72;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
-  const int g = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* s = src + size_t(g) * R * C;
-  uint16_t* d = dst + size_t(g) * dst_stride;
-  const int lane8 = (threadIdx.x % 8) * 8, row = threadIdx.x / 8;     // row 0..31
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int i = row + 32 * pass, r = r0 + i, cc = c0 + lane8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < R && cc < C) v = *reinterpret_cast<const uint4*>(s + size_t(r) * C + cc);
-    *reinterpret_cast<uint4*>(&tile[i * kPitch + lane8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int j = row + 32 * pass, cc = c0 + j, r = r0 + lane8;    // source column j
-    uint16_t e[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) e[q] = tile[(lane8 + q) * kPitch + j];
-    if (cc < C && r < R)
-      *reinterpret_cast<uint4*>(d + size_t(cc) * dst_ld + col0 + r) =
-          make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
-  }
-}
-
 __global__ __launch_bounds__(256) void fill_f32(float* __restrict__ p, int n, float v) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
-}
-
-static hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int G, int R, int C,
-                                   long long dst_ld, int col0, long long dst_stride,
-                                   hipStream_t st) {
-  hipLaunchKernelGGL(transpose_experts, dim3(ceil_div(C, 64), ceil_div(R, 64), G), dim3(256), 0,
-                     st, src, dst, R, C, dst_ld, col0, dst_stride);
-  return hipGetLastError();
 }
 
 // The router logits' backward on the VALU: one fp32 output tile (128 x 128, 8 x 8 per
@@ -410,34 +365,23 @@ hipError_t launch_router_backward(const moe_config& c, const void* x, const void
 
 // Input gradient of the grouped SwiGLU experts (bf16), on the forward's row layout:
 //   a | b   = gathered x rows times W_gate^T | W_up^T      (recomputed, plain GEMMs)
-//   dh      = dy_rows times W_down                         (B = W_down^T per expert)
+//   dh      = dy_rows times W_down                         (W_down [H][I] read as [K][N])
 //   da | db = SwiGLU backward of (a, b, dh)
-//   dX      = [da | db] times [W_gate ; W_up]              (B = [W_gate^T | W_up^T])
+//   dX      = [da | db] times [W_gate ; W_up]              (both [I][H], stacked along K)
 //   dx      = sum of dX over each token's rows              (the combine, unit gates)
 hipError_t launch_expert_backward(const moe_config& c, const void* x, const int32_t* offsets,
                                   const int32_t* row_token, const int32_t* pair_row,
                                   const moe_expert_weights& wt, const void* dy_rows, void* dx,
                                   float* dw_gate, float* dw_up, float* dw_down,
-                                  bool reuse_transposed, const BackwardWorkspace& ws,
-                                  hipStream_t s) {
-  const int T = c.num_tokens, K = c.top_k, Ns = c.num_shared, E = c.num_experts;
-  const int H = c.hidden, I = c.inter, TK = T * K, rows = TK + T * Ns, G = E + Ns;
+                                  const BackwardWorkspace& ws, hipStream_t s) {
+  const int T = c.num_tokens, K = c.top_k, Ns = c.num_shared;
+  const int H = c.hidden, I = c.inter, TK = T * K, rows = TK + T * Ns;
   hipError_t err = launch_build_schedule(c, offsets, kExpertBM, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fill_f32, dim3(ceil_div(TK, 256)), dim3(256), 0, s, ws.ones, TK, 1.0f);
   const auto* wg = static_cast<const uint16_t*>(wt.w_gate);
   const auto* wu = static_cast<const uint16_t*>(wt.w_up);
   const auto* wd = static_cast<const uint16_t*>(wt.w_down);
-  // W_down [G][H][I] -> [G][I][H];  W_gate, W_up [G][I][H] -> [G][H][2I] side by side
-  // (skipped when the workspace already holds them for these weights)
-  if (!reuse_transposed) {
-    if ((err = launch_transpose(wd, ws.wt_down, G, H, I, H, 0, 1LL * I * H, s)) != hipSuccess)
-      return err;
-    if ((err = launch_transpose(wg, ws.wt_gu, G, I, H, 2LL * I, 0, 2LL * H * I, s)) != hipSuccess)
-      return err;
-    if ((err = launch_transpose(wu, ws.wt_gu, G, I, H, 2LL * I, I, 2LL * H * I, s)) != hipSuccess)
-      return err;
-  }
 
   GemmArgs a{};
   a.sched = ws.sched;
@@ -466,14 +410,15 @@ hipError_t launch_expert_backward(const moe_config& c, const void* x, const int3
   d.row_token = nullptr;
   d.gather = 0;
   d.a_rows = rows;
-  d.B0 = ws.wt_down;
+  d.B0 = wd;
   d.b_stride = 1LL * I * H;
   d.C = ws.dh;
   d.ldc = I;
   d.N = I;
   d.K = H;
+  d.k_split = H;
   d.n_tiles = ceil_div(I, 256);
-  if ((err = launch_grouped_plain_bf16(c, d, s)) != hipSuccess) return err;
+  if ((err = launch_grouped_kn_bf16(c, d, s)) != hipSuccess) return err;
   // da | db
   const long long I2 = 2LL * I;
   err = launch_swiglu(false, SwigluArgs{ws.ab, ws.ab + I, ws.dh, ws.dab, ws.dab + I, I2, I2, I,
@@ -490,14 +435,16 @@ hipError_t launch_expert_backward(const moe_config& c, const void* x, const int3
   // dX = [da | db] [W_gate ; W_up]
   GemmArgs q = d;
   q.A = ws.dab;
-  q.B0 = ws.wt_gu;
-  q.b_stride = 2LL * H * I;
+  q.B0 = wg;
+  q.B1 = wu;
+  q.b_stride = 1LL * I * H;
   q.C = ws.dx_rows;
   q.ldc = H;
   q.N = H;
   q.K = 2 * I;
+  q.k_split = I;
   q.n_tiles = ceil_div(H, 256);
-  if ((err = launch_grouped_plain_bf16(c, q, s)) != hipSuccess) return err;
+  if ((err = launch_grouped_kn_bf16(c, q, s)) != hipSuccess) return err;
   // dx: every row of the token with weight one
   return launch_combine(c, ws.dx_rows, pair_row, ws.ones, nullptr, dx, s);
 }

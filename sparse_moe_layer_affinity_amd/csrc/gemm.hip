@@ -93,6 +93,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   constexpr int BN_OUT = MODE == kGatedBf16 ? BN / 2 : BN;
   // bf16 outputs: the MFMAs compute the transposed tile (see the epilogue)
   constexpr bool kTr = MODE != kPlainF32;
+  // weights stored [K][N] (a plain GEMM on the weights as they are, e.g. the input
+  // gradient's dY W_down): a B stage is 64 weight rows (K) x 256 columns (N) of 512
+  // bytes, 16-byte chunk c of row r in slot c ^ 4 (r & 7); fragments are read across
+  // rows with ds_read_b64_tr_b16 (see read_b)
+  constexpr bool kKN = MODE == kPlainKN;
   constexpr int NDA = BM / 32, NDB = BN / 32; // DMA instructions per wave per stage
   __shared__ __attribute__((aligned(1024))) uint4 lds[(2 * ASTAGE + 2 * BSTAGE) / 16];
 
@@ -146,6 +151,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   const int kst0 = blockIdx.y * (a.k_chunk / BK);      // first stage
   const int K = a.k_chunk ? min(a.k_chunk, a.K - blockIdx.y * a.k_chunk) : a.K;
   const uint32_t row_bytes = uint32_t(a.K) * 2u;
+  const uint32_t row_bytes_b = uint32_t(a.N) * 2u;      // [K][N] weights: one K row
 
   // ---- this wave's share of every stage: A rows 80 w.., B rows 64 w.. ---------------
   // B: the tile's first weight row (gated: of the gate and of the up half) is in the
@@ -154,9 +160,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   const uint16_t* const bsel = MODE == kGatedBf16 && w >= 2 ? a.B1 : a.B0;
   auto rsrc_b_of = [&](int g_, int nt_) __attribute__((always_inline)) {
     const int nb = nt_ * BN_OUT;
+    if constexpr (kKN)     // the tile's first column; K rows up to the split from B0
+      return make_rsrc(a.B0 + size_t(g_) * a.b_stride + nb, (uint32_t(a.k_split) * uint32_t(a.N) - nb) * 2u);
     return make_rsrc(bsel + size_t(g_) * a.b_stride + size_t(nb) * a.K, uint32_t(a.N - nb) * row_bytes);
   };
+  // [K][N] weights stacked along K: rows from k_split on come from B1
+  auto rsrc_b1_of = [&](int g_, int nt_) __attribute__((always_inline)) {
+    const int nb = nt_ * BN_OUT;
+    const uint16_t* b1 = a.B1 ? a.B1 : a.B0;
+    const uint32_t n1 = a.K > a.k_split ? (uint32_t(a.K - a.k_split) * uint32_t(a.N) - nb) * 2u : 0u;
+    return make_rsrc(b1 + size_t(g_) * a.b_stride + nb, n1);
+  };
   __amdgpu_buffer_rsrc_t rsrc_b = rsrc_b_of(g, nt);
+  __amdgpu_buffer_rsrc_t rsrc_b1 = rsrc_b;
+  if constexpr (kKN) rsrc_b1 = rsrc_b1_of(g, nt);
   uint32_t voff_a[NDA], voff_b[NDB];
   // A row offsets of a tile: routed rows (below TK) gather their token through
   // row_token; a tile of shared-expert rows maps to consecutive tokens
@@ -178,6 +195,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   set_voff_a(m0, mvalid);
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
+    if constexpr (kKN) {
+      // K rows 16 w + 2 j + (l >> 5) of the stage, slot l & 31 of the row's 32
+      const int kr = 16 * w + 2 * j + (l >> 5);
+      const uint32_t chunk = uint32_t((l & 31) ^ (4 * (kr & 7))) * 16u;
+      voff_b[j] = uint32_t(kr) * row_bytes_b + chunk;
+      continue;
+    }
     const int rw = 8 * j + (l >> 3);
     const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
     // gated: B rows 0..127 are gate rows, 128..255 the matching up rows
@@ -195,6 +219,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   };
   auto dma_b = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
     constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
+    if constexpr (kKN) {
+      const int kr0 = 64 * ks;                            // first K row of the stage
+      const bool hi = kr0 >= a.k_split;
+      dma16(hi ? rsrc_b1 : rsrc_b, voff_b[j], uint32_t(hi ? kr0 - a.k_split : kr0) * row_bytes_b,
+            wave_b + uint32_t(par * BSTAGE + j * 1024));
+      return;
+    }
     dma16(rsrc_b, voff_b[j], uint32_t(ks + kst0) * ROWB, wave_b + uint32_t(par * BSTAGE + j * 1024));
   };
 
@@ -204,9 +235,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   // then die with the K loop instead of staying live (and spilling) through the
   // epilogue of a persistent workgroup.
   uint32_t abase[4], bbase[4], xbase[4];
+  // [K][N] weights: per lane, the byte of its first 8-byte transposed read in block j
+  // (rows 8 (ll >> 5) + (ll & 15) / 4 of a 16-row K step) and of its second (4 rows on)
+  uint32_t kn1[NJ], kn2[NJ];
   auto set_frag_bases = [&]() __attribute__((always_inline)) {
     int ll;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ll));
+    if constexpr (kKN) {
+      const int L = ll & 15, khalf = ll >> 5, nhalf = (ll >> 4) & 1;
+      const int x1 = L >> 2, x2 = 4 + (L >> 2);          // row & 7 of the two reads
+      const uint32_t row1 = uint32_t(8 * khalf + (L >> 2)) * 512u;
+      const uint32_t inner = uint32_t(2 * nhalf + ((L & 3) >> 1)) * 16u + uint32_t(L & 1) * 8u;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        kn1[j] = row1 + uint32_t((4 * wn + j) ^ x1) * 64u + inner;
+        kn2[j] = row1 + 2048u + uint32_t((4 * wn + j) ^ x2) * 64u + inner;
+      }
+    }
     const int lane_row = ll & 31;
     const int b_row0 = (MODE == kGatedBf16 ? wn * (WTN / 2) : wn * WTN) + lane_row;
     const int a_row = wm * WTM + lane_row;
@@ -264,6 +309,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     auto read_b = [&](auto par_tag, auto s_tag, auto j_tag) __attribute__((always_inline)) {
       constexpr int par = decltype(par_tag)::value, s4 = decltype(s_tag)::value;
       constexpr int j = decltype(j_tag)::value;
+      if constexpr (kKN) {
+        // eight K values of one column (n = lane & 31) from two transposed reads: within
+        // a group of 16 lanes, value q of lane i comes from element i & 3 of the 8 bytes
+        // lane 4 q + i / 4 addresses
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const uint32_t off = uint32_t(par * BSTAGE + s4 * 16 * 512);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(reinterpret_cast<char*>(lds) + kn1[j] + off));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(reinterpret_cast<char*>(lds) + kn2[j] + off));
+        fb[s4][j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        return;
+      }
       fb[s4][j] = lds_read(bbase[s4] + uint32_t(par * BSTAGE + b_blk(j) * ROWB));
     };
     auto read_a = [&](auto par_tag, auto s_tag, auto i_tag) __attribute__((always_inline)) {
@@ -422,6 +481,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
           m02 = __builtin_amdgcn_readfirstlane(next_e[1]);
           mv2 = __builtin_amdgcn_readfirstlane(next_e[2]);
           rsrc_b = rsrc_b_of(g2, nt2);
+          if constexpr (kKN) rsrc_b1 = rsrc_b1_of(g2, nt2);
           static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(0, P0{}, j); });
           static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(1, P1{}, j); });
         }
@@ -826,6 +886,23 @@ hipError_t launch_grouped_plain_bf16(const moe_config& c, const GemmArgs& a, hip
   const dim3 grid(unsigned(nwg * kXcds));
   if (a.K == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((grouped_gemm_dma<kPlainBf16, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// The same product on weights stored [K][N] per expert, read as they are: B0 holds K
+// rows 0 .. k_split - 1, B1 (if K > k_split) rows k_split .. K - 1, b_stride elements
+// per expert in each.  N a multiple of 8 (a tile's columns past N load whatever follows
+// in the row, or zeros past the buffer; they feed only output columns that are not
+// stored), K a multiple of 128, k_split of 64.
+hipError_t launch_grouped_kn_bf16(const moe_config& c, const GemmArgs& a, hipStream_t s) {
+  if (a.N % 8 || a.K % 128 || a.k_split % 64 || a.k_split <= 0 || a.k_split > a.K ||
+      (a.k_split < a.K && !a.B1))
+    return hipErrorInvalidValue;
+  const int rounds = ceil_div(expert_row_blocks_upper(c, kExpertBM), kXcds);
+  const int nwg = std::min(resident_workgroups() / kXcds, rounds * a.n_tiles);
+  const dim3 grid(unsigned(nwg * kXcds));
+  if (a.K == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainKN, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_gemm_dma<kPlainKN, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

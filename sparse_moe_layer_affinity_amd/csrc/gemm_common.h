@@ -24,11 +24,15 @@ struct GemmArgs {
   int a_rows;                // rows of A (bounds of the activation buffer)
   int k_chunk;               // split-K: K elements per blockIdx.y (router only)
   long long c_split_stride;  // split-K: elements between the partial outputs
+  int k_split;               // [K][N] weights: K rows taken from B0 (the rest from B1)
 };
 
 hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int4* sched,
                                  int32_t* sched_n, hipStream_t s);
 hipError_t launch_grouped_plain_bf16(const moe_config& c, const GemmArgs& a, hipStream_t s);
+// The same on weights stored [K][N] (B0: K rows 0..k_split-1, B1 the rest; b_stride
+// elements per expert in each), no transposed copy needed.
+hipError_t launch_grouped_kn_bf16(const moe_config& c, const GemmArgs& a, hipStream_t s);
 
 // Arguments of the FP8 expert GEMMs (e4m3 operands, 128x128 / 1x128 block scales).
 struct Fp8Args {
@@ -54,7 +58,7 @@ struct Fp8Args {
   int scale_rows;            // rows of a_scales (the grouped rows)
 };
 
-enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2 };
+enum { kPlainBf16 = 0, kGatedBf16 = 1, kPlainF32 = 2, kPlainKN = 3 };
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

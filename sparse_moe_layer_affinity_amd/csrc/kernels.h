@@ -39,14 +39,12 @@ struct WgradPackWorkspace {
 };
 long long wgrad_packed_rows(const moe_config& c);
 
-// Scratch of the expert backward (its own workspace: the transposed weights alone are
-// as large as the weights)
+// Scratch of the expert backward (its own workspace: row-sized buffers and the packed
+// operands of the weight gradients)
 struct BackwardWorkspace {
   int32_t* sched_n;    // [1] row blocks of the grouped GEMMs
   int4* sched;         // row blocks {group, first row, rows}, largest first
   float* ones;         // [T*K] unit gates for the final row sum
-  uint16_t* wt_down;   // [E+Ns, inter, hidden]  W_down^T per expert
-  uint16_t* wt_gu;     // [E+Ns, hidden, 2*inter] W_gate^T | W_up^T per expert
   uint16_t* ab;        // [rows, 2*inter] recomputed gate | up pre-activations
   uint16_t* dh;        // [rows, inter] gradient of h
   uint16_t* dab;       // [rows, 2*inter] their gradients
@@ -117,8 +115,7 @@ hipError_t launch_expert_backward(const moe_config& c, const void* x, const int3
                                   const int32_t* row_token, const int32_t* pair_row,
                                   const moe_expert_weights& wt, const void* dy_rows, void* dx,
                                   float* dw_gate, float* dw_up, float* dw_down,
-                                  bool reuse_transposed, const BackwardWorkspace& ws,
-                                  hipStream_t s);
+                                  const BackwardWorkspace& ws, hipStream_t s);
 hipError_t launch_expert_wgrad_mfma(const moe_config& c, const void* x, const int32_t* offsets,
                                     const int32_t* row_token, const void* dy_rows,
                                     const uint16_t* ab, const uint16_t* dab, float* dw_gate,

@@ -151,16 +151,17 @@ def test_expert_backward_input(name, over):
     weights = {k: d[k] for k in ("w_gate", "w_up", "w_down")}
     moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
                                   dy_rows.cuda(), dx, ws)
-    # a second micro-batch on the same weights reuses the transposed copies
+    # a second micro-batch through the same workspace equals one through a fresh workspace
+    # full of other bytes: nothing of an earlier call leaks into the next
     dy2 = workloads.make_dense((cfg.rows, H), "bf16", seed=T + 1, name="dy_rows")
     dx2 = torch.empty_like(dx)
     moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
-                                  dy2.cuda(), dx2, ws, reuse_transposed=True)
+                                  dy2.cuda(), dx2, ws)
     dx3 = torch.empty_like(dx)
     moe.moe_expert_backward_input(c, d["x"], i32(off), i32(row_token), i32(pair_row), weights,
-                                  dy2.cuda(), dx3, torch.empty_like(ws))
+                                  dy2.cuda(), dx3, torch.full_like(ws, 0x7f))
     torch.cuda.synchronize()
-    assert torch.equal(dx2, dx3), "reusing the transposed weights changed the result"
+    assert torch.equal(dx2, dx3), "the workspace's earlier contents changed the result"
     toks = workloads.sample_rows(T, 48, seed=4).numpy()
     n = len(toks)
     # the chosen tokens' rows, re-indexed as a problem of n tokens (routed, then shared)
@@ -206,7 +207,7 @@ def test_expert_backward_weights(name, over, n_check):
     dx_only = torch.empty_like(dx)
     args = (c, d["x"], i32(off), i32(row_token), i32(pair_row), weights, dy_rows.cuda())
     moe.moe_expert_backward(*args, dx, dwg, dwu, dwd, ws)
-    moe.moe_expert_backward_input(*args, dx_only, ws, reuse_transposed=True)
+    moe.moe_expert_backward_input(*args, dx_only, ws)
     torch.cuda.synchronize()
     assert torch.equal(dx, dx_only)
     expert_of_row = np.concatenate([np.repeat(np.arange(E), np.diff(off)),
