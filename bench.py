@@ -149,7 +149,8 @@ def cpu_baseline(cfg, d, n_tokens: int, n_tokens_1t: int = 8):
 def calibration_leg(stream):
     """Measured ceilings of this device (calibration kernels of libmoe_calib.so, timed
     between HIP events on the bench stream after the layer steps): a plain read stream
-    over 4 GiB (16-byte vectors, eight in flight per lane) and back-to-back MFMAs
+    over 4 GiB (16-byte vectors, eight in flight per lane), a plain write stream over the
+    same 4 GiB (16-byte vectors) and back-to-back MFMAs
     (eight accumulator chains per wave, four waves per CU, sustained about 20 ms) in
     bf16 (32x32x16) and e4m3 (32x32x64).  Each is run twice; the second run counts."""
     import ctypes
@@ -157,6 +158,8 @@ def calibration_leg(stream):
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_layer_affinity_amd", "libmoe_calib.so"))
     lib.moe_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_int, ctypes.c_void_p]
+    lib.moe_calib_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p]
     lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                    ctypes.c_void_p]
     s = stream.cuda_stream
@@ -178,8 +181,10 @@ def calibration_leg(stream):
     out = torch.empty(blocks * 256 * 4, dtype=torch.int32, device="cuda")
     ms = timed(lambda: lib.moe_calib_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, s))
     read_gbps = nbytes / (ms * 1e-3) / 1e9
+    ms = timed(lambda: lib.moe_calib_write(buf.data_ptr(), nbytes, blocks, s))
+    write_gbps = nbytes / (ms * 1e-3) / 1e9
     del buf
-    res = {"hbm_read_GBps": round(read_gbps, 1)}
+    res = {"hbm_read_GBps": round(read_gbps, 1), "hbm_write_GBps": round(write_gbps, 1)}
     iters = 20000
     outf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     for name, fp8, flop in (("mfma_bf16_TFLOPs", 0, 32768), ("mfma_e4m3_TFLOPs", 1, 131072)):
@@ -262,8 +267,11 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
     if cfg.act != "f32":
         dxr = torch.empty((T, H), device="cuda")
         dwr = torch.empty((E, H), device="cuda")
-        us_rb = timed(lambda: moe.moe_router_backward(c, d["x"], d["w_router"], grad, dxr, dwr))
-        del dxr, dwr
+        rws = torch.empty(moe.moe_router_backward_workspace_bytes(c), dtype=torch.uint8,
+                          device="cuda")
+        us_rb = timed(lambda: moe.moe_router_backward(c, d["x"], d["w_router"], grad, dxr, dwr,
+                                                      rws))
+        del dxr, dwr, rws
     # SwiGLU backward over every grouped row: seeded stand-ins for the pre-activations
     # and the gradient of h (the forward does not keep the pre-activations)
     g = torch.Generator(device="cuda")

@@ -266,16 +266,26 @@ moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                                      const void* dy_rows, void* dx, void* ws, size_t ws_bytes,
                                      void* stream);
 
+/* Bytes of device workspace moe_router_backward needs for `cfg` (its own).  Host-only;
+ * 0 when cfg is invalid or not supported (BF16 activations, hidden a multiple of 8, and
+ * hidden * T and E * T each below about 2^30, with T and E rounded up as below). */
+size_t moe_router_backward_workspace_bytes(const moe_config* cfg);
+
 /* Backward of the router logits z = x w_router^T ("深度解读报告" section 2.2, the
  * affinity logits, differentiated) for a logit gradient grad_logits [T, E] fp32 (the
  * sum of moe_gate_backward's and moe_balance_loss's):
  *   dx[t, c]        = sum_e grad_logits[t, e] * w_router[e, c]     [T, hidden] fp32 out
  *   dw_router[e, c] = sum_t grad_logits[t, e] * x[t, c]            [E, hidden] fp32 out
- * fp32 sums in a fixed order; either output may be NULL, not both.  x [T, hidden] and
- * w_router [E, hidden] BF16 (act_dtype BF16 only; E a multiple of 8). */
+ * On the matrix cores: grad_logits is split into bf16 hi = bf16(g) and lo = bf16(g - hi)
+ * (g = hi + lo within 2^-17 |g|), each multiplied exactly by the bf16 operands, fp32
+ * accumulation; dw_router sums split-K partials over token ranges in a fixed order
+ * (deterministic).  Either output may be NULL, not both.  x [T, hidden] and w_router
+ * [E, hidden] BF16.  Workspace: moe_router_backward_workspace_bytes(cfg), 256-byte
+ * aligned (about 2 (T + E) hidden + 16 E T + 32 E hidden bytes with E rounded up to 64
+ * and T to 128). */
 moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
-                               const float* grad_logits, float* dx, float* dw_router,
-                               void* stream);
+                               const float* grad_logits, float* dx, float* dw_router, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* Input and weight gradients of the grouped SwiGLU experts together
  * ("深度解读报告" section 2.2, differentiated): dx as in moe_expert_backward_input

@@ -9,6 +9,7 @@ from .binding import (MoeConfig, MoeError, MoeExpertWeights, lib, make_config,  
                       moe_combine_backward, moe_gate_backward, moe_grouped_ffn, moe_router_scores,
                       moe_swiglu_backward, moe_backward_workspace_bytes,
                       moe_expert_backward_input, moe_expert_backward, moe_router_backward,
+                      moe_router_backward_workspace_bytes,
                       moe_layer_forward, moe_layer_forward_noalloc, moe_permute, moe_route,
                       moe_status_string,
                       moe_workspace_bytes, DTYPE_CODES)

@@ -64,7 +64,8 @@ _SIGS = {
     "moe_gate_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.c_int32, _P]),
     "moe_swiglu_backward": (ctypes.c_int, [_CFG, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_backward_workspace_bytes": (ctypes.c_size_t, [_CFG]),
-    "moe_router_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
+    "moe_router_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_router_backward_workspace_bytes": (ctypes.c_size_t, [_CFG]),
     "moe_expert_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, ctypes.POINTER(MoeExpertWeights),
                                            _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_backward_input": (ctypes.c_int, [_CFG, _P, _P, _P, _P,
@@ -271,11 +272,17 @@ def moe_expert_backward(cfg, x, expert_offsets, row_token, pair_row, weights: di
         _stream(stream)))
 
 
-def moe_router_backward(cfg, x, w_router, grad_logits, dx, dw_router, stream=None):
+def moe_router_backward_workspace_bytes(cfg: MoeConfig) -> int:
+    return int(lib().moe_router_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def moe_router_backward(cfg, x, w_router, grad_logits, dx, dw_router, ws, ws_bytes=None,
+                        stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("moe_router_backward", lib().moe_router_backward(
         ctypes.byref(cfg), _dev(x, "x"), _dev(w_router, "w_router"),
         _dev(grad_logits, "grad_logits"), _dev(dx, "dx", True), _dev(dw_router, "dw_router", True),
-        _stream(stream)))
+        _dev(ws, "ws"), ws_bytes, _stream(stream)))
 
 
 def moe_status_string(code: int) -> str:

@@ -267,13 +267,29 @@ moe_status moe_expert_backward_input(const moe_config* cfg, const void* x,
                              nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
+static moe_status validate_router_backward(const moe_config* c) {
+  MOE_TRY(validate(c));
+  if (c->act_dtype != MOE_BF16 || c->hidden % 8) return MOE_ERR_UNSUPPORTED;
+  const RouterBwdWorkspace w = router_bwd_workspace_layout(*c, nullptr);
+  const long long lim = (1LL << 31) - (1LL << 20);
+  if (2LL * c->hidden * w.Tp > lim || 4LL * w.Ep * w.Tp > lim) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_router_backward_workspace_bytes(const moe_config* cfg) {
+  if (validate_router_backward(cfg) != MOE_OK) return 0;
+  return router_bwd_workspace_layout(*cfg, nullptr).bytes;
+}
+
 moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
-                               const float* grad_logits, float* dx, float* dw_router,
-                               void* stream) {
-  MOE_TRY(validate(cfg));
+                               const float* grad_logits, float* dx, float* dw_router, void* ws,
+                               size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_router_backward(cfg));
   if (!x || !w_router || !grad_logits || (!dx && !dw_router)) return MOE_ERR_INVALID_ARGUMENT;
-  if (cfg->act_dtype != MOE_BF16 || cfg->num_experts % 8) return MOE_ERR_UNSUPPORTED;
-  return from_hip(launch_router_backward(*cfg, x, w_router, grad_logits, dx, dw_router,
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < router_bwd_workspace_layout(*cfg, nullptr).bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const RouterBwdWorkspace w = router_bwd_workspace_layout(*cfg, ws);
+  return from_hip(launch_router_backward(*cfg, x, w_router, grad_logits, dx, dw_router, w,
                                          static_cast<hipStream_t>(stream)));
 }
 

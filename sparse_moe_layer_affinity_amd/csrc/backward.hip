@@ -19,7 +19,11 @@
 // gradient runs the forward's expert GEMM in its [K][N] weight mode (the weights read
 // as they are stored, fragments transposed on their way out of LDS); their weight
 // gradients run on the matrix cores (wgrad.hip, each expert's row range read on the
-// device); the router logits' backward runs in router_wgrad (fp32 logit gradient, VALU).
+// device).  The router logits' backward runs on the matrix cores too: the fp32 logit
+// gradient is split into two bf16 parts (hi + lo, within 2^-17 of it) stacked along the
+// contraction, so bf16 MFMAs with fp32 accumulation keep about fp32 accuracy.
+#include <algorithm>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -227,138 +231,170 @@ __global__ __launch_bounds__(256) void fill_f32(float* __restrict__ p, int n, fl
   if (i < n) p[i] = v;
 }
 
-// The router logits' backward on the VALU: one fp32 output tile (128 x 128, 8 x 8 per
-// thread; 64 x 64 for small outputs) per workgroup, summed over the rows r of one row
-// group in row order (fp32 FMAs):
-//   C[m][n] = sum_r A(r, m) * B[r][n]
-// A(r, m) = Af[r][m] (row-major fp32) or Af[m][r] (stored transposed); B bf16 rows.
-enum { kWgAf32 = 1, kWgAf32T = 2 };
-struct WgradArgs {
-  const float* Af;
-  long long lda;
-  const uint16_t* B;
-  long long ldb;
-  int rows, M, N;
-  float* C;                                 // [M][N]
-};
+// bf16 bits of v, round to nearest even
+__device__ __forceinline__ uint32_t bf16_rne(float v) { return pack_bf16x2(v, 0.0f) & 0xffffu; }
 
-__device__ __forceinline__ void bf16x4_to_f32(uint2 raw, float f[4]) {
-  f[0] = bf16_bits_to_f32(raw.x & 0xffffu);
-  f[1] = bf16_bits_to_f32(raw.x >> 16);
-  f[2] = bf16_bits_to_f32(raw.y & 0xffffu);
-  f[3] = bf16_bits_to_f32(raw.y >> 16);
-}
-
-template <int AMODE, int kT>
-__global__ __launch_bounds__(256) void router_wgrad(WgradArgs p) {
-  constexpr int kU = kT / 16, kPitch = kT + 4;        // kU x kU outputs per thread
-  __shared__ __attribute__((aligned(16))) float As[16][kPitch];
-  __shared__ __attribute__((aligned(16))) float Bs[16][kPitch];
-  const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  const int lr = tid / 16, lc = (tid % 16) * kU;     // loader: row lr, kU columns from lc
-  float acc[kU][kU];
-#pragma unroll
-  for (int i = 0; i < kU; ++i)
-#pragma unroll
-    for (int j = 0; j < kU; ++j) acc[i][j] = 0.0f;
-  for (int rb = 0; rb < p.rows; rb += 16) {
-    const int r = rb + lr;
-    float av[kU], bv[kU];
-#pragma unroll
-    for (int i = 0; i < kU; ++i) av[i] = bv[i] = 0.0f;
-    // N, and M for the row-major A, are multiples of 8: a group of kU elements is wholly
-    // inside or outside; the transposed A (M = tokens) is guarded per row
-    if (r < p.rows && m0 + lc < p.M) {
-      if (AMODE == kWgAf32) {
-#pragma unroll
-        for (int q = 0; q < kU / 4; ++q) {
-          const float4 f =
-              *reinterpret_cast<const float4*>(p.Af + size_t(r) * p.lda + m0 + lc + 4 * q);
-          av[4 * q] = f.x; av[4 * q + 1] = f.y; av[4 * q + 2] = f.z; av[4 * q + 3] = f.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kU; ++i)
-          av[i] = m0 + lc + i < p.M ? p.Af[size_t(m0 + lc + i) * p.lda + r] : 0.0f;
-      }
-    }
-    if (r < p.rows && n0 + lc < p.N) {
-      const uint16_t* pb = p.B + size_t(r) * p.ldb + n0 + lc;
-#pragma unroll
-      for (int q = 0; q < kU / 4; ++q)
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(pb + 4 * q), bv + 4 * q);
-    }
-    __syncthreads();                        // the previous chunk's reads are done
-#pragma unroll
-    for (int q = 0; q < kU / 4; ++q) {
-      *reinterpret_cast<float4*>(&As[lr][lc + 4 * q]) =
-          make_float4(av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]);
-      *reinterpret_cast<float4*>(&Bs[lr][lc + 4 * q]) =
-          make_float4(bv[4 * q], bv[4 * q + 1], bv[4 * q + 2], bv[4 * q + 3]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float a[kU], b[kU];
-#pragma unroll
-      for (int q = 0; q < kU / 4; ++q) {
-        const float4 fa = *reinterpret_cast<const float4*>(&As[k][ty * kU + 4 * q]);
-        const float4 fb = *reinterpret_cast<const float4*>(&Bs[k][tx * kU + 4 * q]);
-        a[4 * q] = fa.x; a[4 * q + 1] = fa.y; a[4 * q + 2] = fa.z; a[4 * q + 3] = fa.w;
-        b[4 * q] = fb.x; b[4 * q + 1] = fb.y; b[4 * q + 2] = fb.z; b[4 * q + 3] = fb.w;
-      }
-#pragma unroll
-      for (int i = 0; i < kU; ++i)
-#pragma unroll
-        for (int j = 0; j < kU; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+// The logit gradient dz [T][E] (fp32) as hi = bf16(dz) and lo = bf16(dz - hi), so that
+// dz = hi + lo within 2^-17 |dz|, in both layouts the two products read: dzs [T][2 Ep]
+// (hi in columns 0.., lo from column Ep) and dzt [2 Ep][Tp] (hi rows, then lo rows),
+// zeros in the padding (experts E..Ep-1, tokens T..Tp-1).  64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void router_dz_split(const float* __restrict__ dz, int T, int E,
+                                                       int Ep, int Tp, uint16_t* __restrict__ dzs,
+                                                       uint16_t* __restrict__ dzt) {
+  __shared__ uint32_t tile[64][65];          // hi | lo << 16, [token][expert]
+  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int t = t0 + i, e = e0 + tx;
+    const float v = t < T && e < E ? dz[size_t(t) * E + e] : 0.0f;
+    const uint32_t hi = bf16_rne(v);
+    const uint32_t lo = bf16_rne(v - bf16_bits_to_f32(hi));
+    tile[i][tx] = hi | (lo << 16);
+    if (t < T) {
+      dzs[size_t(t) * 2 * Ep + e] = uint16_t(hi);
+      dzs[size_t(t) * 2 * Ep + Ep + e] = uint16_t(lo);
     }
   }
-  if (n0 + tx * kU >= p.N) return;
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int e = e0 + i, t = t0 + tx;
+    const uint32_t v = tile[tx][i];
+    dzt[size_t(e) * Tp + t] = uint16_t(v & 0xffffu);
+    dzt[size_t(Ep + e) * Tp + t] = uint16_t(v >> 16);
+  }
+}
+
+// dst[c][col0 + r] = src[r][c] for r < R, zero for R <= r < Rp: src [R][C] bf16 (C a
+// multiple of 8), dst rows of ld elements, Rp a multiple of 64.  64 x 64 tiles:
+// 16-byte reads along source rows, 16-byte writes along destination rows (each
+// gathered from 8 LDS rows); the LDS pitch of 72 elements keeps rows 16-byte aligned.
+__global__ __launch_bounds__(256) void transpose_pad_bf16(const uint16_t* __restrict__ src, int R,
+                                                          int C, uint16_t* __restrict__ dst,
+                                                          long long ld, int col0) {
+  constexpr int kPitch = 72;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int lane8 = (threadIdx.x % 8) * 8, row = threadIdx.x / 8;     // row 0..31
 #pragma unroll
-  for (int i = 0; i < kU; ++i)
-    if (m0 + ty * kU + i < p.M) {
-      float4* q = reinterpret_cast<float4*>(p.C + size_t(m0 + ty * kU + i) * p.N + n0 + tx * kU);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = row + 32 * pass, r = r0 + i, cc = c0 + lane8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R && cc < C) v = *reinterpret_cast<const uint4*>(src + size_t(r) * C + cc);
+    *reinterpret_cast<uint4*>(&tile[i * kPitch + lane8]) = v;
+  }
+  __syncthreads();
 #pragma unroll
-      for (int u = 0; u < kU / 4; ++u)
-        q[u] = make_float4(acc[i][4 * u], acc[i][4 * u + 1], acc[i][4 * u + 2], acc[i][4 * u + 3]);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int j = row + 32 * pass, cc = c0 + j;                        // source column j
+    uint16_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = tile[(lane8 + q) * kPitch + j];
+    if (cc < C)
+      *reinterpret_cast<uint4*>(dst + size_t(cc) * ld + col0 + r0 + lane8) =
+          make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+  }
+}
+
+// dw[e][c] = sum over splits s of part[s][e][c], then of part[s][Ep + e][c] (the hi and
+// the lo products), in that fixed order.
+__global__ __launch_bounds__(256) void router_dw_reduce(const float4* __restrict__ part, int S,
+                                                        long long split_stride4,
+                                                        long long lo_off4, long long n4,
+                                                        float4* __restrict__ dw) {
+  const long long i = blockIdx.x * 256LL + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int h = 0; h < 2; ++h)
+    for (int s = 0; s < S; ++s) {
+      const float4 v = part[s * split_stride4 + h * lo_off4 + i];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
+  dw[i] = acc;
 }
 
-template <int AMODE, int TILE = 128>
-static hipError_t launch_router_wgrad(const WgradArgs& p, hipStream_t st) {
-  hipLaunchKernelGGL((router_wgrad<AMODE, TILE>), dim3(ceil_div(p.N, TILE), ceil_div(p.M, TILE)),
-                     dim3(256), 0, st, p);
-  return hipGetLastError();
+RouterBwdWorkspace router_bwd_workspace_layout(const moe_config& c, void* base) {
+  RouterBwdWorkspace w{};
+  const long long T = c.num_tokens, E = c.num_experts, H = c.hidden;
+  w.Ep = int((E + 63) / 64 * 64);
+  w.Tp = int(std::max<long long>(256, (T + 127) / 128 * 128));
+  // split-K of dW over the tokens: every split a multiple of 128 and at least 256 long
+  for (w.S = 4; w.S > 1; --w.S) {
+    w.kc = (ceil_div(w.Tp, w.S) + 127) / 128 * 128;
+    if (w.kc >= 256 && w.Tp - (w.S - 1) * w.kc >= 256) break;
+  }
+  if (w.S == 1) w.kc = w.Tp;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return r;
+  };
+  const size_t Ep2 = 2 * size_t(w.Ep);
+  w.dzs = static_cast<uint16_t*>(take(size_t(T) * Ep2 * 2));
+  w.dzt = static_cast<uint16_t*>(take(Ep2 * w.Tp * 2));
+  w.wt2 = static_cast<uint16_t*>(take(size_t(H) * Ep2 * 2));
+  w.xt = static_cast<uint16_t*>(take(size_t(H) * w.Tp * 2));
+  w.part = static_cast<float*>(take(size_t(w.S) * Ep2 * H * 4));
+  w.bytes = off;
+  return w;
 }
 
-// Backward of the router logits z = x W_r^T for a logit gradient dz [T, E] (fp32):
-//   dx = dz W_r  [T, H]   (rows r = experts, A = dz read transposed)
-//   dW = dz^T x  [E, H]   (rows r = tokens)
-// each as one row group through the weight-gradient kernel, fp32 sums in row order.
+// Backward of the router logits z = x W_r^T for a logit gradient dz [T, E] (fp32), on
+// the expert GEMM kernel's fp32-output mode (operands contiguous along the contraction):
+//   dx = [hi | lo] [W_r ; W_r]      [T, H]: A = dzs [T][2 Ep], B = wt2 [H][2 Ep]
+//   dW = hi^T x + lo^T x            [E, H]: A = dzt [2 Ep][Tp], B = x^T [H][Tp], split-K
+//        partials [S][2 Ep][H] summed in a fixed order
 hipError_t launch_router_backward(const moe_config& c, const void* x, const void* w_router,
-                                  const float* dz, float* dx, float* dw, hipStream_t st) {
+                                  const float* dz, float* dx, float* dw,
+                                  const RouterBwdWorkspace& ws, hipStream_t st) {
   const int T = c.num_tokens, E = c.num_experts, H = c.hidden;
-  WgradArgs w{};
-  w.Af = dz;
-  w.lda = E;
-  w.ldb = H;
-  w.N = H;
-  hipError_t err = hipSuccess;
+  const int Ep = ws.Ep, Tp = ws.Tp;
+  hipLaunchKernelGGL(router_dz_split, dim3(Ep / 64, Tp / 64), dim3(256), 0, st, dz, T, E, Ep, Tp,
+                     ws.dzs, ws.dzt);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const auto* wr = static_cast<const uint16_t*>(w_router);
+  const dim3 tgrid_w(ceil_div(H, 64), Ep / 64);
   if (dx) {
-    w.rows = E;
-    w.M = T;
-    w.B = static_cast<const uint16_t*>(w_router);
-    w.C = dx;
-    if ((err = launch_router_wgrad<kWgAf32T>(w, st)) != hipSuccess) return err;
+    hipLaunchKernelGGL(transpose_pad_bf16, tgrid_w, dim3(256), 0, st, wr, E, H, ws.wt2,
+                       2LL * Ep, 0);
+    hipLaunchKernelGGL(transpose_pad_bf16, tgrid_w, dim3(256), 0, st, wr, E, H, ws.wt2,
+                       2LL * Ep, Ep);
+    GemmArgs a{};
+    a.A = ws.dzs;
+    a.a_rows = T;
+    a.T = T;
+    a.K = 2 * Ep;
+    a.B0 = ws.wt2;
+    a.N = H;
+    a.C = dx;
+    a.ldc = H;
+    a.n_tiles = ceil_div(H, 256);
+    if ((err = launch_gemm_f32(a, 1, st)) != hipSuccess) return err;
   }
   if (dw) {
-    w.rows = T;
-    w.M = E;
-    w.B = static_cast<const uint16_t*>(x);
-    w.C = dw;
-    // few output tiles (E x H): 64 x 64 tiles keep more workgroups in flight
-    if ((err = launch_router_wgrad<kWgAf32, 64>(w, st)) != hipSuccess) return err;
+    hipLaunchKernelGGL(transpose_pad_bf16, dim3(ceil_div(H, 64), Tp / 64), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), T, H, ws.xt, (long long)Tp, 0);
+    GemmArgs b{};
+    b.A = ws.dzt;
+    b.a_rows = 2 * Ep;
+    b.T = 2 * Ep;
+    b.K = Tp;
+    b.B0 = ws.xt;
+    b.N = H;
+    b.C = ws.part;
+    b.ldc = H;
+    b.n_tiles = ceil_div(H, 256);
+    b.k_chunk = ws.S > 1 ? ws.kc : 0;
+    b.c_split_stride = 2LL * Ep * H;
+    if ((err = launch_gemm_f32(b, ws.S, st)) != hipSuccess) return err;
+    const long long n4 = 1LL * E * H / 4;
+    hipLaunchKernelGGL(router_dw_reduce, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(ws.part), ws.S, 2LL * Ep * H / 4,
+                       1LL * Ep * H / 4, n4, reinterpret_cast<float4*>(dw));
+    err = hipGetLastError();
   }
   return err;
 }

@@ -1,5 +1,5 @@
 // Calibration kernels for the measurements (not part of the layer): what this
-// device sustains for a plain HBM read stream and for back-to-back MFMAs, to quote
+// device sustains for plain HBM read and write streams and for back-to-back MFMAs, to quote
 // the expert GEMMs' rates against measured ceilings next to the datasheet peaks.
 // Built into its own library (libmoe_calib.so); only the benchmark loads it.
 #include <hip/hip_runtime.h>
@@ -32,6 +32,15 @@ __global__ __launch_bounds__(256) void read_stream(const uint4* __restrict__ p, 
     acc.x ^= a.x; acc.y ^= a.y; acc.z ^= a.z; acc.w ^= a.w;
   }
   out[size_t(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
+}
+
+// Every lane writes 16-byte vectors, grid-stride over the buffer (a plain HBM write
+// stream).
+__global__ __launch_bounds__(256) void write_stream(uint4* __restrict__ p, size_t n16) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint4 v = make_uint4(t, t ^ 0x55555555u, t * 3u, ~t);
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = v;
 }
 
 __device__ __forceinline__ uint32_t mix(uint32_t v) {
@@ -96,6 +105,14 @@ extern "C" {
 int moe_calib_read(const void* buf, size_t bytes, void* out, int blocks, void* stream) {
   hipLaunchKernelGGL(read_stream, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(buf), bytes / 16, static_cast<uint4*>(out));
+  return int(hipGetLastError());
+}
+
+// Writes `bytes` (a multiple of 16) to the device buffer `buf` once.  Returns a
+// hipError_t.
+int moe_calib_write(void* buf, size_t bytes, int blocks, void* stream) {
+  hipLaunchKernelGGL(write_stream, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint4*>(buf), bytes / 16);
   return int(hipGetLastError());
 }
 

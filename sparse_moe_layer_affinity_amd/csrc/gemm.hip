@@ -783,6 +783,19 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_f32(const GemmArgs& a, int splits, hipStream_t s) {
+  const int kc = a.k_chunk ? a.k_chunk : a.K;
+  const int last = a.K - (splits - 1) * kc;
+  if (a.K % 128 || kc % 128 || splits < 1 || (splits > 1 && !a.k_chunk) ||
+      (kc == 128 ? last != 128 : (kc < 256 || last < 256 || last > kc)))
+    return hipErrorInvalidValue;
+  const int rounds = ceil_div(ceil_div(a.T, kExpertBM), kXcds);
+  const dim3 grid(rounds * kXcds * a.n_tiles, splits);
+  if (kc == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_build_schedule(const moe_config& c, const int32_t* offsets, int bm, int4* sched,
                                  int32_t* sched_n, hipStream_t s) {
   const int T = c.num_tokens, E = c.num_experts, Ns = c.num_shared;

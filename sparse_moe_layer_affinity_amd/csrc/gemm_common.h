@@ -33,6 +33,10 @@ hipError_t launch_grouped_plain_bf16(const moe_config& c, const GemmArgs& a, hip
 // The same on weights stored [K][N] (B0: K rows 0..k_split-1, B1 the rest; b_stride
 // elements per expert in each), no transposed copy needed.
 hipError_t launch_grouped_kn_bf16(const moe_config& c, const GemmArgs& a, hipStream_t s);
+// One group of a.T rows, fp32 output C = A B^T (A [a.T][K], B [N][K] bf16), split-K over
+// `splits` ranges of a.k_chunk (0: one range) into partials a.c_split_stride apart.
+// Every range at least 256 long (or every range 128), K a multiple of 128.
+hipError_t launch_gemm_f32(const GemmArgs& a, int splits, hipStream_t s);
 
 // Arguments of the FP8 expert GEMMs (e4m3 operands, 128x128 / 1x128 block scales).
 struct Fp8Args {

@@ -121,8 +121,22 @@ hipError_t launch_expert_wgrad_mfma(const moe_config& c, const void* x, const in
                                     const uint16_t* ab, const uint16_t* dab, float* dw_gate,
                                     float* dw_up, float* dw_down, const WgradPackWorkspace& ws,
                                     hipStream_t s);
+// Scratch of the router backward (its own workspace): the logit gradient split in
+// bf16 hi and lo parts in both layouts, W_r^T twice side by side, x^T, and the split-K
+// partials of dW_r.  Ep = E rounded up to 64, Tp = T rounded up to 128 (at least 256).
+struct RouterBwdWorkspace {
+  uint16_t* dzs;   // [T][2 Ep]   hi | lo
+  uint16_t* dzt;   // [2 Ep][Tp]  hi rows, then lo rows
+  uint16_t* wt2;   // [H][2 Ep]   W_r^T | W_r^T
+  uint16_t* xt;    // [H][Tp]     x^T
+  float* part;     // [S][2 Ep][H]
+  int Ep, Tp, S, kc;   // kc: tokens per split
+  size_t bytes;
+};
+RouterBwdWorkspace router_bwd_workspace_layout(const moe_config& c, void* base);
 hipError_t launch_router_backward(const moe_config& c, const void* x, const void* w_router,
-                                  const float* dz, float* dx, float* dw, hipStream_t s);
+                                  const float* dz, float* dx, float* dw,
+                                  const RouterBwdWorkspace& ws, hipStream_t st);
 hipError_t launch_gate_backward(const moe_config& c, const float* scores, const int32_t* idx,
                                 const float* dgate, float* grad, int accumulate, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int rows, int cols, uint8_t* q, float* scales,

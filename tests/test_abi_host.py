@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
                           "moe_router_scores", "moe_balance_loss", "moe_combine_backward",
                           "moe_gate_backward", "moe_swiglu_backward", "moe_backward_workspace_bytes",
                           "moe_expert_backward_input", "moe_expert_backward", "moe_router_backward",
-                          "moe_layer_forward_noalloc", "moe_status_string"}
+                          "moe_router_backward_workspace_bytes", "moe_layer_forward_noalloc",
+                          "moe_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -223,12 +224,25 @@ def test_expert_backward_argument_checks():
     assert full(dw=(A, 0, A)) == B.MOE_ERR_INVALID_ARGUMENT             # all or none
     assert full(dw=(0, 0, A)) == B.MOE_ERR_INVALID_ARGUMENT
     rb = B.moe_router_backward
-    assert code_of(rb, c, A, A, A, 0, 0, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
-    assert code_of(rb, c, 0, A, A, A, A, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
-    assert code_of(rb, c, A, A, 0, A, None, stream=0) == B.MOE_ERR_INVALID_ARGUMENT
-    assert code_of(rb, cfg(act="f32", w="f32", hidden=256, inter=128, T=64, E=16, K=4, G=4, M=2),
-                   A, A, A, A, A, stream=0) == B.MOE_ERR_UNSUPPORTED
-    assert code_of(rb, cfg(E=250, G=10, M=4), A, A, A, A, A, stream=0) == B.MOE_ERR_UNSUPPORTED
+    rneed = moe.moe_router_backward_workspace_bytes(c)
+    # hi | lo of the logit gradient twice (8192 x 512 bf16 each), W_r^T twice, x^T,
+    # four split-K partials of [512, 7168] fp32
+    assert rneed == 2 * 8192 * 512 * 2 + 7168 * 512 * 2 + 7168 * 8192 * 2 + 4 * 512 * 7168 * 4
+    assert moe.moe_router_backward_workspace_bytes(cfg(act="f32", w="f32")) == 0
+    assert moe.moe_router_backward_workspace_bytes(cfg(hidden=7164)) == 0
+    assert moe.moe_router_backward_workspace_bytes(cfg(E=250, G=10, M=4)) > 0   # E padded to 256
+
+    def router(conf=c, ws=A, ws_bytes=rneed, x=A, w=A, g=A, dx=A, dw=A):
+        return code_of(rb, conf, x, w, g, dx, dw, ws, ws_bytes, stream=0)
+
+    assert router(dx=0, dw=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert router(x=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert router(g=0, dw=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert router(ws=0) == B.MOE_ERR_INVALID_ARGUMENT
+    assert router(ws=A + 32) == B.MOE_ERR_INVALID_ARGUMENT
+    assert router(ws_bytes=rneed - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert router(conf=cfg(act="f32", w="f32", hidden=256, inter=128, T=64, E=16, K=4, G=4,
+                           M=2)) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_weight_scale_pointer_rules():

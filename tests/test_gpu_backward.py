@@ -235,13 +235,17 @@ def test_expert_backward_weights(name, over, n_check):
 
 @pytest.mark.parametrize("name,over", [("decode_bf16", dict(T=37, **SMALL)),
                                        ("decode_bf16", dict(T=3, **SMALL)),
+                                       ("decode_bf16", dict(T=700, **{**SMALL, "E": 72, "G": 8})),
+                                       ("decode_bf16", dict(T=1000, E=250, G=10, M=4)),
                                        ("decode_bf16", {}),
                                        ("prefill_bf16", {})])
 def test_router_backward(name, over):
     """dx = dz W_r (sampled tokens) and dW_r = dz^T x (all experts) against the oracle on
-    a seeded logit gradient; bound 5e-5 of the largest magnitude (fp32 products of the
-    fp32 gradient and bf16 operands, sequential fp32 sums over up to T = 8192 terms:
-    about eps * sqrt(T) relative to the result, with headroom)."""
+    a seeded logit gradient; bound 5e-5 of the largest magnitude: dz enters as two bf16
+    parts (hi + lo within 2^-17 |dz|), products exact, fp32 sums over up to T = 8192
+    terms (about eps * sqrt(T) relative to the result), with headroom.  Also the odd
+    expert counts (padded to 64 inside) and token counts that leave ragged split-K
+    ranges."""
     cfg = workloads.get(name).replace(**over)
     log(f"router backward {name} {over}")
     T, E, H = cfg.T, cfg.E, cfg.hidden
@@ -252,11 +256,15 @@ def test_router_backward(name, over):
     c = config_of(cfg)
     dx = torch.full((T, H), 7.0, device="cuda")
     dw = torch.full((E, H), 7.0, device="cuda")
-    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), dx, dw)
+    ws = torch.full((moe.moe_router_backward_workspace_bytes(c),), 0x7f, dtype=torch.uint8,
+                    device="cuda")
+    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), dx, dw, ws)
     dx_only = torch.empty_like(dx)
-    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), dx_only, None)
+    dw_only = torch.empty_like(dw)
+    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), dx_only, None, ws)
+    moe.moe_router_backward(c, x.cuda(), w_r.cuda(), dz.cuda(), None, dw_only, ws)
     torch.cuda.synchronize()
-    assert torch.equal(dx, dx_only)
+    assert torch.equal(dx, dx_only) and torch.equal(dw, dw_only)
     toks = workloads.sample_rows(T, 256, seed=6).numpy()
     want_dx, _ = oracle.router_backward(x[toks], w_r, dz[toks])
     _, want_dw = oracle.router_backward(x, w_r, dz)
