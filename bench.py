@@ -40,51 +40,38 @@ def log(*a):
 
 
 # the files the counted expert-GEMM kernels are compiled from, and their build flags
+# (bf16 weights; FP8 weights add their own kernels)
 GEMM_SOURCES = ["sparse_moe_layer_affinity_amd/csrc/gemm.hip",
-                "sparse_moe_layer_affinity_amd/csrc/gemm_fp8.hip",
-                "sparse_moe_layer_affinity_amd/csrc/gemm_fp8p2.hip",
                 "sparse_moe_layer_affinity_amd/csrc/gemm_common.h",
                 "sparse_moe_layer_affinity_amd/csrc/kernels.h",
                 "sparse_moe_layer_affinity_amd/csrc/common.h",
                 "include/moe.h",
                 "sparse_moe_layer_affinity_amd/build.py"]
+GEMM_SOURCES_FP8 = ["sparse_moe_layer_affinity_amd/csrc/gemm_fp8.hip",
+                    "sparse_moe_layer_affinity_amd/csrc/gemm_fp8p2.hip"]
 
 
-def source_hash() -> str:
-    """Hash of the expert-GEMM kernels' sources, to tell whether stored counter
-    figures of those kernels still apply."""
+def source_hash(fp8: bool) -> str:
+    """Hash of the expert-GEMM kernels' sources (with the FP8 kernels' for FP8
+    weights), to tell whether stored counter figures of those kernels still apply."""
     h = hashlib.sha256()
-    for name in GEMM_SOURCES:
+    for name in GEMM_SOURCES + (GEMM_SOURCES_FP8 if fp8 else []):
         with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_counters(workload: str):
-    """MFMA-busy fraction, sustained shader clock and fetched/written bytes per expert-GEMM
-    kernel from the committed counter runs (rocprofv3 --pmc), or None when the kernels
-    changed since the counters were taken."""
+def stored_record(workload: str, fp8: bool):
+    """The committed counter runs (rocprofv3 --pmc) of a workload's expert-GEMM kernels,
+    or None when those kernels changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != source_hash():
+    if not rec or rec.get("source_hash") != source_hash(fp8):
         return None
-    return rec.get("kernels")
-
-
-def stored_traffic(workload: str):
-    """HBM bytes per moe_grouped_ffn call from the committed counter runs, or None
-    when the kernels changed since the counters were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(workload)
-    except (OSError, ValueError):
-        return None
-    if not rec or rec.get("source_hash") != source_hash():
-        return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def cpu_baseline(cfg, d, n_tokens: int, n_tokens_1t: int = 8):
@@ -339,6 +326,9 @@ def main():
                     choices=["prefill_bf16", "decode_bf16", "prefill_fp8", "prefill_fp8_pow2", "skewed_bf16"])
     ap.add_argument("--cpu-tokens", type=int, default=48,
                     help="tokens in the oracle's bounded sample (0 skips it)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the layer steps only (no calibration kernels, balance loss or "
+                         "backward legs after them), e.g. for counter runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -444,23 +434,34 @@ def main():
     # the layer's: + the router weight, the bias, indices, gates and loads
     layer_bytes = ffn_bytes + E * cfg.hidden * ab + E * 8 + T * K * 8
     decode = cfg.T <= 512
-    if decode:
-        achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK, 4)}
-        lay = layer_bytes / (ms_per_step * 1e-3) / 1e9
-        roof["layer"] = {"achieved": round(lay, 1), "frac": round(lay / HBM_PEAK, 4),
-                         "bytes": layer_bytes, "ms": round(ms_per_step, 4)}
+    # the bound: whichever of the FLOPs at the dense MFMA peak and the algorithmic bytes
+    # at the HBM peak takes longer (the prefill GEMMs sit just on the HBM side of the
+    # ridge: about 280 FLOP per byte against 2500 / 8 = 312)
+    gb_s = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    t_mfma = ffn_flops / (PEAK[cfg.w] * 1e12)
+    t_hbm = ffn_bytes / (HBM_PEAK * 1e9)
+    hbm_bound = decode or t_hbm > t_mfma
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gb_s, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": round(gb_s / HBM_PEAK, 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK[cfg.w],
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK[cfg.w], 4)}
-    roof["traffic"] = stored_traffic(cfg.name)
+    roof["mfma_frac"] = round(gemm_tflops / PEAK[cfg.w], 4)
+    roof["hbm_frac"] = round(gb_s / HBM_PEAK, 4)
+    roof["ms_at_mfma_peak"] = round(t_mfma * 1e3, 4)
+    roof["ms_at_hbm_peak"] = round(t_hbm * 1e3, 4)
+    if decode:
+        lay = layer_bytes / (ms_per_step * 1e-3) / 1e9
+        roof["layer"] = {"achieved": round(lay, 1), "frac": round(lay / HBM_PEAK, 4),
+                         "bytes": layer_bytes, "ms": round(ms_per_step, 4)}
+    stored = stored_record(cfg.name, workloads.is_fp8(cfg.w))
+    roof["traffic"] = stored["bytes_per_launch"] if stored else None
     roof["kernel"] = "moe_grouped_ffn (grouped_gemm gated GEMM1 + GEMM2)"
     roof["algorithmic"] = {"flops": ffn_flops, "bytes": ffn_bytes,
                            "touched_experts_per_step": [int(v) for v in touched]}
-    counters = stored_counters(cfg.name)
-    if counters:
-        roof["counters"] = counters
+    if stored:
+        roof["counters"] = stored["kernels"]
 
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -485,15 +486,17 @@ def main():
             "max_over_mean_load_per_step": [round(float(v) / mean_load, 3)
                                             for v in loads.max(1).values.cpu().numpy()]}
 
-    cal = calibration_leg(stream)
-    result["calibration"] = cal
-    measured = cal["hbm_read_GBps"] if decode else cal["mfma_e4m3_TFLOPs" if workloads.is_fp8(cfg.w)
-                                                       else "mfma_bf16_TFLOPs"]
-    roof["measured_peak"] = measured
-    roof["frac_of_measured_peak"] = round(roof["achieved"] / measured, 4)
-    result["balance_loss"] = balance_loss_leg(moe, cfg, c, d, idx, ws, stream)
-    result["backward"] = backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row,
-                                      y_rows, y, ws, stream)
+    if not args.no_extras:
+        cal = calibration_leg(stream)
+        result["calibration"] = cal
+        measured = cal["hbm_read_GBps"] if hbm_bound else cal[
+            "mfma_e4m3_TFLOPs" if workloads.is_fp8(cfg.w) else "mfma_bf16_TFLOPs"]
+        roof["measured_peak"] = measured
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / measured, 4)
+        result["balance_loss"] = balance_loss_leg(moe, cfg, c, d, idx, ws, stream)
+        result["backward"] = backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row,
+                                          y_rows, y, ws, stream)
+        result["backward"]["expert_wgrad_fp32_out_bytes"] = 4.0 * 3 * (E + cfg.Ns) * cfg.hidden * cfg.inter
     if args.cpu_tokens > 0:
         log(f"[bench] oracle baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_tokens)
