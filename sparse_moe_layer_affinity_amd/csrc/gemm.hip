@@ -700,9 +700,46 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  for (int id = t; id < total; id += 512) {
-    const int4 blk = block_of(id);
-    sched[atomicAdd(&cls_next[cls_of(blk)], 1)] = blk;
+  // stable placement (blocks of one class keep their id order, so the schedule is the
+  // same on every run): 512 ids at a time, each block's rank among the same-class
+  // blocks of its wave from ballots, the waves' per-class counts added in wave order
+  __shared__ int wcount[8][kClasses];
+  const int lane = t & 63, wv = t >> 6;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int base = 0; base < total; base += 512) {
+    const int id = base + t;
+    const bool valid = id < total;
+    int4 blk = make_int4(0, 0, 0, 0);
+    int cl = -1;
+    if (valid) {
+      blk = block_of(id);
+      cl = cls_of(blk);
+    }
+    wcount[wv][lane] = 0;                   // kClasses == 64: one entry per lane
+    __syncthreads();
+    uint64_t left = __ballot(valid);
+    int rank = 0;
+    while (left) {
+      const int leader = __ffsll((unsigned long long)left) - 1;
+      const int lc = __shfl(cl, leader);
+      const uint64_t same = __ballot(valid && cl == lc);
+      if (valid && cl == lc) rank = __popcll(same & below);
+      if (lane == leader) wcount[wv][lc] = __popcll(same);
+      left &= ~same;
+    }
+    __syncthreads();
+    if (valid) {
+      int pos = cls_next[cl] + rank;
+      for (int w2 = 0; w2 < wv; ++w2) pos += wcount[w2][cl];
+      sched[pos] = blk;
+    }
+    __syncthreads();
+    if (t < kClasses) {
+      int n = 0;
+      for (int w2 = 0; w2 < 8; ++w2) n += wcount[w2][t];
+      cls_next[t] += n;
+    }
+    __syncthreads();
   }
 }
 
