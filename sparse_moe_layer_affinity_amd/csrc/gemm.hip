@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   // block's n-tiles are consecutive slots of one XCD, so they share its A rows through
   // that XCD's L2.  The expert GEMMs run persistent workgroups (one per CU; gridDim.x
   // = 8 x nwg): workgroup j of an XCD takes slots j, j + nwg, j + 2 nwg, ... and loads
-  // the first stage of its next tile while it writes out the current one.  The router
-  // logits run one workgroup per tile.
+  // the first stage of its next tile while it writes out the current one.  The
+  // fp32-output mode (router logits, router backward) runs one workgroup per tile.
   constexpr bool PERSIST = MODE != kPlainF32;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
@@ -133,12 +133,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       g_ = e.x;
       m0_ = e.y;
       mvalid_ = e.z;
-    } else {                                              // router: one group of T rows
-      const int round = s / a.n_tiles;
-      nt_ = s - round * a.n_tiles;
-      pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+    } else {
+      // one group of T rows, one workgroup per tile (not persistent): workgroup b takes
+      // row block b / n_tiles, n-tile b % n_tiles, so any shape spreads over all XCDs
+      // (a shape with fewer row blocks than XCDs included)
+      const int b = int(blockIdx.x);
+      const int mb = b / a.n_tiles;
+      nt_ = b - mb * a.n_tiles;
       g_ = 0;
-      m0_ = pos * BM;
+      m0_ = mb * BM;
       if (m0_ >= a.T) return false;
       mvalid_ = min(BM, a.T - m0_);
     }
@@ -813,8 +816,7 @@ hipError_t launch_gemm_router_bf16(const moe_config& c, const uint16_t* x, const
   a.a_rows = c.num_tokens;
   a.k_chunk = router_k_chunk(c);
   a.c_split_stride = 1LL * c.num_tokens * c.num_experts;
-  const int rounds = ceil_div(ceil_div(c.num_tokens, kExpertBM), kXcds);
-  const dim3 grid(rounds * kXcds * a.n_tiles, router_splits(c));
+  const dim3 grid(ceil_div(c.num_tokens, kExpertBM) * a.n_tiles, router_splits(c));
   if (c.hidden == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -826,8 +828,7 @@ hipError_t launch_gemm_f32(const GemmArgs& a, int splits, hipStream_t s) {
   if (a.K % 128 || kc % 128 || splits < 1 || (splits > 1 && !a.k_chunk) ||
       (kc == 128 ? last != 128 : (kc < 256 || last < 256 || last > kc)))
     return hipErrorInvalidValue;
-  const int rounds = ceil_div(ceil_div(a.T, kExpertBM), kXcds);
-  const dim3 grid(rounds * kXcds * a.n_tiles, splits);
+  const dim3 grid(ceil_div(a.T, kExpertBM) * a.n_tiles, splits);
   if (kc == 128) hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((grouped_gemm_dma<kPlainF32, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
