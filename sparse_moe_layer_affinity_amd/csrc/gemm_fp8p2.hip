@@ -211,10 +211,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
       }
       // the exponents were written by the VALU: wait states before an MFMA reads them
       asm volatile("s_nop 4" ::: "memory");
+      i32x8_t wfb[2];
+      if constexpr (NJB > 0) wfb[0] = lds_frag(w_lane + wb, w_blk(0));
   #pragma unroll
       for (int ib = 0; ib < 8; ++ib) {
         if constexpr (NJB > 0) {
-          const i32x8_t wf = lds_frag(w_lane + wb, w_blk(ib));
+          if (ib + 1 < 8) wfb[(ib + 1) & 1] = lds_frag(w_lane + wb, w_blk(ib + 1));
+          __builtin_amdgcn_sched_barrier(0);
+          const i32x8_t& wf = wfb[ib & 1];
           const int h = (MODE == kGatedBf16 && ib >= 4) ? 1 : 0;
   #pragma unroll
           for (int jb = 0; jb < NJB; ++jb) {
@@ -226,6 +230,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
               else mfma_p2v(acc[ib][jb], wf, tf[jb], ew[h], ea[jb]);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (k + 1 < nk) {
