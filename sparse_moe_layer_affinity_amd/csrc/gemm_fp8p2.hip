@@ -13,12 +13,13 @@
 // 8 x 5 MFMA blocks, 160 accumulators per lane.  Twice the weight rows per token row
 // loaded halves the token bytes per flop.
 //
-// K advances one 128-byte block per stage.  Weights (from HBM) cycle through three
-// 32 KB stage buffers, two stages ahead; tokens (mostly L2 hits) and their scales use
-// one buffer each: every wave reads its stage-k token fragments and scales into
-// registers, a barrier confirms it, and stage k+1's tokens and scales are loaded into
-// the same buffers while stage k's MFMAs run.  Row blocks come from the largest-first
-// XCD schedule of the bf16 kernel.
+// K advances one 128-byte block per stage, with one barrier per stage.  Weights (from
+// HBM, 32 KB a stage), tokens (mostly L2 hits, 40 KB) and their scales have two stage
+// buffers each: right after the barrier that publishes stage k, stage k+1's loads go
+// into the buffers stage k-1 left, and stage k's fragments are read while they fly;
+// within the stage each weight block's fragment is read while the MFMAs of the block
+// before it run.  Row blocks come from the largest-first XCD schedule of the bf16
+// kernel.
 #include "gemm_common.h"
 
 namespace moe {
@@ -53,12 +54,12 @@ template <int MODE>
 __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
   constexpr int BW = 256, BT = kFp8BT, ROWB = 128;
   constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 32 KB, 40 KB
-  constexpr int SW = 3;                                   // weight stage buffers
+  constexpr int SW = 2;                                   // weight stage buffers
   constexpr int NTB = BT / 64;                            // 16-token blocks per wave: 5
-  // LDS: the token buffer, the weight ring, two token-scale and two weight-scale buffers
-  // (waves 5..7 write 256 bytes each, wave 7's are a dummy)
-  constexpr uint32_t kTOff = 0;
-  constexpr uint32_t kWOff = TSTAGE;
+  // LDS: two token buffers, two weight buffers, two token-scale and two weight-scale
+  // buffers (waves 5..7 write 256 bytes each, wave 7's are a dummy)
+  constexpr uint32_t kTOff = 0;                           // two token stage buffers
+  constexpr uint32_t kWOff = 2 * TSTAGE;
   constexpr uint32_t kSaOff = kWOff + SW * WSTAGE;
   constexpr uint32_t kSaStage = 4 * BT;                   // 1280 B
   constexpr uint32_t kSwOff = kSaOff + 2 * kSaStage;
@@ -136,10 +137,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
       dma16(rsrc_w, voff_w[j & 1], uint32_t(ks) * ROWB + uint32_t(j >> 1) * 16u * uint32_t(K),
             dst + j * 1024u);
   };
-  // token rows of stage ks (the one token buffer) and its scales (buffer ks & 1)
+  // token rows of stage ks and its scales (buffers ks & 1)
   auto load_t = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NTB; ++j) dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + j * 1024u);
+    for (int j = 0; j < NTB; ++j)
+      dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + uint32_t(ks & 1) * TSTAGE + j * 1024u);
     dma4(rsrc_s, voff_s, uint32_t(ks) * s_step,
          __builtin_amdgcn_readfirstlane(wave_s + uint32_t(ks & 1) * s_par));
   };
@@ -176,39 +178,32 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
     // 8-bit exponent code of a power-of-two float32, in every byte of the operand
     auto e8 = [](float v) { return int(((__float_as_uint(v) >> 23) & 0xffu) * 0x01010101u); };
 
-    // prologue: tokens 0 (+ scales), weights 0 and 1; stage 0 published once only
-    // weight stage 1 (4 loads) may be pending.  K is a multiple of 128: nk >= 1.
+    // prologue: stage 0 (tokens, scales, weights), published
     const int nk = KBLK;
     load_t(0);
     load_w(0);
-    if (nk > 1) {
-      load_w(1);
-      wait_vmcnt<4>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     stage_barrier();
     auto stage = [&](int k, auto first_tag) __attribute__((always_inline)) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      const uint32_t wb = kWOff + uint32_t(k % SW) * WSTAGE;
+      const uint32_t wb = kWOff + uint32_t(k & 1) * WSTAGE;
+      const uint32_t tb = kTOff + uint32_t(k & 1) * TSTAGE;
       const uint32_t sp = uint32_t(k & 1);
+      // every wave is past stage k-1: its buffers take stage k+1
+      if (k + 1 < nk) {
+        load_t(k + 1);
+        load_w(k + 1);
+      }
       // token fragments and exponents of stage k into registers
       i32x8_t tf[NJB > 0 ? NJB : 1];
   #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) tf[jb] = lds_frag(t_lane, kTOff + uint32_t(16 * jb) * ROWB);
+      for (int jb = 0; jb < NJB; ++jb) tf[jb] = lds_frag(t_lane, tb + uint32_t(16 * jb) * ROWB);
       int ea[NJB > 0 ? NJB : 1], ew[2];
       ew[0] = e8(lds_f32(kSwOff + sp * kSwStage + (MODE == kGatedBf16 ? 0u : 256u * wn)));
       ew[1] = MODE == kGatedBf16 ? e8(lds_f32(kSwOff + sp * kSwStage + 256u)) : ew[0];
   #pragma unroll
       for (int jb = 0; jb < NJB; ++jb)
         ea[jb] = e8(lds_f32(kSaOff + sp * kSaStage + uint32_t(t_row + 16 * jb) * 4u));
-      if (k + 1 < nk) {
-        // every wave holds its stage-k tokens: that buffer takes stage k+1, and the
-        // weight buffer stage k-1 left takes weights k+2
-        stage_barrier();
-        load_t(k + 1);
-        if (k + 2 < nk) load_w(k + 2);
-      }
       // the exponents were written by the VALU: wait states before an MFMA reads them
       asm volatile("s_nop 4" ::: "memory");
       i32x8_t wfb[2];
@@ -234,10 +229,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
         }
       }
       if (k + 1 < nk) {
-        // publish stage k+1: its tokens went out this stage, its weights one stage ago;
-        // weights k+2 may stay in flight
-        if (k + 2 < nk) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
+        // publish stage k+1
+        wait_vmcnt<0>();
         stage_barrier();
       }
     };
@@ -260,7 +253,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
     // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
     if constexpr (MODE == kGatedBf16) {
       if (a.Q) {
-        // staging in the token buffer and the weight ring (80 KB of their 136 KB)
+        // staging in the two token buffers (80 KB)
         fp8_epilogue_hquant<NJB>(acc, w, l, m0, mvalid, n0, a.Q, a.ldc, a.QS, a.scale_rows,
                                  reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kAmOff),
                                  reinterpret_cast<uint32_t*>(lds), true);
