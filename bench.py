@@ -227,8 +227,9 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
     writes the [T, E] logit gradient; SwiGLU backward reads three [rows, inter] arrays
     and writes two.  The experts' input gradient (bf16) is timed on the step's own
     inputs and the combine backward's row gradients, reported with its GEMM FLOPs, and
-    their weight gradients with the a, b and dh GEMMs they need, and
-    the router logits' backward (dx and dW_r, 4 T E H flops)."""
+    their weight gradients with the a, b and dh GEMMs they need, both in one call (a, b
+    and dh shared: 14 rows H I flops), and the router logits' backward (dx and dW_r,
+    4 T E H flops)."""
     import torch
     T, E, K, H = cfg.T, cfg.E, cfg.K, cfg.hidden
     eb = 4 if cfg.act == "f32" else 2
@@ -289,6 +290,9 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
         dwd = torch.empty((G, H, cfg.inter), device="cuda")
         us_w = timed(lambda: moe.moe_expert_backward(c, d["x"], offsets, row_token, pair_row, wts,
                                                      dy_rows, None, dwg, dwu, dwd, bws), n=2)
+        # both gradients in one call (a, b and dh computed once for both)
+        us_full = timed(lambda: moe.moe_expert_backward(c, d["x"], offsets, row_token, pair_row,
+                                                        wts, dy_rows, dx, dwg, dwu, dwd, bws), n=2)
         del dwg, dwu, dwd
         flops_w = 6.0 * cfg.rows * H * cfg.inter      # three weight gradients: 2 r H I each
         flops = 8.0 * cfg.rows * H * cfg.inter        # a, b, dh: 2 r H I each; dX: 4 r H I
@@ -298,7 +302,10 @@ def backward_leg(moe, cfg, c, d, idx, gate, offsets, row_token, pair_row, y_rows
               "expert_backward_weights_us": round(us_w, 1),
               "expert_backward_weights_flops": flops_w + 6.0 * cfg.rows * H * cfg.inter,
               "expert_backward_weights_tflops": round(
-                  (flops_w + 6.0 * cfg.rows * H * cfg.inter) / (us_w * 1e-6) / 1e12, 1)}
+                  (flops_w + 6.0 * cfg.rows * H * cfg.inter) / (us_w * 1e-6) / 1e12, 1),
+              "expert_backward_full_us": round(us_full, 1),
+              "expert_backward_full_flops": flops + flops_w,
+              "expert_backward_full_tflops": round((flops + flops_w) / (us_full * 1e-6) / 1e12, 1)}
         del bws
     b_comb = T * H * eb + T * K * H * eb + cfg.rows * H * eb + T * K * (4 + 8)
     b_gate = T * K * 12 + T * E * 4
