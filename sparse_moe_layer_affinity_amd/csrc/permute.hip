@@ -3,9 +3,10 @@
 // section 2.4: no token dropping; section 2.3: loads are counted over the whole
 // batch).
 //
-// Deterministic and atomic-free, in three passes over 64-token chunks:
-//   1. masks: thread e of a chunk's workgroup owns expert e and builds the 64-bit
-//      mask of the chunk's tokens that chose e (no shared counters at all);
+// Deterministic, in three passes over 64-token chunks:
+//   1. masks: every (token, k) entry of a chunk ORs its token's bit into its expert's
+//      64-bit mask in LDS (an OR commutes: the masks do not depend on the order; no
+//      counter is shared);
 //   2. scan:  one workgroup: per expert, running popcounts over the chunks give each
 //      chunk's base row and the expert load; an LDS scan over experts gives offsets;
 //   3. scatter: pair (t, k) with expert e goes to row
@@ -16,21 +17,20 @@ namespace moe {
 
 __global__ __launch_bounds__(256) void permute_masks(const int32_t* __restrict__ idx, int T,
                                                      int K, int E, uint64_t* __restrict__ masks) {
-  __shared__ int32_t ids[kTokChunk * 8];
+  // each (token, k) entry of the chunk sets its token's bit in its expert's mask (an OR:
+  // the same masks in any order); entries outside [0, E) set nothing
+  __shared__ unsigned long long m[256];
   const int c = blockIdx.x;
   const int t0 = c * kTokChunk;
   const int ntok = min(kTokChunk, T - t0);
-  for (int i = threadIdx.x; i < ntok * K; i += 256) ids[i] = idx[size_t(t0) * K + i];
+  if (threadIdx.x < E) m[threadIdx.x] = 0ull;
   __syncthreads();
-  const int e = threadIdx.x;
-  if (e >= E) return;
-  uint64_t m = 0;
-  for (int t = 0; t < ntok; ++t) {
-    bool hit = false;
-    for (int k = 0; k < K; ++k) hit |= ids[t * K + k] == e;
-    m |= uint64_t(hit) << t;
+  for (int i = threadIdx.x; i < ntok * K; i += 256) {
+    const int e = idx[size_t(t0) * K + i];
+    if (e >= 0 && e < E) atomicOr(&m[e], 1ull << (i / K));
   }
-  masks[size_t(c) * E + e] = m;
+  __syncthreads();
+  if (threadIdx.x < E) masks[size_t(c) * E + threadIdx.x] = m[threadIdx.x];
 }
 
 // One workgroup of 256 threads (E <= 256).
