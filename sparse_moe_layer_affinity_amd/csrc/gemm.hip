@@ -103,10 +103,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
 
   // ---- tiles ---------------------------------------------------------------------
   // Workgroups reach the XCDs round-robin (b % 8).  The row blocks (see build_schedule),
-  // sorted largest first, are dealt to the XCDs in snake order (round r: XCDs 0..7,
-  // then 7..0), so every XCD gets an even share and runs its largest blocks first; a
-  // block's n-tiles are consecutive slots of one XCD, so they share its A rows through
-  // that XCD's L2.  The expert GEMMs run persistent workgroups (one per CU; gridDim.x
+  // sorted largest first, are dealt to the XCDs in pairs of adjacent blocks in snake
+  // order (round r: XCDs 0..7, then 7..0), so every XCD gets an even share and runs its
+  // largest blocks first; a pair's n-tiles are consecutive slots of one XCD, so they
+  // share its A rows (and, for two blocks of one expert, its weight tiles) through that
+  // XCD's L2.  The expert GEMMs run persistent workgroups (one per CU; gridDim.x
   // = 8 x nwg): workgroup j of an XCD takes slots j, j + nwg, j + 2 nwg, ... and loads
   // the first stage of its next tile while it writes out the current one.  The
   // fp32-output mode (router logits, router backward) runs one workgroup per tile.
@@ -118,12 +119,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   int slot = blockIdx.x / kXcds;
   const int nblocks = a.sched ? *a.sched_n : 0;
   // place of slot s of this XCD: schedule position pos, n-tile nt; valid if it has a block
+  // slots walk pairs of adjacent schedule positions (pair q = round * 8 + the XCD's
+  // snake place), the n-tiles of the pair's two blocks interleaved, so a busy expert's
+  // consecutive blocks stream each weight tile side by side through one L2; an odd block
+  // count leaves the last pair's second slots empty (skipped)
   auto place_of = [&](int s, int& pos_, int& nt_) __attribute__((always_inline)) {
-    const int round = s / a.n_tiles;
-    nt_ = s - round * a.n_tiles;
-    pos_ = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+    const int per = 2 * a.n_tiles;
+    const int rp = s / per, rem = s - rp * per;
+    nt_ = rem >> 1;
+    const int q = rp * kXcds + ((rp & 1) ? kXcds - 1 - xcd : xcd);
+    pos_ = 2 * q + (rem & 1);
     return pos_ < nblocks;
   };
+  // slots past this one hold no block on any XCD
+  const int slot_limit = ((nblocks + 1) / 2 + kXcds - 1) / kXcds * 2 * a.n_tiles;
   // tile of slot s: group g, rows m0 .. m0 + mvalid - 1, n-tile nt
   auto tile_of = [&](int s, int& g_, int& m0_, int& mvalid_, int& nt_) __attribute__((always_inline)) {
     int pos;
@@ -148,7 +157,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     return true;
   };
   int g = 0, m0 = 0, mvalid = 0, nt = 0;
-  if (!tile_of(slot, g, m0, mvalid, nt)) return;
+  if (a.sched) {
+    // the first slot of this workgroup with a block
+    while (slot < slot_limit && !tile_of(slot, g, m0, mvalid, nt)) slot += nwg;
+    if (slot >= slot_limit) return;
+  } else if (!tile_of(slot, g, m0, mvalid, nt)) return;
   int n0 = nt * BN_OUT;
   // split-K (router logits): this workgroup's K range, its own partial output slice
   const int kst0 = blockIdx.y * (a.k_chunk / BK);      // first stage
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   };
   const int nk = K / BK;
   bool has_next = false;                     // next tile of this workgroup and its place
-  int pos2 = 0, g2 = 0, m02 = 0, mv2 = 0, nt2 = 0;
+  int pos2 = 0, g2 = 0, m02 = 0, mv2 = 0, nt2 = 0, next_slot = 0;
   // the next tile's schedule entry, loaded at the start of a tile (a vector load: the
   // scalar-cache wait would land in the stage barriers) and read in its epilogue
   const __amdgpu_buffer_rsrc_t rsrc_sched = make_rsrc(a.sched, uint32_t(nblocks) * 16u);
@@ -616,7 +629,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   static_for<0, NDB>([&](auto j) __attribute__((always_inline)) { dma_b(1, I1{}, j); });
   for (;;) {
     set_frag_bases();
-    has_next = PERSIST && place_of(slot + nwg, pos2, nt2);
+    if constexpr (PERSIST) {
+      int s2 = slot + nwg;
+      while (s2 < slot_limit && !place_of(s2, pos2, nt2)) s2 += nwg;
+      has_next = s2 < slot_limit;
+      next_slot = s2;
+    }
     const int ni_valid = min(4, max(0, (min(mvalid, BMAIN) - wm * WTM + 31) >> 5));
     // rows 256..319 form two 32-row extra strips; every wave takes two 32-column blocks
     // of each strip that has rows (nx strips), so the four waves stay balanced
@@ -639,7 +657,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     // these offsets inside the epilogue makes the register allocator spill.
     set_voff_a(m02, mv2);
     static_for<0, NDA>([&](auto j) __attribute__((always_inline)) { dma_a(0, I0{}, j); });
-    slot += nwg;
+    slot = next_slot;
     g = g2;
     m0 = m02;
     mvalid = mv2;
