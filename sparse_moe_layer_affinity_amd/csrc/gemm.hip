@@ -193,7 +193,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   uint32_t voff_a[NDA], voff_b[NDB];
   // A row offsets of a tile: routed rows (below TK) gather their token through
   // row_token; a tile of shared-expert rows maps to consecutive tokens
+  int a_rows_valid = 0;                       // rows of the tile whose A offsets are set
   auto set_voff_a = [&](int m0_, int mvalid_) __attribute__((always_inline)) {
+    a_rows_valid = mvalid_;
     const bool lookup = a.gather && m0_ < a.TK;
     const int base = !a.gather ? m0_ : (lookup ? 0 : (m0_ - a.TK) % a.T);
 #pragma unroll
@@ -231,7 +233,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   const uint32_t wave_b = lds_base + uint32_t(w) * (BSTAGE / 4);
   auto dma_a = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
     constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
-    dma16(rsrc_a, voff_a[j], uint32_t(ks + kst0) * ROWB, wave_a + uint32_t(par * ASTAGE + j * 1024));
+    // 8-row groups wholly past the tile's rows are not loaded: their LDS rows keep
+    // stale values, which reach only output rows that are never stored
+    if ((BM / 4) * w + 8 * j < a_rows_valid)
+      dma16(rsrc_a, voff_a[j], uint32_t(ks + kst0) * ROWB, wave_a + uint32_t(par * ASTAGE + j * 1024));
   };
   auto dma_b = [&](int ks, auto par_tag, auto j_tag) __attribute__((always_inline)) {
     constexpr int j = decltype(j_tag)::value, par = decltype(par_tag)::value;
