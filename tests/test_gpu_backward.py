@@ -130,6 +130,11 @@ SMALL = dict(hidden=256, inter=256, E=16, K=4, G=4, M=2, topn=2)
                                        ("decode_bf16", dict(T=400, **{**SMALL, "inter": 128})),
                                        ("decode_bf16", dict(T=50, **{**SMALL, "hidden": 128,
                                                                      "inter": 128})),
+                                       # hidden 384, inter 640: partial last column tiles
+                                       # of the [K][N]-weight GEMMs (dh: N = 640; dX:
+                                       # N = 384, K = 1280 stacked at k_split = 640)
+                                       ("decode_bf16", dict(T=90, **{**SMALL, "hidden": 384,
+                                                                     "inter": 640})),
                                        ("decode_bf16", {})])
 def test_expert_backward_input(name, over):
     """dx of the grouped SwiGLU experts against the oracle on up to 48 sampled tokens (the
@@ -181,6 +186,8 @@ def test_expert_backward_input(name, over):
 @pytest.mark.parametrize("name,over,n_check", [("decode_bf16", dict(T=37, **SMALL), None),
                                                ("decode_bf16", dict(T=29, Ns=2, **SMALL), None),
                                                ("decode_bf16", dict(T=3, **SMALL), None),
+                                               ("decode_bf16", dict(T=90, **{**SMALL, "hidden": 384,
+                                                                             "inter": 640}), None),
                                                ("decode_bf16", {}, 4)])
 def test_expert_backward_weights(name, over, n_check):
     """Weight gradients of every expert (small shapes) or of the shared expert and a few
