@@ -387,8 +387,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     //  R2  step 1; reads of A step 2; DMA B k+2 into B k's buffer (if DB)
     //  R3  step 2; reads of A step 3
     //  R4  first half of step 3; then publish stage k+1 (if PUB; VM loads may stay in flight)
+    // VM < 0: the bound is chosen at run time (NDB when this stage's B loads went out,
+    // else 0); with DB, the B loads of stage kb go out only when db_rt holds
     auto stage = [&](int k, auto par_tag, auto prev_tag, auto da_tag, auto db_tag, auto pub_tag,
-                     auto vm_tag) __attribute__((always_inline)) {
+                     auto vm_tag, int kb, bool db_rt) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par_tag)::value;
       constexpr bool PREV = decltype(prev_tag)::value, DA = decltype(da_tag)::value;
       constexpr bool DB = decltype(db_tag)::value, PUB = decltype(pub_tag)::value;
@@ -414,7 +416,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
           [&](auto m) __attribute__((always_inline)) { mfma_of(S0{}, m, std::bool_constant<!PREV>{}); }, rd1, none);
       stage_barrier();                          // every wave holds its B k fragments
       auto rd2 = [&](auto q_tag) __attribute__((always_inline)) { read_a(P{}, S2{}, q_tag); };
-      auto dma_b2 = [&](auto j_tag) __attribute__((always_inline)) { dma_b(k + 2, P{}, j_tag); };
+      // B stage kb (k + 2, or a stage of the next tile) into the buffer stage k leaves
+      auto dma_b2 = [&](auto j_tag) __attribute__((always_inline)) {
+        if (db_rt) dma_b(kb, P{}, j_tag);
+      };
       interleave<0, NMS, NA, DB ? NDB : 0>(
           [&](auto m) __attribute__((always_inline)) { mfma_of(S1{}, m, F_{}); }, rd2, dma_b2);
       auto rd3 = [&](auto q_tag) __attribute__((always_inline)) { read_a(P{}, S3{}, q_tag); };
@@ -423,7 +428,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       interleave<0, NMS / 2, 0, 0>(
           [&](auto m) __attribute__((always_inline)) { mfma_of(S3{}, m, F_{}); }, none, none);
       if constexpr (PUB) {
-        wait_vmcnt<VM>();
+        if constexpr (VM >= 0) {
+          wait_vmcnt<VM>();
+        } else {
+          if (db_rt) wait_vmcnt<NDB>();
+          else wait_vmcnt<0>();
+        }
         stage_barrier();
       }
     };
@@ -437,23 +447,37 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
     wait_vmcnt<0>();
     stage_barrier();
     i32x4_t next_e{};
+    bool b_early = false;                    // the next tile's B 0 and B 1 already went out
     if constexpr (PERSIST) {
       if (has_next) next_e = __builtin_amdgcn_raw_buffer_load_b128(rsrc_sched, uint32_t(pos2) * 16u, 0, 0);
     }
     // nk = K / 64 is even (K is a multiple of 128)
     auto two_stages = [&]() __attribute__((always_inline)) {
-      stage(0, P0{}, F_{}, T_{}, F_{}, T_{}, V0{});
-      stage(1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{});
+      stage(0, P0{}, F_{}, T_{}, F_{}, T_{}, V0{}, 2, false);
+      stage(1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{}, 3, false);
     };
     auto k_loop = [&]() __attribute__((always_inline)) {
-      stage(0, P0{}, F_{}, T_{}, T_{}, T_{}, VB{});
-      stage(1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{});
+      stage(0, P0{}, F_{}, T_{}, T_{}, T_{}, VB{}, 2, true);
+      stage(1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{}, 3, true);
       for (int k = 2; k < nk - 2; k += 2) {
-        stage(k, P0{}, T_{}, T_{}, T_{}, T_{}, VB{});
-        stage(k + 1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{});
+        stage(k, P0{}, T_{}, T_{}, T_{}, T_{}, VB{}, k + 2, true);
+        stage(k + 1, P1{}, T_{}, T_{}, T_{}, T_{}, VB{}, k + 3, true);
       }
-      stage(nk - 2, P0{}, T_{}, T_{}, F_{}, T_{}, V0{});
-      stage(nk - 1, P1{}, T_{}, F_{}, F_{}, F_{}, V0{});
+      // the next tile's B 0 and B 1 go out in the last two stages, into the buffers
+      // those stages free (nk is even: the same parities), so their HBM latency hides
+      // behind this tile's last MFMAs and epilogue; stage nk - 2 then publishes stage
+      // nk - 1 with the next tile's B 0 still in flight
+      if (PERSIST && has_next) {
+        g2 = __builtin_amdgcn_readfirstlane(next_e[0]);
+        m02 = __builtin_amdgcn_readfirstlane(next_e[1]);
+        mv2 = __builtin_amdgcn_readfirstlane(next_e[2]);
+        rsrc_b = rsrc_b_of(g2, nt2);
+        if constexpr (kKN) rsrc_b1 = rsrc_b1_of(g2, nt2);
+        b_early = true;
+      }
+      using VR = std::integral_constant<int, -1>;
+      stage(nk - 2, P0{}, T_{}, T_{}, T_{}, T_{}, VR{}, 0, b_early);
+      stage(nk - 1, P1{}, T_{}, F_{}, T_{}, F_{}, V0{}, 1, b_early);
     };
     if constexpr (SHORT_K) {
       two_stages();
@@ -494,10 +518,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
       });
     } else {
       stage_barrier();                          // every wave is done with this tile's LDS
-      // the next tile's B 0 and B 1 now (their HBM latency hides behind the epilogue);
+      // the next tile's B 0 and B 1 now unless the last two stages sent them (K = 128);
       // its A 0 after the epilogue, which stages through A buffer 1
       if constexpr (PERSIST) {
-        if (has_next) {
+        if (has_next && !b_early) {
           g2 = __builtin_amdgcn_readfirstlane(next_e[0]);
           m02 = __builtin_amdgcn_readfirstlane(next_e[1]);
           mv2 = __builtin_amdgcn_readfirstlane(next_e[2]);
