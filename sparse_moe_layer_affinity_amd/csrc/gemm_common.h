@@ -119,33 +119,36 @@ namespace moe {
 // to bf16, then quantised per token over the tile's 128 h columns -- one 1x128 block
 // ("DeepSeek-V3 ... 技术解析" (devpress), section 2) -- with the arithmetic of
 // act_quant_e4m3: scale amax / 448 (pow2: the smallest power of two s >= 2^-126 with
-// amax <= 448 s), code = RNE-saturate(h / scale).  Each wave holds 64 of the 128
-// columns (wn = w & 1 picks the half).  Pass 1 reads each accumulator once, writes the
-// bf16 h to the wave's LDS staging area (stage: 8 waves x 80 tokens x 64 columns,
-// 80 KB; the caller's operand buffers, free once every wave has passed the barrier at
-// the start) and its per-token amax to amax_lds (8 x 80 floats); after a second
-// workgroup barrier pass 2 combines the two halves' amax and quantises from LDS.
-// Every wave of the workgroup calls this (two barriers).  Codes go to hq [rows][ldq]
-// (4 bytes per lane and block), scales to hs [ldq / 128][scale_rows] at block n0 / 128.
-template <int NJB, class Acc>
+// amax <= 448 s), code = RNE-saturate(h / scale).  The 8 waves are WN column groups
+// (wn = w % WN) by 8 / WN token groups of 80 (wt = w / WN); each wave holds NIB 16-wide
+// blocks of h columns: gate accumulators acc[ib], up accumulators acc[ib + NIB].
+// Pass 1 reads each accumulator once, writes the bf16 h to the wave's LDS staging area
+// (8 waves x 80 tokens x 16 NIB columns, NIB x 10 KB; the caller's operand buffers, free
+// once every wave has passed the barrier at the start) and its per-token amax to
+// amax_lds (8 x 80 floats); after a second workgroup barrier pass 2 combines the WN
+// column groups' amax and quantises from LDS.  Every wave of the workgroup calls this
+// (two barriers).  Codes go to hq [rows][ldq] (4 bytes per lane and block), scales to
+// hs [ldq / 128][scale_rows] at block n0 / 128.
+template <int NJB, int WN, int NIB, class Acc>
 __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l, int m0,
                                                     int mvalid, int n0, uint8_t* hq, int ldq,
                                                     float* hs, int scale_rows, float* amax_lds,
                                                     uint32_t* stage, bool pow2) {
-  const int wn = w & 1, wt = w >> 1;
+  static_assert(WN * NIB * 16 == 128, "a tile holds one 128-wide block of h");
+  const int wn = w % WN, wt = w / WN;
   // staging: wave w, token block jb, block ib: 64 lanes x 2 dwords (lane l's four bf16)
-  uint2* st = reinterpret_cast<uint2*>(stage) + size_t(w) * (5 * 4 * 64);
+  uint2* st = reinterpret_cast<uint2*>(stage) + size_t(w) * (5 * NIB * 64);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // operand buffers free
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
     float a = 0.f;
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
+    for (int ib = 0; ib < NIB; ++ib) {
       float hv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q];
+      for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + NIB][jb][q];
       const uint32_t lo = pack_bf16x2(hv[0], hv[1]), hi = pack_bf16x2(hv[2], hv[3]);
-      st[(jb * 4 + ib) * 64 + l] = make_uint2(lo, hi);
+      st[(jb * NIB + ib) * 64 + l] = make_uint2(lo, hi);
       a = fmaxf(a, fmaxf(fmaxf(fabsf(bf16_bits_to_f32(lo & 0xffffu)), fabsf(bf16_bits_to_f32(lo >> 16))),
                          fmaxf(fabsf(bf16_bits_to_f32(hi & 0xffffu)), fabsf(bf16_bits_to_f32(hi >> 16)))));
     }
@@ -157,7 +160,9 @@ __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
     const int tk = jb * 16 + (l & 15);
-    const float a = fmaxf(amax_lds[w * 80 + tk], amax_lds[(w ^ 1) * 80 + tk]);
+    float a = amax_lds[(wt * WN) * 80 + tk];
+#pragma unroll
+    for (int i = 1; i < WN; ++i) a = fmaxf(a, amax_lds[(wt * WN + i) * 80 + tk]);
     float s = 1.0f;
     if (a > 0.f) {
       if (pow2) {
@@ -173,11 +178,11 @@ __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l
     uint8_t* qrow = hq + size_t(m0 + rl) * ldq;
     const float rs = 1.0f / s;                           // exact for a power of two
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      const uint2 hb = st[(jb * 4 + ib) * 64 + l];
+    for (int ib = 0; ib < NIB; ++ib) {
+      const uint2 hb = st[(jb * NIB + ib) * 64 + l];
       const float v[4] = {bf16_bits_to_f32(hb.x & 0xffffu), bf16_bits_to_f32(hb.x >> 16),
                           bf16_bits_to_f32(hb.y & 0xffffu), bf16_bits_to_f32(hb.y >> 16)};
-      const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
+      const int col = n0 + wn * (16 * NIB) + ib * 16 + 4 * (l >> 4);
       uint32_t c = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q)

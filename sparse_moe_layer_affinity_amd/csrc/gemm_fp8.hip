@@ -16,16 +16,20 @@
 // VGPRs (the VALU adds into them), and this file is compiled with MFMA results in
 // VGPRs as well, so no copies out of AGPRs.
 //
-// Tile: 128 weight rows (GEMM1: 64 gate rows over the matching 64 up rows) x 320 tokens
-// (an expert's whole row block, as in the bf16 kernel, so its weights stream from HBM
-// once), 8 waves (two per SIMD: one wave's rescale FMAs run while the other's MFMAs hold
-// the matrix core), each 64 weight rows x 80 tokens = 4 x 5 MFMA blocks.  K advances one
+// Tiles.  GEMM2 (plain): 128 weight rows x 320 tokens (an expert's whole row block, as
+// in the bf16 kernel, so its weights stream from HBM once), 8 waves (two per SIMD: one
+// wave's rescale FMAs run while the other's MFMAs hold the matrix core) of 64 weight
+// rows x 80 tokens = 4 x 5 MFMA blocks.  GEMM1 (gated): 256 weight rows (128 gate rows
+// over the matching 128 up rows) x 160 tokens, the same 64 x 80 per wave: a tile holds
+// 128 h columns, one whole 1x128 block, so h is quantised to e4m3 in its epilogue; a row
+// block of more than 160 rows is split evenly between two tiles in adjacent slots of
+// one XCD, which stay in step over the same weight tiles in L2.  K advances one
 // 128-byte scale block per stage.  Operands and scales go global -> LDS with buffer
-// loads in LDS mode.  Weights (streamed from HBM) cycle through three 16 KB stage
-// buffers, two stages ahead; tokens (mostly L2 hits) and scales through two, one and a
-// half stages ahead, and from there into one of two register sets one stage ahead, so
-// their LDS reads overlap the MFMAs.  Row blocks come from the same largest-first XCD
-// schedule as the bf16 kernel.
+// loads in LDS mode.  Weights (streamed from HBM) cycle through three stage buffers, two
+// stages ahead; tokens (mostly L2 hits) and scales through two, one and a half stages
+// ahead, and from there into one of two register sets one stage ahead, so their LDS
+// reads overlap the MFMAs.  Row blocks come from the same largest-first XCD schedule as
+// the bf16 kernel.
 #include "gemm_common.h"
 
 namespace moe {
@@ -33,108 +37,137 @@ namespace moe {
 
 template <int MODE>
 __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
-  constexpr int BW = 128, BT = kFp8BT, ROWB = 128;
-  constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // 16 KB, 40 KB
+  constexpr bool GATED = MODE == kGatedBf16;
+  // gated: 256 weight rows (128 gate over the matching 128 up rows: 128 h columns, one
+  // 1x128 block of h) x 160 tokens (half a row block); plain: 128 weight rows x 320
+  constexpr int BW = GATED ? 256 : 128, BT = GATED ? kFp8BT / 2 : kFp8BT, ROWB = 128;
+  constexpr int WSTAGE = BW * ROWB, TSTAGE = BT * ROWB;   // gated 32 KB, 20 KB; plain 16, 40
   constexpr int SW = 3;                                   // weight stage buffers
-  constexpr int NTB = BT / 64;                            // 16-token blocks per wave: 5
+  constexpr int NTB = 5;                                  // 16-token blocks per wave (80 tokens)
+  constexpr int WN = GATED ? 4 : 2;                       // waves along the weight rows
+  constexpr int NWL = BW / 64;                            // weight loads (8 rows each) per wave
+  constexpr int NTL = GATED ? 3 : 5;                      // token loads per wave
+  constexpr int NSA = (BT + 63) / 64;                     // waves loading the token scales
   // LDS: the two token buffers, the weight ring, the two token-scale and the two
-  // weight-scale buffers (waves 5..7 write 256 bytes each, wave 7's are a dummy)
+  // weight-scale buffers (waves NSA.. write 256 bytes each, those past the weight
+  // scales a dummy); gated: the dummy token loads of waves 4..7 and the epilogue's amax
+  // exchange
   constexpr uint32_t kTOff = 0;
   constexpr uint32_t kWOff = 2 * TSTAGE;
   constexpr uint32_t kSaOff = kWOff + SW * WSTAGE;
-  constexpr uint32_t kSaStage = 4 * BT;                   // 1280 B
+  constexpr uint32_t kSaStage = 256 * NSA;
   constexpr uint32_t kSwOff = kSaOff + 2 * kSaStage;
-  constexpr uint32_t kSwStage = 768;
-  constexpr int BN_OUT = MODE == kGatedBf16 ? BW / 2 : BW;
-  __shared__ __attribute__((aligned(1024))) uint4 lds[(kSwOff + 2 * kSwStage) / 16];
+  constexpr uint32_t kSwStage = 256 * (8 - NSA);
+  constexpr uint32_t kDumOff = kSwOff + 2 * kSwStage;
+  constexpr uint32_t kAmOff = kDumOff + (GATED ? 1024 : 0);
+  constexpr uint32_t kLdsBytes = kAmOff + (GATED ? 8 * 80 * 4 : 0);
+  constexpr int BN_OUT = GATED ? BW / 2 : BW;             // output columns: 128
+  __shared__ __attribute__((aligned(1024))) uint4 lds[kLdsBytes / 16];
 
   // ---- tile decode: row blocks dealt to the XCDs in snake order, a block's n-tiles
-  // consecutive on one XCD (see the bf16 expert GEMM) ------------------------------
+  // consecutive on one XCD (see the bf16 expert GEMM); gated: the two halves of a
+  // block's n-tile in adjacent slots of one XCD, so they share its weight tiles in L2 --
   const int b = blockIdx.x;
-  const int xcd = b % kXcds, slot = b / kXcds;
+  const int xcd = b % kXcds, slot0 = b / kXcds;
+  const int half = GATED ? (slot0 & 1) : 0;
+  const int slot = GATED ? (slot0 >> 1) : slot0;
   const int round = slot / a.n_tiles, nt = slot % a.n_tiles;
   const int pos = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
   if (pos >= *a.sched_n) return;
   const int4 blk = a.sched[pos];
-  const int g = blk.x, m0 = blk.y, mvalid = blk.z;
+  // gated: a block of more than 160 rows splits evenly (the first half rounded up to 16
+  // rows), so the two halves do the same MFMA work and stay in step over the weights
+  const int rows0 = GATED && blk.z > BT ? (((blk.z + 1) / 2 + 15) & ~15) : blk.z;
+  const int g = blk.x, m0 = blk.y + half * rows0, mvalid = half ? blk.z - rows0 : rows0;
+  if (mvalid <= 0) return;
   const int n0 = nt * BN_OUT;
   const int tid = threadIdx.x;
   const int K = a.K, KBLK = a.K / 128;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
 
-  // ---- this wave's share of every stage: weight rows 16 w .., token rows 40 w .. ----
+  // ---- this wave's share of every stage: weight rows 8 NWL w .., tokens ------------
   // A tile row lies in the tile's base for every load of this wave, so the lane offsets
-  // are per-wave constants.  Gated: stage rows 0..63 are gate rows n0.., 64..127 the
+  // are per-wave constants.  Gated: stage rows 0..127 are gate rows n0.., 128..255 the
   // matching up rows.
-  const bool up = MODE == kGatedBf16 && w >= 4;
-  const int wrow0 = MODE == kGatedBf16 ? n0 + 16 * (w & 3) : n0 + 16 * w;
+  const bool up = GATED && w >= 4;
+  const int wrow0 = GATED ? n0 + 32 * (w & 3) : n0 + 16 * w;
   const __amdgpu_buffer_rsrc_t rsrc_w =
       make_rsrc((up ? a.B1 : a.B0) + size_t(g) * a.b_stride, uint32_t(a.N) * uint32_t(K));
   const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(a.A, uint32_t(a.a_rows) * uint32_t(K));
-  uint32_t voff_w[2], voff_t[NTB];
+  uint32_t voff_w[NWL], voff_t[NTL];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    // stage row 16 w + 8 j + (l >> 3): bit 3 of the row is j
-    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ j) * 16u;
+  for (int j = 0; j < NWL; ++j) {
+    // stage row 8 NWL w + 8 j + (l >> 3): bit 3 of the row is j & 1 (NWL is even)
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (j & 1)) * 16u;
     voff_w[j] = uint32_t(wrow0 + 8 * j + (l >> 3)) * uint32_t(K) + chunk;   // rows >= N read zero
   }
   // shared-expert tiles map rows to consecutive tokens; routed rows gather
   const bool lookup = a.gather && m0 < a.TK;
   const int tbase = !a.gather ? m0 : (lookup ? 0 : (m0 - a.TK) % a.T);
   auto src_of = [&](int row) { return lookup ? a.row_token[m0 + row] : tbase + row; };
+  // plain: wave w loads stage rows 40 w + 8 j (j < 5); gated: 8-row group 8 j + w (rows
+  // 8 (8 j + w) ..), of which waves 4..7 have no third (their third load is a dummy,
+  // every lane out of range, so the load counts stay uniform)
+  auto trow_of = [&](int j) { return GATED ? 8 * (8 * j + w) + (l >> 3) : 40 * w + 8 * j + (l >> 3); };
 #pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    // stage row 40 w + 8 j + (l >> 3): bit 3 of the row is (5 w + j) & 1
-    const int trow = 40 * w + 8 * j + (l >> 3);
-    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ ((5 * w + j) & 1)) * 16u;
-    voff_t[j] = trow < mvalid ? uint32_t(src_of(trow)) * uint32_t(K) + chunk : kOob;
+  for (int j = 0; j < NTL; ++j) {
+    const int trow = trow_of(j);
+    const int grp = GATED ? 8 * j + w : 5 * w + j;       // bit 3 of the row
+    const uint32_t chunk = uint32_t((l & 7) ^ (l >> 3) ^ (grp & 1)) * 16u;
+    const bool real = !GATED || j < 2 || w < 4;
+    voff_t[j] = real && trow < mvalid ? uint32_t(src_of(trow)) * uint32_t(K) + chunk : kOob;
   }
-  // one scale load per wave per stage: waves 0..4 the token scales of tokens
-  // 64 w + lane, waves 5 and 6 one weight block scale each (lane 0; gated: gate and up,
-  // plain: the tile's block and nothing), wave 7 nothing useful (every lane out of range;
-  // the load counts stay uniform)
+  // one scale load per wave per stage: waves 0..NSA-1 the token scales of tokens
+  // 64 w + lane, the next two one weight block scale each (lane 0; gated: gate and up,
+  // plain: the tile's block and nothing), the rest nothing useful (every lane out of
+  // range; the load counts stay uniform)
   __amdgpu_buffer_rsrc_t rsrc_s;
   uint32_t voff_s = kOob;
-  if (w < 5) {
+  if (w < NSA) {
     rsrc_s = make_rsrc(a.a_scales, uint32_t(a.scale_rows) * KBLK * 4u);
     const int row = 64 * w + l;
     if (row < mvalid) voff_s = uint32_t(m0 + row) * 4u;
   } else {
-    const bool sup = MODE == kGatedBf16 && w == 6;
+    const bool sup = GATED && w == NSA + 1;
     rsrc_s = make_rsrc((sup ? a.S1 : a.S0) + size_t(g) * a.s_stride, uint32_t(a.s_stride) * 4u);
-    if (l == 0 && (w == 5 || sup)) voff_s = uint32_t((n0 / 128) * KBLK) * 4u;
+    if (l == 0 && (w == NSA || sup)) voff_s = uint32_t((n0 / 128) * KBLK) * 4u;
   }
   // K block ks of the scales: token scales [K/128, scale_rows], weight scales [.., K/128]
-  const uint32_t s_step = w < 5 ? uint32_t(a.scale_rows) * 4u : 4u;
+  const uint32_t s_step = w < NSA ? uint32_t(a.scale_rows) * 4u : 4u;
   const uint32_t lds_base = uint32_t(uintptr_t(&lds[0]));
   const uint32_t wave_w = lds_base + kWOff + uint32_t(w) * (WSTAGE / 8);
-  const uint32_t wave_t = lds_base + kTOff + uint32_t(w) * (TSTAGE / 8);
-  const uint32_t wave_s = lds_base + (w < 5 ? kSaOff + 256u * w : kSwOff + 256u * (w - 5));
-  const uint32_t s_par = w < 5 ? kSaStage : kSwStage;
+  const uint32_t wave_s = lds_base + (w < NSA ? kSaOff + 256u * w : kSwOff + 256u * (w - NSA));
+  const uint32_t s_par = w < NSA ? kSaStage : kSwStage;
+  // LDS byte of token load j in buffer 0 (gated dummies: one shared area, no parity)
+  auto tdst = [&](int j) -> uint32_t {
+    if (GATED) return j == 2 && w >= 4 ? lds_base + kDumOff : lds_base + kTOff + uint32_t(8 * j + w) * 1024u;
+    return lds_base + kTOff + uint32_t(w) * (TSTAGE / 8) + uint32_t(j) * 1024u;
+  };
+  auto tpar = [&](int j) -> uint32_t { return GATED && j == 2 && w >= 4 ? 0u : uint32_t(TSTAGE); };
 
   auto load_w = [&](int ks) __attribute__((always_inline)) {
     const uint32_t dst = wave_w + uint32_t(ks % SW) * WSTAGE;
-    dma16(rsrc_w, voff_w[0], uint32_t(ks) * ROWB, dst);
-    dma16(rsrc_w, voff_w[1], uint32_t(ks) * ROWB, dst + 1024u);
+#pragma unroll
+    for (int j = 0; j < NWL; ++j) dma16(rsrc_w, voff_w[j], uint32_t(ks) * ROWB, dst + uint32_t(j) * 1024u);
   };
-  // token rows of stage ks and its scales, into buffer ks & 1 (NTB + 1 loads)
+  // token rows of stage ks and its scales, into buffer ks & 1 (NTL + 1 loads)
   auto load_t = [&](int ks) __attribute__((always_inline)) {
     const uint32_t par = uint32_t(ks & 1);
 #pragma unroll
-    for (int j = 0; j < NTB; ++j)
-      dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, wave_t + par * TSTAGE + j * 1024u);
+    for (int j = 0; j < NTL; ++j)
+      dma16(rsrc_t, voff_t[j], uint32_t(ks) * ROWB, __builtin_amdgcn_readfirstlane(tdst(j) + par * tpar(j)));
     dma4(rsrc_s, voff_s, uint32_t(ks) * s_step, __builtin_amdgcn_readfirstlane(wave_s + par * s_par));
   };
 
-  // ---- wave geometry: 2 (weight rows) x 4 (tokens) --------------------------------
-  const int wn = w & 1, wt = w >> 1;
+  // ---- wave geometry: WN (weight rows) x 8 / WN (tokens, 80 each) -----------------
+  const int wn = w % WN, wt = w / WN;
   // LDS row of this lane in weight block ib (gated: gate blocks 0, 1, up blocks 2, 3)
   // and token block jb, and its two K chunks
   int w_row[4];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
     int r;
-    if (MODE == kGatedBf16) r = ib < 2 ? wn * 32 + ib * 16 : 64 + wn * 32 + (ib - 2) * 16;
+    if (GATED) r = ib < 2 ? wn * 32 + ib * 16 : BW / 2 + wn * 32 + (ib - 2) * 16;
     else r = wn * 64 + ib * 16;
     w_row[ib] = r + (l & 15);
   }
@@ -225,8 +258,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
       constexpr int S = decltype(set_tag)::value;
       using N = std::integral_constant<int, 1 - S>;
       // P_k: pending may stay weights k+1 and tokens k+2
-      if (k + 2 < nk) wait_vmcnt<NTB + 3>();
-      else if (k + 1 < nk) wait_vmcnt<2>();
+      if (k + 2 < nk) wait_vmcnt<NWL + NTL + 1>();
+      else if (k + 1 < nk) wait_vmcnt<NWL>();
       else wait_vmcnt<0>();
       stage_barrier();
       if (k + 2 < nk) load_w(k + 2);
@@ -250,22 +283,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
     }
 
     // ---- epilogue: lane l holds weight rows 4*(l/16)+q of each block, token l%16 ----
+    if constexpr (GATED) {
+      // h quantised to e4m3 per 1x128 block here; staging in the two token buffers
+      fp8_epilogue_hquant<NJB, WN, 2>(acc, w, l, m0, mvalid, n0, a.Q, a.ldc, a.QS, a.scale_rows,
+                                      reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kAmOff),
+                                      reinterpret_cast<uint32_t*>(lds), false);
+    } else {
   #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      const int rl = wt * 80 + jb * 16 + (l & 15);
-      if (rl >= mvalid) continue;
-      uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
-      if (MODE == kGatedBf16) {
-  #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const int col = n0 + wn * 32 + ib * 16 + 4 * (l >> 4);
-          if (col >= a.N) continue;
-          float hv[4];
-  #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 2][jb][q];
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-        }
-      } else {
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int rl = wt * 80 + jb * 16 + (l & 15);
+        if (rl >= mvalid) continue;
+        uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
   #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
           const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
@@ -304,8 +332,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
   err = launch_build_schedule(c, offsets, kFp8BT, ws.sched, ws.sched_n, s);
   if (err != hipSuccess) return err;
   const int rounds = ceil_div(expert_row_blocks_upper(c, kFp8BT), kXcds);
-  // GEMM1: gated; the power-of-two kernel's tiles hold 128 h columns, a whole 1x128
-  // block, and quantise h to e4m3 (codes + scales) in their epilogue
+  // GEMM1: gated; both kernels' tiles hold 128 h columns, a whole 1x128 block, and
+  // quantise h to e4m3 (codes + scales) in their epilogue
   Fp8Args a{};
   a.A = ws.xq;
   a.a_scales = ws.xg_scales;
@@ -333,14 +361,9 @@ hipError_t launch_grouped_ffn_fp8(const moe_config& c, const void* x, const int3
     err = launch_gemm_fp8p2(a, true, rounds * kXcds * a.n_tiles, s);
     if (err != hipSuccess) return err;
   } else {
-    // 128-row tiles (64 h columns): h goes out in bf16 and is quantised by its own pass
-    Fp8Args f = a;
-    f.Q = nullptr;
-    f.QS = nullptr;
-    f.C = static_cast<uint16_t*>(ws.h);
-    f.n_tiles = ceil_div(I, 64);
-    hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * f.n_tiles), dim3(512), 0, s, f);
-    err = launch_act_quant(ws.h, rows, I, ws.hq, ws.h_scales, s, true, false);
+    // 256-weight-row tiles over the two 160-row halves of each block
+    hipLaunchKernelGGL(grouped_gemm_fp8<kGatedBf16>, dim3(rounds * kXcds * a.n_tiles * 2), dim3(512), 0, s, a);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   // GEMM2: plain, on the e4m3 h

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
     if constexpr (MODE == kGatedBf16) {
       if (a.Q) {
         // staging in the two token buffers (80 KB)
-        fp8_epilogue_hquant<NJB>(acc, w, l, m0, mvalid, n0, a.Q, a.ldc, a.QS, a.scale_rows,
+        fp8_epilogue_hquant<NJB, 2, 4>(acc, w, l, m0, mvalid, n0, a.Q, a.ldc, a.QS, a.scale_rows,
                                  reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kAmOff),
                                  reinterpret_cast<uint32_t*>(lds), true);
         return;
