@@ -25,11 +25,11 @@
 // block of more than 160 rows is split evenly between two tiles in adjacent slots of
 // one XCD, which stay in step over the same weight tiles in L2.  K advances one
 // 128-byte scale block per stage.  Operands and scales go global -> LDS with buffer
-// loads in LDS mode.  Weights (streamed from HBM) cycle through three stage buffers, two
-// stages ahead; tokens (mostly L2 hits) and scales through two, one and a half stages
-// ahead, and from there into one of two register sets one stage ahead, so their LDS
-// reads overlap the MFMAs.  Row blocks come from the same largest-first XCD schedule as
-// the bf16 kernel.
+// loads in LDS mode, one workgroup barrier per stage, after which stage k+2's tokens and
+// weights go out.  Weights (streamed from HBM) cycle through three stage buffers; tokens
+// (mostly L2 hits) and scales through two, and from there into one of two register
+// sets a stage early, so their LDS reads overlap the MFMAs.  Row blocks come from the
+// same largest-first XCD schedule as the bf16 kernel.
 #include "gemm_common.h"
 
 namespace moe {
@@ -240,37 +240,36 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
         }
       }
     };
-    // prologue: weights and tokens of stages 0 and 1, stage 0's fragments, tokens 2
-    load_w(0);
+    // prologue: tokens and weights of stages 0 and 1 (in that order), stage 0's token
+    // fragments
     load_t(0);
+    load_w(0);
     if (nk > 1) {
-      load_w(1);
       load_t(1);
+      load_w(1);
+      wait_vmcnt<2 * NWL + NTL + 1>();
+    } else {
+      wait_vmcnt<NWL>();
     }
-    wait_vmcnt<0>();
     stage_barrier();
     read_tokens(std::integral_constant<int, 0>{}, 0);
-    if (nk > 2) {
-      stage_barrier();
-      load_t(2);
-    }
     auto stage = [&](auto set_tag, int k) __attribute__((always_inline)) {
       constexpr int S = decltype(set_tag)::value;
       using N = std::integral_constant<int, 1 - S>;
-      // P_k: pending may stay weights k+1 and tokens k+2
-      if (k + 2 < nk) wait_vmcnt<NWL + NTL + 1>();
-      else if (k + 1 < nk) wait_vmcnt<NWL>();
+      // one barrier per stage: stage k's weights and stage k+1's tokens are in LDS
+      // (only the weights of k+1, issued last, may stay in flight), and every wave is
+      // done with stage k-1 (weights k-1, tokens k read a stage early), whose buffers
+      // take stage k+2's tokens and weights
+      if (k + 1 < nk) wait_vmcnt<NWL>();
       else wait_vmcnt<0>();
       stage_barrier();
-      if (k + 2 < nk) load_w(k + 2);
+      if (k + 2 < nk) {
+        load_t(k + 2);
+        load_w(k + 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (k + 1 < nk) read_tokens(N{}, k + 1);
       block_row(set_tag, k, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k + 3 < nk) {                        // R_k
-        stage_barrier();
-        load_t(k + 3);
-      }
       __builtin_amdgcn_sched_barrier(0);
       block_row(set_tag, k, 1);
       block_row(set_tag, k, 2);
