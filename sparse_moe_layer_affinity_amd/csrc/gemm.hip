@@ -102,12 +102,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint4 lds[(2 * ASTAGE + 2 * BSTAGE) / 16];
 
   // ---- tiles ---------------------------------------------------------------------
-  // Workgroups reach the XCDs round-robin (b % 8).  The row blocks (see build_schedule),
-  // sorted largest first, are dealt to the XCDs in pairs of adjacent blocks in snake
-  // order (round r: XCDs 0..7, then 7..0), so every XCD gets an even share and runs its
-  // largest blocks first; a pair's n-tiles are consecutive slots of one XCD, so they
-  // share its A rows (and, for two blocks of one expert, its weight tiles) through that
-  // XCD's L2.  The expert GEMMs run persistent workgroups (one per CU; gridDim.x
+  // Workgroups reach the XCDs round-robin (b % 8).  The row blocks (see build_schedule:
+  // pairs of one expert's equal blocks, then lone blocks, each largest first) are dealt
+  // to the XCDs in pairs of adjacent blocks in snake order (round r: XCDs 0..7, then
+  // 7..0), so every XCD gets an even share and runs its largest blocks first; a pair's
+  // n-tiles are consecutive slots of one XCD, so the two blocks of one expert stream
+  // each weight tile side by side through that XCD's L2.  The expert GEMMs run persistent workgroups (one per CU; gridDim.x
   // = 8 x nwg): workgroup j of an XCD takes slots j, j + nwg, j + 2 nwg, ... and loads
   // the first stage of its next tile while it writes out the current one.  The
   // fp32-output mode (router logits, router backward) runs one workgroup per tile.
@@ -696,25 +696,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma(GemmArgs a) {
 }
 
 // Schedule of the expert GEMMs, one workgroup (G <= 512).  A group's rows split into
-// blocks of bm rows; the output lists every block as {group, first row, rows}, ordered
-// by row count, largest first (a counting sort over 32-row classes; the order inside a
-// class is arbitrary and changes no result: each block computes the same values
-// wherever it runs), and the number of blocks.
+// c = ceil(rows / bm) blocks of at most bm rows, listed as {group, first row, rows};
+// the output holds every row once, and the number of blocks.  A group gives c / 2
+// pairs of consecutive blocks and, for odd c, a lone last block (the remainder); for
+// even c the last pair splits the rows it covers evenly (the first block rounded up to
+// 32 rows), so the two blocks of every pair do the same work.  The pairs come first,
+// each on two adjacent positions from an even one, then the lone blocks; each kind by
+// row count, largest first (a counting sort over 32-row classes, stable: units of one
+// class keep the order of their groups, so the schedule is the same on every run).
+// The bf16 expert GEMM runs the two blocks of positions 2q and 2q + 1 side by side on
+// one XCD, so a pair streams each of its expert's weight tiles once through that L2.
 __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict__ offsets, int E,
                                                       int Ns, int T, int TK, int bm,
                                                       int4* __restrict__ sched,
                                                       int32_t* __restrict__ sched_n) {
-  constexpr int kClasses = 64;
+  constexpr int kClasses = 64;              // 0..31 pairs, 32..63 lone blocks
   __shared__ int pre[512];
   __shared__ int cls_count[kClasses], cls_next[kClasses];
   const int t = threadIdx.x, G = E + Ns;
-  int c = 0;
+  int u = 0;
   if (t < G) {
     int r0, r1;
     group_rows(offsets, t, E, T, TK, r0, r1);
-    c = ceil_div(r1 - r0, bm);
+    const int c = ceil_div(r1 - r0, bm);
+    u = c / 2 + (c & 1);
   }
-  pre[t] = c;
+  pre[t] = u;
   if (t < kClasses) cls_count[t] = 0;
   __syncthreads();
   for (int d = 1; d < 512; d <<= 1) {
@@ -723,47 +730,70 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     pre[t] += v;
     __syncthreads();
   }
-  const int total = pre[G - 1];
-  if (t == 0) *sched_n = total;
-  // block id -> {group, first row, rows}; its group is the first g with pre[g] > id
-  auto block_of = [&](int id) {
+  const int units = pre[G - 1];
+  // unit id -> its group (the first g with pre[g] > id), first row, the rows of its
+  // first block and of its second (0 for a lone block)
+  struct Unit { int g, m0, rows0, rows1; };
+  auto unit_of = [&](int id) {
     int lo = -1, hi = G - 1;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] > id) hi = mid; else lo = mid;
     }
     const int g = hi;
-    const int first = g > 0 ? pre[g - 1] : 0;
+    const int j = id - (g > 0 ? pre[g - 1] : 0);
     int r0, r1;
     group_rows(offsets, g, E, T, TK, r0, r1);
-    const int m0 = r0 + (id - first) * bm;
-    return make_int4(g, m0, min(bm, r1 - m0), 0);
+    const int c = ceil_div(r1 - r0, bm);
+    Unit un;
+    un.g = g;
+    if (j < c / 2) {
+      un.m0 = r0 + 2 * j * bm;
+      if ((c & 1) || j < c / 2 - 1) {        // two whole blocks
+        un.rows0 = bm;
+        un.rows1 = bm;
+      } else {                                // the last pair: bm < rest <= 2 bm, split
+        const int rest = r1 - un.m0;
+        un.rows0 = min(bm, ((rest + 1) / 2 + 31) & ~31);
+        un.rows1 = rest - un.rows0;
+      }
+    } else {                                  // the remainder of an odd count
+      un.m0 = r0 + (c - 1) * bm;
+      un.rows0 = r1 - un.m0;
+      un.rows1 = 0;
+    }
+    return un;
   };
-  auto cls_of = [&](const int4& blk) { return min(kClasses - 1, (bm - blk.z) >> 5); };
-  for (int id = t; id < total; id += 512) atomicAdd(&cls_count[cls_of(block_of(id))], 1);
+  auto cls_of = [&](const Unit& un) {
+    return un.rows1 > 0 ? min(31, (2 * bm - un.rows0 - un.rows1) >> 5)
+                        : 32 + min(31, (bm - un.rows0) >> 5);
+  };
+  // positions per unit of class k
+  auto width = [](int k) { return k < 32 ? 2 : 1; };
+  for (int id = t; id < units; id += 512) atomicAdd(&cls_count[cls_of(unit_of(id))], 1);
   __syncthreads();
   if (t == 0) {
     int acc = 0;
     for (int k = 0; k < kClasses; ++k) {
       cls_next[k] = acc;
-      acc += cls_count[k];
+      acc += width(k) * cls_count[k];
     }
+    *sched_n = acc;
   }
   __syncthreads();
-  // stable placement (blocks of one class keep their id order, so the schedule is the
-  // same on every run): 512 ids at a time, each block's rank among the same-class
-  // blocks of its wave from ballots, the waves' per-class counts added in wave order
+  // stable placement: 512 units at a time, each unit's rank among the same-class
+  // units of its wave from ballots, the waves' per-class counts added in wave order
   __shared__ int wcount[8][kClasses];
   const int lane = t & 63, wv = t >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int base = 0; base < total; base += 512) {
+  for (int base = 0; base < units; base += 512) {
     const int id = base + t;
-    const bool valid = id < total;
-    int4 blk = make_int4(0, 0, 0, 0);
+    const bool valid = id < units;
+    Unit un{0, 0, 0, 0};
     int cl = -1;
     if (valid) {
-      blk = block_of(id);
-      cl = cls_of(blk);
+      un = unit_of(id);
+      cl = cls_of(un);
     }
     wcount[wv][lane] = 0;                   // kClasses == 64: one entry per lane
     __syncthreads();
@@ -779,15 +809,17 @@ __global__ __launch_bounds__(512) void build_schedule(const int32_t* __restrict_
     }
     __syncthreads();
     if (valid) {
-      int pos = cls_next[cl] + rank;
-      for (int w2 = 0; w2 < wv; ++w2) pos += wcount[w2][cl];
-      sched[pos] = blk;
+      int n = rank;
+      for (int w2 = 0; w2 < wv; ++w2) n += wcount[w2][cl];
+      const int pos = cls_next[cl] + width(cl) * n;
+      sched[pos] = make_int4(un.g, un.m0, un.rows0, 0);
+      if (un.rows1 > 0) sched[pos + 1] = make_int4(un.g, un.m0 + un.rows0, un.rows1, 0);
     }
     __syncthreads();
     if (t < kClasses) {
       int n = 0;
       for (int w2 = 0; w2 < 8; ++w2) n += wcount[w2][t];
-      cls_next[t] += n;
+      cls_next[t] += width(t) * n;
     }
     __syncthreads();
   }
