@@ -33,7 +33,8 @@ Workspace workspace_layout(const moe_config& c, void* base) {
   w.row_token = static_cast<int32_t*>(take(TK * 4));
   w.pair_row = static_cast<int32_t*>(take(TK * 4));
   w.sched_n = static_cast<int32_t*>(take(4));
-  w.sched = static_cast<int4*>(take(size_t(expert_row_blocks_upper(c, kFp8BT)) * 16));
+  // room for the smallest row blocks any expert GEMM schedules (256 rows)
+  w.sched = static_cast<int4*>(take(size_t(expert_row_blocks_upper(c, kFp8BT32)) * 16));
   w.h = take(rows * I * act_bytes(c));
   w.hq = fp8 ? static_cast<uint8_t*>(take(rows * I)) : nullptr;
   w.h_scales = fp8 ? static_cast<float*>(take(rows * (I / 128) * 4)) : nullptr;

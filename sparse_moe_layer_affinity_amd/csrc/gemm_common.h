@@ -123,13 +123,13 @@ namespace moe {
 // (wn = w % WN) by 8 / WN token groups of 80 (wt = w / WN); each wave holds NIB 16-wide
 // blocks of h columns: gate accumulators acc[ib], up accumulators acc[ib + NIB].
 // Pass 1 reads each accumulator once, writes the bf16 h to the wave's LDS staging area
-// (8 waves x 80 tokens x 16 NIB columns, NIB x 10 KB; the caller's operand buffers, free
-// once every wave has passed the barrier at the start) and its per-token amax to
-// amax_lds (8 x 80 floats); after a second workgroup barrier pass 2 combines the WN
+// (8 waves x TPW tokens x 16 NIB columns, NIB x TPW / 8 KB; the caller's operand
+// buffers, free once every wave has passed the barrier at the start) and its per-token
+// amax to amax_lds (8 x TPW floats); after a second workgroup barrier pass 2 combines the WN
 // column groups' amax and quantises from LDS.  Every wave of the workgroup calls this
 // (two barriers).  Codes go to hq [rows][ldq] (4 bytes per lane and block), scales to
 // hs [ldq / 128][scale_rows] at block n0 / 128.
-template <int NJB, int WN, int NIB, class Acc>
+template <int NJB, int WN, int NIB, int TPW = 80, class Acc>
 __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l, int m0,
                                                     int mvalid, int n0, uint8_t* hq, int ldq,
                                                     float* hs, int scale_rows, float* amax_lds,
@@ -137,7 +137,7 @@ __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l
   static_assert(WN * NIB * 16 == 128, "a tile holds one 128-wide block of h");
   const int wn = w % WN, wt = w / WN;
   // staging: wave w, token block jb, block ib: 64 lanes x 2 dwords (lane l's four bf16)
-  uint2* st = reinterpret_cast<uint2*>(stage) + size_t(w) * (5 * NIB * 64);
+  uint2* st = reinterpret_cast<uint2*>(stage) + size_t(w) * ((TPW / 16) * NIB * 64);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // operand buffers free
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
@@ -154,15 +154,15 @@ __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l
     }
     a = fmaxf(a, __shfl_xor(a, 16));
     a = fmaxf(a, __shfl_xor(a, 32));
-    if ((l >> 4) == 0) amax_lds[w * 80 + jb * 16 + (l & 15)] = a;
+    if ((l >> 4) == 0) amax_lds[w * TPW + jb * 16 + (l & 15)] = a;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
     const int tk = jb * 16 + (l & 15);
-    float a = amax_lds[(wt * WN) * 80 + tk];
+    float a = amax_lds[(wt * WN) * TPW + tk];
 #pragma unroll
-    for (int i = 1; i < WN; ++i) a = fmaxf(a, amax_lds[(wt * WN + i) * 80 + tk]);
+    for (int i = 1; i < WN; ++i) a = fmaxf(a, amax_lds[(wt * WN + i) * TPW + tk]);
     float s = 1.0f;
     if (a > 0.f) {
       if (pow2) {
@@ -173,7 +173,7 @@ __device__ __forceinline__ void fp8_epilogue_hquant(const Acc& acc, int w, int l
         s = __fdiv_rn(a, 448.0f);
       }
     }
-    const int rl = wt * 80 + tk;
+    const int rl = wt * TPW + tk;
     if (rl >= mvalid) continue;
     uint8_t* qrow = hq + size_t(m0 + rl) * ldq;
     const float rs = 1.0f / s;                           // exact for a power of two

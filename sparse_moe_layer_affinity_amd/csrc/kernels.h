@@ -59,7 +59,8 @@ inline bool is_fp8(moe_dtype d) { return d == MOE_E4M3 || d == MOE_E4M3_POW2; }
 
 constexpr int kTokChunk = 64;   // tokens per permute chunk (one 64-bit mask)
 constexpr int kExpertBM = 320;  // rows per row block of the bf16 expert GEMMs
-constexpr int kFp8BT = 320;     // rows per row block of the FP8 expert GEMMs (<= kExpertBM)
+constexpr int kFp8BT = 320;     // rows per row block of the power-of-two FP8 expert GEMMs (<= kExpertBM)
+constexpr int kFp8BT32 = 256;   // rows per row block of the fp32-scale FP8 expert GEMMs
 
 // Upper bound on the row blocks (m-tiles of bm rows) over all groups: every routed
 // expert may end in a partial block, the shared experts have T rows each.
