@@ -180,6 +180,39 @@ def calibration_leg(stream):
     return res
 
 
+def library_leg(cfg, stream, reps: int = 5):
+    """The vendor library on the expert GEMMs' shapes, for comparison only (not on the
+    layer's path): batched bf16 GEMMs through torch.bmm (hipBLASLt / rocBLAS) over E
+    experts of ceil(T (K + Ns) / E) rows each, with E distinct weight matrices streamed
+    from HBM as in the grouped GEMM: GEMM1 [rows, h] x [h, 2 inter] (gate and up
+    together, no SwiGLU) and GEMM2 [rows, inter] x [inter, h]; row-major operands,
+    both contiguous.  No gather, no SwiGLU, no ragged rows: an easier problem than the
+    grouped FFN's.  Timed between HIP events, ``reps`` calls after one warm-up."""
+    import torch
+    E, H, I = cfg.E, cfg.hidden, cfg.inter
+    m = -(-cfg.T * (cfg.K + cfg.Ns) // E)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    res = {"batch": E, "rows_per_expert": m}
+    for name, k, n in (("gemm1", H, 2 * I), ("gemm2", I, H)):
+        a = (torch.randn((E, m, k), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+        b = (torch.randn((E, k, n), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        out = torch.empty((E, m, n), dtype=torch.bfloat16, device="cuda")
+        torch.bmm(a, b, out=out)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            torch.bmm(a, b, out=out)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        flops = 2.0 * E * m * k * n
+        res[name + "_ms"] = round(ms, 4)
+        res[name + "_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        del a, b, out
+    return res
+
+
 def balance_loss_leg(moe, cfg, c, d, idx, ws, stream, reps: int = 20):
     """Time the training-side extras outside the layer step: moe_router_scores and
     moe_balance_loss (two sequences of T/2 tokens, with f, P and the logit gradient),
@@ -495,6 +528,8 @@ def main():
 
     if not args.no_extras:
         cal = calibration_leg(stream)
+        if cfg.act == "bf16" and cfg.w == "bf16":
+            cal["library_bmm_bf16"] = library_leg(cfg, stream)
         result["calibration"] = cal
         measured = cal["hbm_read_GBps"] if hbm_bound else cal[
             "mfma_e4m3_TFLOPs" if workloads.is_fp8(cfg.w) else "mfma_bf16_TFLOPs"]
