@@ -1,8 +1,10 @@
 """Row-block edges of the expert GEMMs, driven through moe_grouped_ffn with prescribed
 per-expert row counts (the grouped rows of every expert compared with the oracle).
 
-bf16 rows are blocked by 320 (the extra strips start at rows 256 and 288 of a block),
-FP8 rows by 256; the counts straddle every edge: empty experts, 1 row, 32/33, 255..257,
+bf16 and power-of-two FP8 rows are blocked by 320 (the bf16 extra strips start at rows
+256 and 288 of a block), fp32-scale FP8 rows by 256 (an expert over 256 rows as a pair of
+blocks, the last pair split evenly); the counts straddle every edge: empty experts, 1
+row, 32/33, 255..257,
 288/289, 320/321, 512/513, 640, and a shared expert of several blocks.  hidden and
 inter of 128 take the one- and two-stage K loops.
 """
