@@ -255,18 +255,33 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8(Fp8Args a) {
                                          reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kAmOff),
                                          reinterpret_cast<uint32_t*>(lds), false);
     } else {
+      // bf16 rows through LDS: each wave stages its 64 tokens x 128 columns (16 KB, in
+      // the operand buffers, free once every wave is past the barrier) as rows of 256
+      // bytes, 16-byte chunk c of row r in slot c ^ (r & 15), then stores whole 16-byte
+      // chunks of four rows per instruction (a row's 256 bytes contiguous)
+      stage_barrier();
+      char* const stg = reinterpret_cast<char*>(lds) + w * 16384;
   #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
-        const int rl = wt * 64 + jb * 16 + (l & 15);
-        if (rl >= mvalid) continue;
-        uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
+        const int r = jb * 16 + (l & 15);
   #pragma unroll
         for (int ib = 0; ib < 8; ++ib) {
-          const int col = n0 + wn * 128 + ib * 16 + 4 * (l >> 4);
-          if (col >= a.N) continue;
+          const int cc = 2 * ib + (l >> 5);                // 16-byte chunk of the row
           const f32x4_t& v = acc[ib][jb];
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(stg + r * 256 + ((cc ^ (r & 15)) << 4) + ((l >> 4) & 1) * 8) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int cc = l & 15;
+      const int col = n0 + wn * 128 + cc * 8;
+  #pragma unroll
+      for (int r0 = 0; r0 < 16 * NJB; r0 += 4) {
+        const int r = r0 + (l >> 4);
+        const int rl = wt * 64 + r;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((cc ^ (r & 15)) << 4));
+        if (rl < mvalid && col < a.N)
+          *reinterpret_cast<uint4*>(a.C + size_t(m0 + rl) * a.ldc + col) = v;
       }
     }
   };

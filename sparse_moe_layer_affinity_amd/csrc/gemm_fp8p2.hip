@@ -260,12 +260,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
         return;
       }
     }
+    if constexpr (MODE == kGatedBf16) {
   #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      const int rl = wt * 80 + jb * 16 + (l & 15);
-      if (rl >= mvalid) continue;
-      uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
-      if (MODE == kGatedBf16) {
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int rl = wt * 80 + jb * 16 + (l & 15);
+        if (rl >= mvalid) continue;
+        uint16_t* crow = a.C + size_t(m0 + rl) * a.ldc;
   #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
           const int col = n0 + wn * 64 + ib * 16 + 4 * (l >> 4);
@@ -275,15 +275,43 @@ __global__ __launch_bounds__(512) void grouped_gemm_fp8p2(Fp8Args a) {
           for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[ib][jb][q]) * acc[ib + 4][jb][q];
           *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
-      } else {
-  #pragma unroll
-        for (int ib = 0; ib < 8; ++ib) {
-          const int col = n0 + wn * 128 + ib * 16 + 4 * (l >> 4);
-          if (col >= a.N) continue;
-          const f32x4_t& v = acc[ib][jb];
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
       }
+    } else {
+      // bf16 rows through LDS: each wave stages up to 64 of its tokens x 128 columns
+      // (16 KB, in the operand buffers, free once every wave is past the barrier) as rows
+      // of 256 bytes, 16-byte chunk c of row r in slot c ^ (r & 15), then stores whole
+      // 16-byte chunks of four rows per instruction; a fifth token block goes through the
+      // same area in a second pass
+      stage_barrier();
+      char* const stg = reinterpret_cast<char*>(lds) + w * 16384;
+      auto pass = [&](auto jb0_tag, auto jb1_tag) __attribute__((always_inline)) {
+        constexpr int JB0 = decltype(jb0_tag)::value, JB1 = decltype(jb1_tag)::value;
+  #pragma unroll
+        for (int jb = JB0; jb < JB1; ++jb) {
+          const int r = (jb - JB0) * 16 + (l & 15);
+  #pragma unroll
+          for (int ib = 0; ib < 8; ++ib) {
+            const int cc = 2 * ib + (l >> 5);
+            const f32x4_t& v = acc[ib][jb];
+            *reinterpret_cast<uint2*>(stg + r * 256 + ((cc ^ (r & 15)) << 4) + ((l >> 4) & 1) * 8) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int cc = l & 15;
+        const int col = n0 + wn * 128 + cc * 8;
+  #pragma unroll
+        for (int r0 = 0; r0 < 16 * (JB1 - JB0); r0 += 4) {
+          const int r = r0 + (l >> 4);
+          const int rl = wt * 80 + JB0 * 16 + r;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((cc ^ (r & 15)) << 4));
+          if (rl < mvalid && col < a.N)
+            *reinterpret_cast<uint4*>(a.C + size_t(m0 + rl) * a.ldc + col) = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      };
+      pass(std::integral_constant<int, 0>{}, std::integral_constant<int, (NJB < 4 ? NJB : 4)>{});
+      if constexpr (NJB > 4) pass(std::integral_constant<int, 4>{}, std::integral_constant<int, NJB>{});
     }
   };
   if (njb >= 5) body(std::integral_constant<int, 5>{});
